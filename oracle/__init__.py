@@ -1,0 +1,34 @@
+"""CPU oracle for content-aware block-sparse attention — TEST INFRASTRUCTURE.
+
+A plain, slow, float64 numpy statement of what the library computes.  Only
+the tests, the smoke check and the benchmark's CPU-baseline leg may import
+it; the library itself never does, and this package imports nothing from the
+library.  Inputs arrive as numpy arrays (bf16/f32 values upcast exactly to
+float64); outputs are float64.
+
+Page key used in citations:
+  [DMA]  lsdiaocha.cn/2025/0807/3170092.shtml — retelling of
+         "Dynamic Mask Attention" (arXiv:2508.02124).
+  [SA]   studyai.ink/2025/08/30 — "什么是稀疏注意力" explainer.
+  [NSA]  news.news/tag/稀疏注意力 — summary of "Native Sparse Attention".
+  [SF]   techwalker.com/2025/0429/3165971.shtml — retelling of
+         "The Sparse Frontier" (arXiv:2504.17768).
+
+Pinning status (the tests under tests/ that check each function against
+something other than itself):
+  prefill.pool_blocks, prefill.block_scores_pooled   — bilinearity, needles
+  prefill.select_blocks                              — brute-force subsets, counts
+  prefill.sparse_attention                           — dense causal SDPA, block-diagonal limit,
+                                                       softmax invariants, hand worked example
+  decode.page_minmax, decode.page_scores             — bound >= true max, equality cases
+  decode.decode_attention                            — dense single-query limit
+  nsa.compress                                       — stride = len = 1 identity, hand example
+  nsa.cmp_attention                                  — dense causal limit (len = stride = 1)
+  nsa.cmp_block_scores                               — row-mass invariant and a hand example;
+                                                       the overlap-fraction mapping itself is a
+                                                       reading, so its split rule is only pinned
+                                                       by those two (documented as partly pinned)
+  nsa.window_attention                               — W >= S dense limit, W = 1 identity
+  nsa.combine                                        — closed form when branches coincide
+"""
+from . import decode, nsa, prefill  # noqa: F401

@@ -1,0 +1,144 @@
+"""Pins for the three-branch (compressed / selected / sliding) oracle.
+
+[NSA] §03: three branches over the causal history, fused per token by
+gates.  The checks: exact limits where every branch collapses to dense
+causal attention, the probability-mass invariant of the block scores, and
+a hand-worked block-score example (tests/golden/nsa_block_scores_example.json).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from dynamic_block_sparse_head_amd import configs, inputs
+from oracle import nsa as N
+from oracle import prefill as P
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np(t):
+    return t.to(torch.float64).cpu().numpy()
+
+
+def _sdpa_causal(q, k, v, scale):
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    G = q.shape[1] // k.shape[1]
+    return F.scaled_dot_product_attention(q, k.repeat_interleave(G, 1), v.repeat_interleave(G, 1),
+                                          is_causal=True, scale=scale).numpy()
+
+
+def _small(S=256, Hq=8, Hkv=2, seed=0):
+    from dataclasses import replace
+    c = replace(configs.NSA_32K, S=S, Hq=Hq, Hkv=Hkv)
+    x = inputs.nsa_inputs(c, seed=seed)
+    return c, _np(x["q"]), _np(x["k"]), _np(x["v"]), _np(x["z"])
+
+
+def test_compress_identity_and_arange():
+    x = np.arange(40, dtype=np.float64).reshape(1, 1, 40, 1)
+    assert np.array_equal(N.compress(x, 1, 1), x)
+    ck = N.compress(x, 32, 16)     # (40-32)//16 + 1 = 1 summary: tokens 0..31
+    assert ck.shape[2] == 1 and ck[0, 0, 0, 0] == 15.5
+    y = np.arange(64, dtype=np.float64).reshape(1, 1, 64, 1)
+    ck = N.compress(y, 32, 16)     # starts 0, 16, 32 -> means 15.5, 31.5, 47.5
+    assert list(ck[0, 0, :, 0]) == [15.5, 31.5, 47.5]
+
+
+def test_unit_compression_is_dense_causal():
+    """len = stride = 1: the summaries are the keys themselves and branch 1 is
+    dense causal attention."""
+    c, q, k, v, _ = _small(S=128)
+    ck, cv = N.compress(k, 1, 1), N.compress(v, 1, 1)
+    o1, lse, p = N.cmp_attention(q, ck, cv, 1, 1, c.scale)
+    assert np.max(np.abs(o1 - _sdpa_causal(q, k, v, c.scale))) < 1e-12
+    assert np.max(np.abs(p.sum(-1) - 1)) < 1e-12
+
+
+def test_rows_without_a_summary_are_zero():
+    c, q, k, v, _ = _small(S=128)
+    ck, cv = N.compress(k, 32, 16), N.compress(v, 32, 16)
+    o1, lse, p = N.cmp_attention(q, ck, cv, 32, 16, c.scale)
+    assert (o1[:, :, :31] == 0).all() and np.isneginf(lse[:, :, :31]).all()
+    assert np.isfinite(lse[:, :, 31:]).all()
+    # row 31 sees only summary 0; row 47 sees summaries 0 and 1
+    assert np.allclose(o1[:, :, 31], np.repeat(cv[:, :, 0], c.G, axis=1), atol=1e-15, rtol=0)
+    assert (p[:, :, 47, 2:] == 0).all() and (p[:, :, 47, :2] > 0).all()
+
+
+def test_window_limits():
+    c, q, k, v, _ = _small(S=128)
+    o, _ = N.window_attention(q, k, v, 1000, c.scale)
+    assert np.max(np.abs(o - _sdpa_causal(q, k, v, c.scale))) < 1e-12
+    o, _ = N.window_attention(q, k, v, 1, c.scale)
+    assert np.max(np.abs(o - np.repeat(v, c.G, axis=1))) < 1e-15
+
+
+def test_every_branch_dense_gives_closed_form():
+    """len = stride = 1, k >= blocks, window >= S: each branch is dense causal
+    attention, so out = (sigmoid(z1)+sigmoid(z2)+sigmoid(z3)) * dense."""
+    c, q, k, v, z = _small(S=192)
+    res = N.forward(q, k, v, z, 1, 1, c.sel_block, 10, 10_000, c.scale)
+    dense = _sdpa_causal(q, k, v, c.scale)
+    gsum = (1 / (1 + np.exp(-z))).sum(-1).transpose(0, 2, 1)[..., None]
+    assert np.max(np.abs(res["out"] - gsum * dense)) < 1e-12
+
+
+def test_block_scores_mass_invariant():
+    """Each summary's probability is split over blocks with weights summing
+    to one, so a row of block scores sums to the fraction of (row, head)
+    pairs in the query block that see at least one summary."""
+    c, q, k, v, _ = _small(S=256)
+    ck, cv = N.compress(k, c.cmp_len, c.cmp_stride), N.compress(v, c.cmp_len, c.cmp_stride)
+    _, _, p = N.cmp_attention(q, ck, cv, c.cmp_len, c.cmp_stride, c.scale)
+    s = N.cmp_block_scores(p, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
+    w = N.overlap_weights(ck.shape[2], c.cmp_len, c.cmp_stride, c.sel_block, c.n_blocks)
+    assert np.allclose(w.sum(1), 1.0, atol=0, rtol=0)
+    for i in range(c.n_blocks):
+        t = np.arange(i * c.sel_block, (i + 1) * c.sel_block)
+        frac = np.mean(t >= c.cmp_len - 1)
+        assert np.allclose(s[:, :, i].sum(-1), frac, atol=1e-13)
+        assert (s[:, :, i, i + 1:] == 0).all()     # no mass after the query block
+
+
+def test_block_scores_hand_example():
+    """Uniform logits (q = 0): scores worked out by hand in the golden file."""
+    with open(os.path.join(GOLDEN, "nsa_block_scores_example.json")) as f:
+        ex = json.load(f)
+    S, L, st, sb = ex["S"], ex["len"], ex["stride"], ex["sel_block"]
+    rng = np.random.default_rng(0)
+    q = np.zeros((1, 1, S, 4))
+    k = rng.standard_normal((1, 1, S, 4))
+    v = rng.standard_normal((1, 1, S, 4))
+    ck, cv = N.compress(k, L, st), N.compress(v, L, st)
+    _, _, p = N.cmp_attention(q, ck, cv, L, st, 0.5)
+    s = N.cmp_block_scores(p, 1, L, st, sb, S)
+    want = np.array([[eval(x, {}) for x in row] for row in ex["scores_expr"]])
+    assert np.max(np.abs(s[0, 0] - want)) < 1e-14
+
+
+def test_selected_branch_uses_top16_of_candidates():
+    c, q, k, v, z = _small(S=256 * 8, Hq=4, Hkv=1)
+    ck, cv = N.compress(k, c.cmp_len, c.cmp_stride), N.compress(v, c.cmp_len, c.cmp_stride)
+    _, _, p = N.cmp_attention(q, ck, cv, c.cmp_len, c.cmp_stride, c.scale)
+    s = N.cmp_block_scores(p, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
+    idx, cnt = P.select_blocks(s, c.sel_k, 0, causal=True)
+    for i in range(c.n_blocks):
+        assert cnt[0, 0, i] == min(i + 1, c.sel_k)
+        chosen = set(idx[0, 0, i, :cnt[0, 0, i]])
+        rest = [j for j in range(i + 1) if j not in chosen]
+        if rest:
+            assert min(s[0, 0, i, j] for j in chosen) >= max(s[0, 0, i, j] for j in rest)
+
+
+def test_combine_gates():
+    rng = np.random.default_rng(2)
+    o = [rng.standard_normal((1, 2, 3, 4)) for _ in range(3)]
+    z = np.zeros((1, 3, 2, 3))
+    assert np.allclose(N.combine(*o, z), 0.5 * (o[0] + o[1] + o[2]), atol=1e-15, rtol=0)
+    z[..., 1] = 60.0
+    z[..., 0] = z[..., 2] = -60.0
+    assert np.allclose(N.combine(*o, z), o[1], atol=1e-15, rtol=0)
