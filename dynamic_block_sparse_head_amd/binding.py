@@ -1,0 +1,203 @@
+"""ctypes binding of libdsa.so: the same entry points as include/dsa.h.
+
+Argument marshalling only.  Tensors are torch tensors on the GPU (torch is
+used for device memory and the current HIP stream); every computation runs
+in the library's HIP kernels.  There is no fallback: without the built
+library, or without a GPU, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OK, DSA_E_ARG, DSA_E_UNSUPPORTED, DSA_E_WORKSPACE, DSA_E_HIP = 0, -1, -2, -3, -4
+DSA_F32, DSA_BF16 = 0, 1
+DSA_SCORE_POOLED, DSA_SCORE_PAGE_BOUND = 0, 1
+
+_c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+# name -> (restype, argtypes); mirrors include/dsa.h
+SIGNATURES = {
+    "dsa_version": (_c_int, []),
+    "dsa_status_string": (ctypes.c_char_p, [_c_int]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_block_scores_workspace_size": (_c_size, [_c_int] * 7),
+    "dsa_block_scores": (_c_int, [_c_int, _c_int, _vp, _vp, _vp] + [_c_int] * 6
+                         + [_vp, _c_size, _vp, _vp]),
+    "dsa_topk_select": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
+    "dsa_sparse_attn_prefill": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                                + [_c_int] * 3 + [_c_float, _vp, _vp, _vp]),
+    "dsa_page_minmax": (_c_int, [_c_int, _vp] + [_c_int] * 5 + [_vp, _vp, _vp]),
+    "dsa_sparse_attn_decode_workspace_size": (_c_size, [_c_int] * 6),
+    "dsa_sparse_attn_decode": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                               + [_c_int] * 2 + [_c_float, _vp, _c_size, _vp, _vp]),
+    "dsa_nsa_compress": (_c_int, [_c_int, _vp, _vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
+    "dsa_nsa_cmp_attn": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 8
+                         + [_c_float, _vp, _vp, _vp, _vp]),
+    "dsa_nsa_combine": (_c_int, [_c_int, _vp, _vp, _vp, _vp] + [_c_int] * 4 + [_vp, _vp]),
+}
+
+_lib = None
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: status {status}: {message}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsa.so once and declare its prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m dynamic_block_sparse_head_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != DSA_OK:
+        msg = load().dsa_last_error().decode(errors="replace")
+        raise DSAError(status, where, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, name, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+# ----------------------------------------------------------------- entries
+def dsa_version() -> int:
+    return load().dsa_version()
+
+
+def dsa_block_scores_workspace_size(kind, B, Hq, Hkv, n, D, block) -> int:
+    return load().dsa_block_scores_workspace_size(kind, B, Hq, Hkv, n, D, block)
+
+
+def dsa_block_scores(kind, q, k_or_kmin, kmax, block, workspace, scores, stream=None):
+    """POOLED: q [B,Hq,S,D], k [B,Hkv,S,D] -> scores [B,Hkv,nb,nb].
+    PAGE_BOUND: q [B,Hq,D], kmin/kmax [B,Hkv,nP,D] -> scores [B,Hkv,nP]."""
+    if kind == DSA_SCORE_POOLED:
+        B, Hq, n, D = q.shape
+        Hkv = k_or_kmin.shape[1]
+    else:
+        B, Hq, D = q.shape
+        Hkv, n = k_or_kmin.shape[1], k_or_kmin.shape[2]
+    ws_ptr = _ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().dsa_block_scores(kind, _dtype_code(q), _ptr(q, "q"), _ptr(k_or_kmin, "k"),
+                                 _ptr(kmax, "kmax"), B, Hq, Hkv, n, D, block, ws_ptr, ws_bytes,
+                                 _ptr(scores, "scores", torch.float32), _stream(stream))
+    _check(st, "dsa_block_scores")
+
+
+def dsa_topk_select(scores, k, n_local, causal, idx, count, stream=None):
+    """scores [..., n_q, n_k] float32 -> idx [..., n_q, k+n_local], count [..., n_q] int32."""
+    n_q, n_k = scores.shape[-2], scores.shape[-1]
+    rows = scores.numel() // (n_q * n_k)
+    st = load().dsa_topk_select(_ptr(scores, "scores", torch.float32), rows, n_q, n_k, k, n_local,
+                                int(bool(causal)), _ptr(idx, "idx", torch.int32),
+                                _ptr(count, "count", torch.int32), _stream(stream))
+    _check(st, "dsa_topk_select")
+
+
+def dsa_sparse_attn_prefill(q, k, v, idx, count, block, window, scale, out, lse=None, stream=None):
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    width = idx.shape[-1] if idx is not None else 0
+    st = load().dsa_sparse_attn_prefill(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S, D,
+        _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), width, block, window,
+        float(scale), _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream))
+    _check(st, "dsa_sparse_attn_prefill")
+
+
+def dsa_page_minmax(k, page, kmin, kmax, stream=None):
+    B, Hkv, L, D = k.shape
+    st = load().dsa_page_minmax(_dtype_code(k), _ptr(k, "k"), B, Hkv, L, D, page,
+                                _ptr(kmin, "kmin", k.dtype), _ptr(kmax, "kmax", k.dtype),
+                                _stream(stream))
+    _check(st, "dsa_page_minmax")
+
+
+def dsa_sparse_attn_decode_workspace_size(B, Hq, Hkv, idx_width, page, D) -> int:
+    return load().dsa_sparse_attn_decode_workspace_size(B, Hq, Hkv, idx_width, page, D)
+
+
+def dsa_sparse_attn_decode(q, k_cache, v_cache, idx, count, page, scale, workspace, out,
+                           stream=None):
+    B, Hq, D = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    st = load().dsa_sparse_attn_decode(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k_cache, "k_cache", q.dtype),
+        _ptr(v_cache, "v_cache", q.dtype), B, Hq, Hkv, L, D, _ptr(idx, "idx", torch.int32),
+        _ptr(count, "count", torch.int32), idx.shape[-1], page, float(scale),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, "out", q.dtype), _stream(stream))
+    _check(st, "dsa_sparse_attn_decode")
+
+
+def dsa_nsa_compress(k, v, length, stride, ck, cv, stream=None):
+    B, Hkv, S, D = k.shape
+    st = load().dsa_nsa_compress(_dtype_code(k), _ptr(k, "k"), _ptr(v, "v", k.dtype), B, Hkv, S, D,
+                                 length, stride, _ptr(ck, "ck", k.dtype), _ptr(cv, "cv", k.dtype),
+                                 _stream(stream))
+    _check(st, "dsa_nsa_compress")
+
+
+def dsa_nsa_cmp_attn(q, ck, cv, length, stride, sel_block, scale, out, lse, block_scores=None,
+                     stream=None):
+    B, Hq, S, D = q.shape
+    Hkv = ck.shape[1]
+    st = load().dsa_nsa_cmp_attn(
+        _dtype_code(q), _ptr(q, "q"), _ptr(ck, "ck", q.dtype), _ptr(cv, "cv", q.dtype), B, Hq, Hkv,
+        S, D, length, stride, sel_block, float(scale), _ptr(out, "out", q.dtype),
+        _ptr(lse, "lse", torch.float32), _ptr(block_scores, "block_scores", torch.float32),
+        _stream(stream))
+    _check(st, "dsa_nsa_cmp_attn")
+
+
+def dsa_nsa_combine(o_cmp, o_sel, o_win, gate_logits, out, stream=None):
+    B, Hq, S, D = o_cmp.shape
+    st = load().dsa_nsa_combine(_dtype_code(o_cmp), _ptr(o_cmp, "o_cmp"),
+                                _ptr(o_sel, "o_sel", o_cmp.dtype), _ptr(o_win, "o_win", o_cmp.dtype),
+                                _ptr(gate_logits, "gate_logits", torch.float32), B, Hq, S, D,
+                                _ptr(out, "out", o_cmp.dtype), _stream(stream))
+    _check(st, "dsa_nsa_combine")

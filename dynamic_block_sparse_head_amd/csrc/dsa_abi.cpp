@@ -1,0 +1,352 @@
+// C-ABI entry points of libdsa.so: argument validation, workspace carving
+// and kernel dispatch.  Validation runs entirely on the host and makes no
+// HIP call, so a rejected call enqueues nothing and touches no output.
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p)                                                        \
+  do {                                                                        \
+    if ((p) == nullptr) return fail(DSA_E_ARG, "%s must not be NULL", #p);    \
+    if (!aligned16(p)) return fail(DSA_E_ARG, "%s must be 16-byte aligned", #p); \
+  } while (0)
+
+int check_dtype(int dtype, bool f32_ok) {
+  if (dtype == DSA_BF16) return DSA_OK;
+  if (dtype == DSA_F32 && f32_ok) return DSA_OK;
+  if (dtype == DSA_F32) return fail(DSA_E_UNSUPPORTED, "dtype DSA_F32 is not supported by this call");
+  return fail(DSA_E_ARG, "unknown dtype %d", dtype);
+}
+
+int check_heads(int B, int Hq, int Hkv) {
+  REQUIRE(B >= 1, DSA_E_ARG, "B must be >= 1 (got %d)", B);
+  REQUIRE(Hq >= 1 && Hkv >= 1, DSA_E_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", Hq, Hkv);
+  REQUIRE(Hq % Hkv == 0, DSA_E_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  // launch grids put B, B*Hkv or Hq in a 16-bit grid dimension
+  REQUIRE(B <= 65535 && Hq <= 65535 && (long long)B * Hkv <= 65535, DSA_E_UNSUPPORTED,
+          "B (%d), Hq (%d) and B*Hkv must be at most 65535", B, Hq);
+  return DSA_OK;
+}
+
+int check_dim(int D) {
+  REQUIRE(D == 64 || D == 128, DSA_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", D);
+  return DSA_OK;
+}
+
+int check_block(int block, const char* what) {
+  REQUIRE(block > 0, DSA_E_ARG, "%s must be > 0 (got %d)", what, block);
+  REQUIRE(block % 32 == 0 && block <= 256, DSA_E_UNSUPPORTED,
+          "%s %d not supported (a multiple of 32, at most 256)", what, block);
+  return DSA_OK;
+}
+
+// largest element count a kernel may address with 64-bit offsets but 32-bit
+// row indices: keep every row count below 2^31
+bool rows_fit(long long a, long long b, long long c) { return a * b * c < (1ll << 31); }
+
+#define TRY(x)                     \
+  do {                             \
+    const int _st = (x);           \
+    if (_st != DSA_OK) return _st; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return DSA_VERSION; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_E_ARG: return "DSA_E_ARG: invalid argument";
+    case DSA_E_UNSUPPORTED: return "DSA_E_UNSUPPORTED: no kernel for this configuration";
+    case DSA_E_WORKSPACE: return "DSA_E_WORKSPACE: workspace missing or too small";
+    case DSA_E_HIP: return "DSA_E_HIP: HIP launch failure";
+    default: return "unknown dsa status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+size_t dsa_block_scores_workspace_size(int kind, int B, int Hq, int Hkv, int n, int D, int block) {
+  (void)Hq;
+  if (kind != DSA_SCORE_POOLED || B <= 0 || Hkv <= 0 || n <= 0 || D <= 0 || block <= 0) return 0;
+  const size_t nb = (size_t(n) + block - 1) / block;
+  return size_t(2) * B * Hkv * nb * D * sizeof(double);
+}
+
+int dsa_block_scores(int kind, int dtype, const void* q, const void* k_or_kmin, const void* kmax,
+                     int B, int Hq, int Hkv, int n, int D, int block, void* workspace,
+                     size_t workspace_bytes, float* scores, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, true));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  REQUIRE(n >= 1, DSA_E_ARG, "n must be >= 1 (got %d)", n);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_or_kmin);
+  REQUIRE_PTR(scores);
+  auto s = static_cast<hipStream_t>(stream);
+  if (kind == DSA_SCORE_POOLED) {
+    TRY(check_block(block, "block"));
+    REQUIRE(kmax == nullptr, DSA_E_ARG, "kmax must be NULL for DSA_SCORE_POOLED");
+    REQUIRE(rows_fit(B, Hq, n), DSA_E_ARG, "B*Hq*n too large");
+    const size_t need = dsa_block_scores_workspace_size(kind, B, Hq, Hkv, n, D, block);
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
+            "pooled scores need a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+    REQUIRE_PTR(workspace);
+    const int nb = (n + block - 1) / block;
+    dsa::PoolScoreArgs a{dtype, q, k_or_kmin, B, Hq, Hkv, n, D, block,
+                         static_cast<double*>(workspace),
+                         static_cast<double*>(workspace) + size_t(B) * Hkv * nb * D, scores};
+    return hip_status(dsa::launch_pooled_scores(a, s), "dsa_block_scores");
+  }
+  if (kind == DSA_SCORE_PAGE_BOUND) {
+    REQUIRE_PTR(kmax);
+    REQUIRE(Hq / Hkv <= 64, DSA_E_UNSUPPORTED, "at most 64 query heads per KV head");
+    dsa::PageScoreArgs a{dtype, q, k_or_kmin, kmax, B, Hq, Hkv, n, D, scores};
+    return hip_status(dsa::launch_page_scores(a, s), "dsa_block_scores");
+  }
+  return fail(DSA_E_ARG, "unknown score kind %d", kind);
+}
+
+int dsa_topk_select(const float* scores, int rows, int n_q, int n_k, int k, int n_local,
+                    int causal, int32_t* idx, int32_t* count, void* stream) {
+  g_err.clear();
+  REQUIRE(rows >= 1 && n_q >= 1 && n_k >= 1, DSA_E_ARG,
+          "rows, n_q, n_k must be >= 1 (got %d, %d, %d)", rows, n_q, n_k);
+  REQUIRE(k >= 0, DSA_E_ARG, "k must be >= 0 (got %d)", k);
+  REQUIRE(n_local >= 0, DSA_E_ARG, "n_local must be >= 0 (got %d)", n_local);
+  REQUIRE(k + n_local >= 1, DSA_E_ARG, "k + n_local must be >= 1");
+  REQUIRE(n_k <= 8192, DSA_E_UNSUPPORTED, "n_k %d exceeds 8192", n_k);
+  REQUIRE(!causal || n_q <= n_k, DSA_E_ARG, "causal selection needs n_q <= n_k (%d > %d)", n_q, n_k);
+  REQUIRE(causal || n_local <= n_k, DSA_E_ARG, "n_local (%d) exceeds n_k (%d)", n_local, n_k);
+  REQUIRE(rows_fit(rows, n_q, 1), DSA_E_ARG, "rows*n_q too large");
+  REQUIRE_PTR(scores);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  return hip_status(dsa::launch_topk(scores, rows, n_q, n_k, k, n_local, causal, idx, count,
+                                     static_cast<hipStream_t>(stream)),
+                    "dsa_topk_select");
+}
+
+int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                            int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
+                            int idx_width, int block, int window, float scale, void* out,
+                            float* lse, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, true));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  TRY(check_block(block, "block"));
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  const bool index_mode = idx != nullptr || count != nullptr;
+  if (index_mode) {
+    REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must both be given");
+    REQUIRE(window == 0, DSA_E_ARG, "window must be 0 in index mode (got %d)", window);
+    REQUIRE(idx_width >= 1, DSA_E_ARG, "idx_width must be >= 1 (got %d)", idx_width);
+  } else {
+    REQUIRE(window >= 1, DSA_E_ARG, "window mode needs window >= 1 (got %d)", window);
+  }
+  dsa::AttnArgs a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.idx = idx;
+  a.count = count;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.Skv = S;
+  a.D = D;
+  a.block = block;
+  a.idx_width = idx_width;
+  a.mode = index_mode ? dsa::MODE_INDEX : dsa::MODE_WINDOW;
+  a.window = window;
+  a.cmp_len = 1;
+  a.cmp_stride = 1;
+  a.scale = scale;
+  return hip_status(dsa::launch_attention(a, static_cast<hipStream_t>(stream)),
+                    "dsa_sparse_attn_prefill");
+}
+
+int dsa_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int page, void* kmin,
+                    void* kmax, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, true));
+  TRY(check_heads(B, Hkv, Hkv));
+  TRY(check_dim(D));
+  REQUIRE(page >= 1, DSA_E_ARG, "page must be >= 1 (got %d)", page);
+  REQUIRE(L >= page && L % page == 0, DSA_E_ARG, "L (%d) must be a positive multiple of page (%d)",
+          L, page);
+  REQUIRE(L / page <= 65535, DSA_E_UNSUPPORTED, "at most 65535 pages per sequence");
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(kmin);
+  REQUIRE_PTR(kmax);
+  return hip_status(dsa::launch_page_minmax(dtype, k, B, Hkv, L, D, page, kmin, kmax,
+                                            static_cast<hipStream_t>(stream)),
+                    "dsa_page_minmax");
+}
+
+size_t dsa_sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int idx_width, int page, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || idx_width <= 0 || page <= 0 || D <= 0) return 0;
+  return dsa::decode_workspace_bytes(B, Hq, Hkv, idx_width, page, D);
+}
+
+int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                           int B, int Hq, int Hkv, int L, int D, const int32_t* idx,
+                           const int32_t* count, int idx_width, int page, float scale,
+                           void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  const int G = Hq / Hkv;
+  REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, DSA_E_UNSUPPORTED,
+          "decode supports 1, 2, 4 or 8 query heads per KV head (got %d)", G);
+  REQUIRE(page >= 32 && page % 32 == 0 && page <= 512, DSA_E_UNSUPPORTED,
+          "page %d not supported (a multiple of 32, at most 512)", page);
+  REQUIRE(L >= page && L % page == 0, DSA_E_ARG, "L (%d) must be a positive multiple of page (%d)",
+          L, page);
+  REQUIRE(idx_width >= 1 && idx_width <= L / page, DSA_E_ARG,
+          "idx_width must be in [1, L/page] (got %d)", idx_width);
+  REQUIRE(B * Hkv <= 65535, DSA_E_UNSUPPORTED, "B*Hkv must be at most 65535");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache);
+  REQUIRE_PTR(out);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  const size_t need = dsa::decode_workspace_bytes(B, Hq, Hkv, idx_width, page, D);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
+          "decode needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  dsa::DecodeArgs a{q,  k_cache, v_cache, idx,   count, B, Hq, Hkv, L, D, idx_width, page,
+                    scale, static_cast<float*>(workspace), out};
+  return hip_status(dsa::launch_decode(a, static_cast<hipStream_t>(stream)),
+                    "dsa_sparse_attn_decode");
+}
+
+int dsa_nsa_compress(int dtype, const void* k, const void* v, int B, int Hkv, int S, int D, int len,
+                     int stride, void* ck, void* cv, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hkv, Hkv));
+  TRY(check_dim(D));
+  REQUIRE(len >= 1 && stride >= 1, DSA_E_ARG, "len and stride must be >= 1 (got %d, %d)", len,
+          stride);
+  REQUIRE(S >= len, DSA_E_ARG, "S (%d) must be >= len (%d)", S, len);
+  REQUIRE(B * Hkv <= 65535, DSA_E_UNSUPPORTED, "B*Hkv must be at most 65535");
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(ck);
+  REQUIRE_PTR(cv);
+  return hip_status(dsa::launch_nsa_compress(k, v, B, Hkv, S, D, len, stride, ck, cv,
+                                             static_cast<hipStream_t>(stream)),
+                    "dsa_nsa_compress");
+}
+
+int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, int B, int Hq,
+                     int Hkv, int S, int D, int len, int stride, int sel_block, float scale,
+                     void* out, float* lse, float* block_scores, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  TRY(check_block(sel_block, "sel_block"));
+  REQUIRE(len >= 1 && stride >= 1, DSA_E_ARG, "len and stride must be >= 1 (got %d, %d)", len,
+          stride);
+  REQUIRE(S >= len, DSA_E_ARG, "S (%d) must be >= len (%d)", S, len);
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  const int n_cmp = (S - len) / stride + 1;
+  REQUIRE(n_cmp <= 24576, DSA_E_UNSUPPORTED, "at most 24576 summaries (got %d)", n_cmp);
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(ck);
+  REQUIRE_PTR(cv);
+  REQUIRE_PTR(out);
+  REQUIRE(lse != nullptr, DSA_E_ARG, "lse must not be NULL");
+  auto s = static_cast<hipStream_t>(stream);
+  dsa::AttnArgs a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = ck;
+  a.v = cv;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.Skv = n_cmp;
+  a.D = D;
+  a.block = sel_block;
+  a.mode = dsa::MODE_CMP;
+  a.cmp_len = len;
+  a.cmp_stride = stride;
+  a.scale = scale;
+  int st = hip_status(dsa::launch_attention(a, s), "dsa_nsa_cmp_attn");
+  if (st != DSA_OK || block_scores == nullptr) return st;
+  dsa::CmpScoreArgs c{q, ck, lse, B, Hq, Hkv, S, n_cmp, D, len, stride, sel_block, scale,
+                      block_scores};
+  return hip_status(dsa::launch_cmp_block_scores(c, s), "dsa_nsa_cmp_attn");
+}
+
+int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void* o_win,
+                    const float* gate_logits, int B, int Hq, int S, int D, void* out,
+                    void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hq));
+  TRY(check_dim(D));
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE_PTR(o_cmp);
+  REQUIRE_PTR(o_sel);
+  REQUIRE_PTR(o_win);
+  REQUIRE_PTR(gate_logits);
+  REQUIRE_PTR(out);
+  return hip_status(dsa::launch_nsa_combine(o_cmp, o_sel, o_win, gate_logits, B, Hq, S, D, out,
+                                            static_cast<hipStream_t>(stream)),
+                    "dsa_nsa_combine");
+}
+
+}  // extern "C"

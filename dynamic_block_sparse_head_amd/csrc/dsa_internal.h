@@ -1,0 +1,94 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of
+// libdsa.so.  Nothing here is part of the public interface (include/dsa.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dsa {
+
+// ---------------------------------------------------------------- launches
+// Every launcher enqueues on `stream` and returns the launch status.  The
+// arguments were validated by the C-ABI layer before any launcher runs.
+
+struct PoolScoreArgs {
+  int dtype;
+  const void* q;     // [B,Hq,S,D]
+  const void* k;     // [B,Hkv,S,D]
+  int B, Hq, Hkv, S, D, block;
+  double* ws_q;      // [B*Hkv, nb, D]  group-summed pooled queries
+  double* ws_k;      // [B*Hkv, nb, D]  pooled keys
+  float* scores;     // [B,Hkv,nb,nb]
+};
+hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s);
+
+struct PageScoreArgs {
+  int dtype;
+  const void* q;     // [B,Hq,D]
+  const void* kmin;  // [B,Hkv,nP,D]
+  const void* kmax;
+  int B, Hq, Hkv, nP, D;
+  float* scores;     // [B,Hkv,nP]
+};
+hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s);
+
+hipError_t launch_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int page,
+                              void* kmin, void* kmax, hipStream_t s);
+
+hipError_t launch_topk(const float* scores, int rows, int n_q, int n_k, int k, int n_local,
+                       int causal, int32_t* idx, int32_t* count, hipStream_t s);
+
+enum AttnMode { MODE_INDEX = 0, MODE_WINDOW = 1, MODE_CMP = 2 };
+
+struct AttnArgs {
+  int dtype;
+  const void* q;        // [B,Hq,S,D]
+  const void* k;        // [B,Hkv,Skv,D]
+  const void* v;        // [B,Hkv,Skv,D]
+  void* out;            // [B,Hq,S,D]
+  float* lse;           // [B,Hq,S] or null
+  const int32_t* idx;   // index mode: [B,Hkv,nqb,idx_width]
+  const int32_t* count; // index mode: [B,Hkv,nqb]
+  int B, Hq, Hkv, S, Skv, D;
+  int block;            // query rows per query block (and key block size in index mode)
+  int idx_width;
+  int mode;
+  int window;           // window mode: tokens
+  int cmp_len, cmp_stride;  // compressed mode: summary c ends at c*stride+len-1
+  float scale;
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const void* q;        // [B,Hq,D] bf16
+  const void* k;        // [B,Hkv,L,D]
+  const void* v;
+  const int32_t* idx;   // [B,Hkv,idx_width]
+  const int32_t* count; // [B,Hkv]
+  int B, Hq, Hkv, L, D, idx_width, page;
+  float scale;
+  float* partial;       // workspace
+  void* out;            // [B,Hq,D] bf16
+};
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int idx_width, int page, int D);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+hipError_t launch_nsa_compress(const void* k, const void* v, int B, int Hkv, int S, int D,
+                               int len, int stride, void* ck, void* cv, hipStream_t s);
+
+struct CmpScoreArgs {
+  const void* q;        // [B,Hq,S,D] bf16
+  const void* ck;       // [B,Hkv,n_cmp,D] bf16
+  const float* lse;     // [B,Hq,S] from the compressed-branch attention
+  int B, Hq, Hkv, S, n_cmp, D, len, stride, sel_block;
+  float scale;
+  float* scores;        // [B,Hkv,nb,nb]
+};
+hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s);
+
+hipError_t launch_nsa_combine(const void* o1, const void* o2, const void* o3, const float* z,
+                              int B, int Hq, int S, int D, void* out, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,251 @@
+// Three-branch attention support kernels ([NSA] §03: a compressed branch
+// that scans summaries of the history, a selected branch over important
+// blocks, a sliding branch, fused per token by gates).
+//
+//  * k_compress: summaries = plain means of `len` keys (values) every
+//    `stride` tokens.
+//  * k_cmp_block_scores: second pass of the compressed branch.  With the
+//    branch's log-sum-exp known, it recomputes each row's probabilities over
+//    the summaries (bf16 MFMA), sums them over the rows and heads of a query
+//    block, and spreads each summary's mass over the key blocks it overlaps
+//    in proportion to the overlap: the importance that ranks blocks for the
+//    selected branch.  One workgroup per (group, query block), so the
+//    reduction order is fixed.
+//  * k_combine: out = sum over branches of sigmoid(gate logit) * branch output.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+// grid (ceil(n_cmp*D/8 / 256), B*Hkv, 2)
+__global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k,
+                                                  const uint16_t* __restrict__ v, int S, int D,
+                                                  int len, int stride, int n_cmp,
+                                                  uint16_t* __restrict__ ck,
+                                                  uint16_t* __restrict__ cv) {
+  const int cpr = D / 8;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n_cmp * cpr) return;
+  const int cidx = e / cpr, dc = e % cpr;
+  const int bg = blockIdx.y;
+  const uint16_t* src = (blockIdx.z == 0 ? k : v) + (size_t(bg) * S + size_t(cidx) * stride) * D + dc * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < len; ++r) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + size_t(r) * D);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      acc[2 * x] += bf16lo(w[x]);
+      acc[2 * x + 1] += bf16hi(w[x]);
+    }
+  }
+  const float inv = 1.f / float(len);
+  u32x4 o;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) o[x] = pack_bf16x2(acc[2 * x] * inv, acc[2 * x + 1] * inv);
+  uint16_t* dst = (blockIdx.z == 0 ? ck : cv) + (size_t(bg) * n_cmp + cidx) * D + dc * 8;
+  *reinterpret_cast<u32x4*>(dst) = o;
+}
+
+constexpr int kNW = 4;      // waves per workgroup
+constexpr int kQT = 2;      // 32-row tiles per wave
+constexpr int kRows = kNW * 32 * kQT;
+
+// grid (B*Hkv*nqb); dynamic LDS: colsum[n_cmp] floats
+template <int D>
+__global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
+  constexpr int CSTR = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][32 * CSTR];
+  __shared__ float wpart[kNW][32];
+  extern __shared__ float colsum[];
+
+  const int bg = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int sb = a.sel_block;
+  const int t0 = i * sb, t1 = min(a.S, t0 + sb) - 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const float c = a.scale * kLog2e;
+
+  for (int x = threadIdx.x; x < a.n_cmp; x += kNW * 64) colsum[x] = 0.f;
+
+  int c_hi = -1;
+  if (t1 >= a.len - 1) c_hi = min(a.n_cmp - 1, (t1 - (a.len - 1)) / a.stride);
+  const int nkt = c_hi < 0 ? 0 : c_hi / 32 + 1;
+  const uint16_t* ckp = static_cast<const uint16_t*>(a.ck) + size_t(bg) * a.n_cmp * D;
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+
+  const int total_rows = G * sb;
+  const int nchunks = (total_rows + kRows - 1) / kRows;
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    // this wave's query rows, their Q operands and base-2 log-sum-exp
+    bf16x8 qf[kQT][D / 16];
+    float lse2[kQT][16];
+    int rt[kQT];
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
+      const int r = chunk * kRows + wave * 32 * kQT + qt * 32 + col;
+      const int hh = r / sb;
+      const int t = t0 + r % sb;
+      const bool ok = hh < G && t <= t1;
+      const uint16_t* src = qp + ((size_t(b) * a.Hq + g * G + hh) * a.S + t) * D + half * 8;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        if (ok) {
+          qf[qt][ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[qt][ks][e] = static_cast<__bf16>(0.0f);
+        }
+      }
+      // rows of the accumulator tile held by this lane: (r/4)*8 + half*4 + r%4
+      const int rbase = chunk * kRows + wave * 32 * kQT + qt * 32;
+      rt[qt] = rbase;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int r2 = rbase + (rr >> 2) * 8 + half * 4 + (rr & 3);
+        const int h2 = r2 / sb, tt = t0 + r2 % sb;
+        float v = -__builtin_inff();
+        if (h2 < G && tt <= t1) v = a.lse[(size_t(b) * a.Hq + g * G + h2) * a.S + tt] * kLog2e;
+        lse2[qt][rr] = v;
+      }
+    }
+
+    auto stage = [&](int kt, int buf) {
+      for (int e = threadIdx.x; e < 32 * (D / 8); e += kNW * 64) {
+        const int key = kt * 32 + e / (D / 8), dc = e % (D / 8);
+        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+        if (key < a.n_cmp) w = *reinterpret_cast<const u32x4*>(ckp + size_t(key) * D + dc * 8);
+        *reinterpret_cast<u32x4*>(&c_lds[buf][(e / (D / 8)) * CSTR + dc * 8]) = w;
+      }
+    };
+    if (nkt > 0) stage(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nkt) stage(kt + 1, buf ^ 1);
+      floatx16 s[kQT];
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 cb = *reinterpret_cast<const bf16x8*>(&c_lds[buf][col * CSTR + ks * 16 + half * 8]);
+#pragma unroll
+        for (int qt = 0; qt < kQT; ++qt)
+          s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], cb, s[qt], 0, 0, 0);
+      }
+      // lane holds summary kt*32+col for 16 rows of each row tile
+      const int cs = kt * 32 + col;
+      const int cend = cs * a.stride + a.len - 1;
+      float part = 0.f;
+#pragma unroll
+      for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int r2 = rt[qt] + (rr >> 2) * 8 + half * 4 + (rr & 3);
+          const int tt = t0 + r2 % sb;
+          const bool vis = cs < a.n_cmp && cend <= tt && lse2[qt][rr] != -__builtin_inff();
+          if (vis) part += fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
+        }
+      part += __shfl_xor(part, 32);
+      if (half == 0) wpart[wave][col] = part;
+      __syncthreads();
+      if (threadIdx.x < 32) {
+        float t = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kNW; ++w2) t += wpart[w2][threadIdx.x];
+        const int cc = kt * 32 + threadIdx.x;
+        if (cc < a.n_cmp) colsum[cc] += t;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+
+  // spread each summary's mass over the key blocks it overlaps
+  const int nb = (a.S + sb - 1) / sb;
+  const float norm = 1.f / (float(t1 - t0 + 1) * float(G));
+  float* out = a.scores + (size_t(bg) * nqb + i) * nb;
+  for (int j = threadIdx.x; j < nb; j += kNW * 64) {
+    const int j0 = j * sb, j1 = j * sb + sb - 1;
+    int c0 = (j0 - a.len + 1 + a.stride - 1);
+    c0 = c0 <= 0 ? 0 : c0 / a.stride;
+    const int c1 = min(c_hi, j1 / a.stride);
+    float acc = 0.f;
+    for (int cc = c0; cc <= c1; ++cc) {
+      const int a0 = cc * a.stride, a1 = a0 + a.len - 1;
+      const int ov = min(a1, j1) - max(a0, j0) + 1;
+      if (ov > 0) acc += colsum[cc] * (float(ov) / float(a.len));
+    }
+    out[j] = acc * norm;
+  }
+}
+
+// grid-stride over 8-element chunks of the outputs
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o1,
+                                                 const uint16_t* __restrict__ o2,
+                                                 const uint16_t* __restrict__ o3,
+                                                 const float* __restrict__ z, int Hq, int S, int D,
+                                                 size_t nchunks, uint16_t* __restrict__ out) {
+  const int cpr = D / 8;
+  for (size_t e = size_t(blockIdx.x) * 256 + threadIdx.x; e < nchunks; e += size_t(gridDim.x) * 256) {
+    const size_t row = e / cpr;            // (b*Hq + h)*S + t
+    const int t = int(row % S);
+    const size_t bh = row / S;
+    const int h = int(bh % Hq);
+    const size_t b = bh / Hq;
+    const float* zz = z + ((b * S + t) * Hq + h) * 3;
+    const float g1 = 1.f / (1.f + __expf(-zz[0]));
+    const float g2 = 1.f / (1.f + __expf(-zz[1]));
+    const float g3 = 1.f / (1.f + __expf(-zz[2]));
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o1 + e * 8);
+    const u32x4 bb = *reinterpret_cast<const u32x4*>(o2 + e * 8);
+    const u32x4 cc = *reinterpret_cast<const u32x4*>(o3 + e * 8);
+    u32x4 r;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float lo = g1 * bf16lo(a[x]) + g2 * bf16lo(bb[x]) + g3 * bf16lo(cc[x]);
+      const float hi = g1 * bf16hi(a[x]) + g2 * bf16hi(bb[x]) + g3 * bf16hi(cc[x]);
+      r[x] = pack_bf16x2(lo, hi);
+    }
+    *reinterpret_cast<u32x4*>(out + e * 8) = r;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_nsa_compress(const void* k, const void* v, int B, int Hkv, int S, int D,
+                               int len, int stride, void* ck, void* cv, hipStream_t s) {
+  const int n_cmp = (S - len) / stride + 1;
+  const int work = n_cmp * (D / 8);
+  k_compress<<<dim3((work + 255) / 256, B * Hkv, 2), 256, 0, s>>>(
+      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), S, D, len, stride, n_cmp,
+      static_cast<uint16_t*>(ck), static_cast<uint16_t*>(cv));
+  return hipGetLastError();
+}
+
+hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s) {
+  const int nqb = (a.S + a.sel_block - 1) / a.sel_block;
+  const size_t lds = size_t(a.n_cmp) * sizeof(float);
+  if (a.D == 128)
+    k_cmp_block_scores<128><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
+  else
+    k_cmp_block_scores<64><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
+  return hipGetLastError();
+}
+
+hipError_t launch_nsa_combine(const void* o1, const void* o2, const void* o3, const float* z,
+                              int B, int Hq, int S, int D, void* out, hipStream_t s) {
+  const size_t nchunks = size_t(B) * Hq * S * (D / 8);
+  const size_t blocks = (nchunks + 255) / 256;
+  const unsigned grid = unsigned(blocks < 65536 ? blocks : 65536);
+  k_combine<<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(o1), static_cast<const uint16_t*>(o2),
+                                 static_cast<const uint16_t*>(o3), z, Hq, S, D, nchunks,
+                                 static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace dsa

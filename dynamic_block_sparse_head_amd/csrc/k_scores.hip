@@ -1,0 +1,255 @@
+// Block and page importance scores.
+//
+//  * Pooled prefill scores ([DMA] §四-§五: an importance score per history
+//    position from its content, causal mask before selection; [SA] "策略":
+//    blocks as the unit): score[b,g,i,j] = (sum over the group's query
+//    heads of the mean query of block i) . (mean key of block j), j <= i.
+//    Two kernels: a pooling pass that reads Q and K once (HBM bound) and a
+//    small float64 dot-product pass over the pooled vectors.
+//  * Page bounds for decode ([SF] §二-§四, page-level selection with the full
+//    cache kept): sum over heads and dims of max(q*kmin, q*kmax).
+//  * Page min/max metadata: element-wise extremes of each page's keys.
+//
+// All sums are float64 in a fixed order, so results are deterministic and
+// agree with an exact float64 evaluation to ~1e-15 relative.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Load 8 consecutive elements as float.
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf16lo(w[e]);
+    f[2 * e + 1] = bf16hi(w[e]);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  const floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  const floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = a[e];
+    f[4 + e] = b[e];
+  }
+}
+
+// out[bg, i, :] = sum over hpg heads of mean over the rows of block i.
+// grid (nb, B*Hkv); each thread owns 8 columns and a strided set of rows.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ x, int H, int S, int D,
+                                                   int block, int hpg, int Hkv,
+                                                   double* __restrict__ out) {
+  __shared__ double red[kThreads * 8];
+  const int i = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int ncg = D / 8;
+  const int nrg = kThreads / ncg;
+  const int cg = threadIdx.x % ncg;
+  const int rg = threadIdx.x / ncg;
+  const int row0 = i * block;
+  const int nrows = min(block, S - row0);
+  const int R = hpg * nrows;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int r = rg; r < R; r += nrg) {
+    const int hh = r / nrows, row = r % nrows;
+    const size_t off = ((size_t(b) * H + size_t(g) * hpg + hh) * S + row0 + row) * D + cg * 8;
+    float f[8];
+    load8(x + off, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += double(f[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg * D + cg * 8 + e] = acc[e];
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    double s = 0.0;
+    for (int r = 0; r < nrg; ++r) s += red[r * D + d];
+    out[(size_t(bg) * gridDim.x + i) * D + d] = s / double(nrows);
+  }
+}
+
+// scores[bg, i, j] = qs[bg, i, :] . kb[bg, j, :] for j <= i, -inf above the
+// diagonal.  16x16 output tile per workgroup, float64 dots from LDS.
+__global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restrict__ qs,
+                                                         const double* __restrict__ kb, int nb,
+                                                         int D, float* __restrict__ scores) {
+  extern __shared__ double lds[];  // [16][D+1] queries, then [16][D+1] keys
+  const int bg = blockIdx.z;
+  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
+  const int i = i0 + ti, j = j0 + tj;
+  float* srow = scores + size_t(bg) * nb * nb;
+  if (j0 > i0 + 15) {  // whole tile above the diagonal
+    if (i < nb && j < nb) srow[size_t(i) * nb + j] = -__builtin_inff();
+    return;
+  }
+  const int ld = D + 1;
+  double* lq = lds;
+  double* lk = lds + 16 * ld;
+  for (int e = threadIdx.x; e < 16 * D; e += kThreads) {
+    const int r = e / D, d = e % D;
+    lq[r * ld + d] = (i0 + r < nb) ? qs[(size_t(bg) * nb + i0 + r) * D + d] : 0.0;
+    lk[r * ld + d] = (j0 + r < nb) ? kb[(size_t(bg) * nb + j0 + r) * D + d] : 0.0;
+  }
+  __syncthreads();
+  if (i >= nb || j >= nb) return;
+  float res = -__builtin_inff();
+  if (j <= i) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += lq[ti * ld + d] * lk[tj * ld + d];
+    res = float(s);
+  }
+  srow[size_t(i) * nb + j] = res;
+}
+
+// Page bound scores.  Each page is handled by D/8 lanes (8 dims each); the
+// group's G query vectors sit in LDS as float.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_page_scores(const T* __restrict__ q,
+                                                          const T* __restrict__ kmin,
+                                                          const T* __restrict__ kmax, int Hq,
+                                                          int Hkv, int nP, int D,
+                                                          float* __restrict__ scores) {
+  extern __shared__ float lq[];  // [G][D]
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int G = Hq / Hkv;
+  for (int e = threadIdx.x; e < G * D; e += kThreads) {
+    const size_t off = (size_t(b) * Hq + size_t(g) * G) * D + e;
+    if constexpr (sizeof(T) == 2) lq[e] = bf16_to_f32(q[off]);
+    else lq[e] = q[off];
+  }
+  __syncthreads();
+  const int lpp = D / 8;                 // lanes per page
+  const int ppw = kThreads / lpp;        // pages per workgroup
+  const int sub = threadIdx.x % lpp;
+  const int p = blockIdx.x * ppw + threadIdx.x / lpp;
+  double acc = 0.0;
+  if (p < nP) {
+    const size_t off = (size_t(bg) * nP + p) * D + sub * 8;
+    float lo[8], hi[8];
+    load8(kmin + off, lo);
+    load8(kmax + off, hi);
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double qd = double(lq[h * D + sub * 8 + e]);
+        acc += fmax(qd * double(lo[e]), qd * double(hi[e]));
+      }
+    }
+  }
+  for (int o = lpp / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
+  if (p < nP && sub == 0) scores[size_t(bg) * nP + p] = float(acc);
+}
+
+// Element-wise min and max over each page.  grid (nP, B*Hkv).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ k, int L, int D,
+                                                          int page, T* __restrict__ kmin,
+                                                          T* __restrict__ kmax) {
+  __shared__ float rmin[kThreads * 8];
+  __shared__ float rmax[kThreads * 8];
+  const int p = blockIdx.x, bg = blockIdx.y;
+  const int nP = L / page;
+  const int ncg = D / 8, nrg = kThreads / ncg;
+  const int cg = threadIdx.x % ncg, rg = threadIdx.x / ncg;
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = __builtin_inff();
+    mx[e] = -__builtin_inff();
+  }
+  for (int r = rg; r < page; r += nrg) {
+    float f[8];
+    load8(k + (size_t(bg) * L + size_t(p) * page + r) * D + cg * 8, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = fminf(mn[e], f[e]);
+      mx[e] = fmaxf(mx[e], f[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    rmin[rg * D + cg * 8 + e] = mn[e];
+    rmax[rg * D + cg * 8 + e] = mx[e];
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float a = __builtin_inff(), c = -__builtin_inff();
+    for (int r = 0; r < nrg && r < page; ++r) {
+      a = fminf(a, rmin[r * D + d]);
+      c = fmaxf(c, rmax[r * D + d]);
+    }
+    const size_t off = (size_t(bg) * nP + p) * D + d;
+    if constexpr (sizeof(T) == 2) {
+      kmin[off] = f32_to_bf16(a);   // exact: a is a bf16 value
+      kmax[off] = f32_to_bf16(c);
+    } else {
+      kmin[off] = a;
+      kmax[off] = c;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s) {
+  const int nb = (a.S + a.block - 1) / a.block;
+  const int G = a.Hq / a.Hkv;
+  dim3 grid(nb, a.B * a.Hkv);
+  if (a.dtype == 1) {
+    k_pool<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(a.q), a.Hq, a.S, a.D,
+                                               a.block, G, a.Hkv, a.ws_q);
+    k_pool<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(a.k), a.Hkv, a.S, a.D,
+                                               a.block, 1, a.Hkv, a.ws_k);
+  } else {
+    k_pool<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(a.q), a.Hq, a.S, a.D,
+                                            a.block, G, a.Hkv, a.ws_q);
+    k_pool<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(a.k), a.Hkv, a.S, a.D,
+                                            a.block, 1, a.Hkv, a.ws_k);
+  }
+  const int nt = (nb + 15) / 16;
+  const size_t lds = size_t(2) * 16 * (a.D + 1) * sizeof(double);
+  k_pooled_dot<<<dim3(nt, nt, a.B * a.Hkv), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, a.D, a.scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s) {
+  const int ppw = kThreads / (a.D / 8);
+  dim3 grid((a.nP + ppw - 1) / ppw, a.B * a.Hkv);
+  const size_t lds = size_t(a.Hq / a.Hkv) * a.D * sizeof(float);
+  if (a.dtype == 1)
+    k_page_scores<uint16_t><<<grid, kThreads, lds, s>>>(
+        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kmin),
+        static_cast<const uint16_t*>(a.kmax), a.Hq, a.Hkv, a.nP, a.D, a.scores);
+  else
+    k_page_scores<float><<<grid, kThreads, lds, s>>>(
+        static_cast<const float*>(a.q), static_cast<const float*>(a.kmin),
+        static_cast<const float*>(a.kmax), a.Hq, a.Hkv, a.nP, a.D, a.scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int page,
+                              void* kmin, void* kmax, hipStream_t s) {
+  dim3 grid(L / page, B * Hkv);
+  if (dtype == 1)
+    k_page_minmax<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(k), L, D, page,
+                                                      static_cast<uint16_t*>(kmin),
+                                                      static_cast<uint16_t*>(kmax));
+  else
+    k_page_minmax<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(k), L, D, page,
+                                                   static_cast<float*>(kmin),
+                                                   static_cast<float*>(kmax));
+  return hipGetLastError();
+}
+
+}  // namespace dsa

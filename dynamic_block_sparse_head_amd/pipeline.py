@@ -1,0 +1,124 @@
+"""The three paths as sequences of library calls.
+
+Orchestration only: outputs and workspaces are allocated with torch (device
+memory), every step is a call into libdsa.so on the current stream.  Plans
+allocate once so that repeated runs (benchmarks, serving loops) allocate
+nothing.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as L
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+class PrefillPlan:
+    """Pooled scores -> top-k + window -> block-sparse attention ([DMA] §五)."""
+
+    def __init__(self, B, Hq, Hkv, S, D, block, topk, n_local, dtype, device, scale=None):
+        self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
+        self.block, self.topk, self.n_local = block, topk, n_local
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
+        self.nb = -(-S // block)
+        ws = L.dsa_block_scores_workspace_size(L.DSA_SCORE_POOLED, B, Hq, Hkv, S, D, block)
+        self.ws = _empty((ws,), torch.uint8, device)
+        self.scores = _empty((B, Hkv, self.nb, self.nb), torch.float32, device)
+        self.idx = _empty((B, Hkv, self.nb, topk + n_local), torch.int32, device)
+        self.count = _empty((B, Hkv, self.nb), torch.int32, device)
+        self.out = _empty((B, Hq, S, D), dtype, device)
+        self.lse = _empty((B, Hq, S), torch.float32, device)
+
+    def score(self, q, k):
+        L.dsa_block_scores(L.DSA_SCORE_POOLED, q, k, None, self.block, self.ws, self.scores)
+
+    def select(self):
+        L.dsa_topk_select(self.scores, self.topk, self.n_local, True, self.idx, self.count)
+
+    def attend(self, q, k, v):
+        L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.block, 0, self.scale,
+                                  self.out, self.lse)
+
+    def run(self, q, k, v):
+        self.score(q, k)
+        self.select()
+        self.attend(q, k, v)
+        return self.out
+
+
+class DecodePlan:
+    """Page bounds -> top pages -> attention over the selected pages ([SF] §二-§四)."""
+
+    def __init__(self, B, Hq, Hkv, L_, D, page, topk, dtype, device, scale=None):
+        self.B, self.Hq, self.Hkv, self.L, self.D, self.page, self.topk = B, Hq, Hkv, L_, D, page, topk
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
+        self.nP = L_ // page
+        self.kmin = _empty((B, Hkv, self.nP, D), dtype, device)
+        self.kmax = _empty((B, Hkv, self.nP, D), dtype, device)
+        self.scores = _empty((B, Hkv, 1, self.nP), torch.float32, device)
+        self.idx = _empty((B, Hkv, 1, topk), torch.int32, device)
+        self.count = _empty((B, Hkv, 1), torch.int32, device)
+        ws = L.dsa_sparse_attn_decode_workspace_size(B, Hq, Hkv, topk, page, D)
+        self.ws = _empty((ws,), torch.uint8, device)
+        self.out = _empty((B, Hq, D), dtype, device)
+
+    def build_metadata(self, k_cache):
+        L.dsa_page_minmax(k_cache, self.page, self.kmin, self.kmax)
+
+    def score(self, q):
+        L.dsa_block_scores(L.DSA_SCORE_PAGE_BOUND, q, self.kmin, self.kmax, self.page, None,
+                           self.scores)
+
+    def select(self):
+        L.dsa_topk_select(self.scores, self.topk, 0, False, self.idx, self.count)
+
+    def attend(self, q, k_cache, v_cache):
+        L.dsa_sparse_attn_decode(q, k_cache, v_cache, self.idx, self.count, self.page, self.scale,
+                                 self.ws, self.out)
+
+    def run(self, q, k_cache, v_cache):
+        self.score(q)
+        self.select()
+        self.attend(q, k_cache, v_cache)
+        return self.out
+
+
+class NSAPlan:
+    """Compressed branch (+ block scores) -> top-k blocks -> selected branch;
+    sliding branch; gated combine ([NSA] §03)."""
+
+    def __init__(self, B, Hq, Hkv, S, D, cmp_len, cmp_stride, sel_block, sel_k, window, dtype,
+                 device, scale=None):
+        self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
+        self.cmp_len, self.cmp_stride = cmp_len, cmp_stride
+        self.sel_block, self.sel_k, self.window = sel_block, sel_k, window
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
+        self.n_cmp = (S - cmp_len) // cmp_stride + 1
+        self.nb = -(-S // sel_block)
+        self.ck = _empty((B, Hkv, self.n_cmp, D), dtype, device)
+        self.cv = _empty((B, Hkv, self.n_cmp, D), dtype, device)
+        self.o_cmp = _empty((B, Hq, S, D), dtype, device)
+        self.lse_cmp = _empty((B, Hq, S), torch.float32, device)
+        self.scores = _empty((B, Hkv, self.nb, self.nb), torch.float32, device)
+        self.idx = _empty((B, Hkv, self.nb, sel_k), torch.int32, device)
+        self.count = _empty((B, Hkv, self.nb), torch.int32, device)
+        self.o_sel = _empty((B, Hq, S, D), dtype, device)
+        self.o_win = _empty((B, Hq, S, D), dtype, device)
+        self.out = _empty((B, Hq, S, D), dtype, device)
+
+    def run(self, q, k, v, z):
+        L.dsa_nsa_compress(k, v, self.cmp_len, self.cmp_stride, self.ck, self.cv)
+        L.dsa_nsa_cmp_attn(q, self.ck, self.cv, self.cmp_len, self.cmp_stride, self.sel_block,
+                           self.scale, self.o_cmp, self.lse_cmp, self.scores)
+        L.dsa_topk_select(self.scores, self.sel_k, 0, True, self.idx, self.count)
+        L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.sel_block, 0, self.scale,
+                                  self.o_sel)
+        L.dsa_sparse_attn_prefill(q, k, v, None, None, self.sel_block, self.window, self.scale,
+                                  self.o_win)
+        L.dsa_nsa_combine(self.o_cmp, self.o_sel, self.o_win, z, self.out)
+        return self.out

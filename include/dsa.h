@@ -1,0 +1,198 @@
+/*
+ * dsa.h — content-aware top-k block-sparse attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libdsa.so.  Every entry point takes plain device pointers and
+ * sizes, enqueues its kernels on the given HIP stream (a hipStream_t passed
+ * as void*; NULL = the default stream) and returns without waiting.
+ *
+ * Pages cited (by subject, address and section):
+ *   [DMA] Dynamic Mask Attention retelling, lsdiaocha.cn/2025/0807/3170092.shtml
+ *   [SA]  sparse-attention explainer, studyai.ink/2025/08/30 ("什么是稀疏注意力")
+ *   [NSA] Native Sparse Attention summary, news.news/tag/稀疏注意力
+ *   [SF]  The Sparse Frontier retelling, techwalker.com/2025/0429/3165971.shtml
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense and row-major with the last dimension contiguous;
+ *     shapes are given in brackets.  bf16 tensors hold IEEE bfloat16 bits.
+ *   - dtype is DSA_F32 or DSA_BF16 and applies to q, k, v and outputs of the
+ *     same role; scores, log-sum-exp and gate logits are always float32;
+ *     index and count tensors are int32.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device memory, keeps no pointer after a call returns and holds no
+ *     global mutable state besides a thread-local error message.  Scratch
+ *     memory comes only through an explicit workspace argument whose size
+ *     the matching *_workspace_size() call returns.
+ *   - Errors: a call returns DSA_OK (0) or a negative status.  On
+ *     DSA_E_ARG, DSA_E_UNSUPPORTED or DSA_E_WORKSPACE nothing is enqueued and
+ *     no output is touched; dsa_last_error() names the offending argument.
+ *     DSA_E_HIP reports a failed launch with the HIP error text.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Results are deterministic: fixed reduction orders, no floating-point
+ *     atomics; two identical calls produce identical bits.
+ *   - Supported: head dim D in {64, 128}; block / page sizes that are
+ *     multiples of 32 (up to 256); bf16 for every call, float32 for the
+ *     scoring, selection and prefill calls as well.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_VERSION 100
+
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_E_ARG = -1,          /* null pointer, bad size, misaligned pointer, bad k/window */
+  DSA_E_UNSUPPORTED = -2,  /* dtype / head dim / block size with no compiled kernel */
+  DSA_E_WORKSPACE = -3,    /* workspace missing or smaller than *_workspace_size() */
+  DSA_E_HIP = -4           /* kernel launch failed (text in dsa_last_error) */
+};
+
+enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1 };
+
+enum dsa_score_kind {
+  DSA_SCORE_POOLED = 0,     /* prefill: mean-pooled query block . mean-pooled key block */
+  DSA_SCORE_PAGE_BOUND = 1  /* decode: per-page min/max key bound */
+};
+
+int dsa_version(void);
+const char* dsa_status_string(int status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Block / page importance scores ([DMA] §四-§五: a per-position importance
+ * score from content, causal mask, then top-k; [SF] §二 page-level decode).
+ *
+ * kind = DSA_SCORE_POOLED ([SA] "策略" block granularity):
+ *   q [B,Hq,n,D], k_or_kmin = K [B,Hkv,n,D] (n = sequence length), kmax = NULL,
+ *   block = rows per block, nb = ceil(n/block).
+ *   scores [B,Hkv,nb,nb] float32: scores[b,g,i,j] = sum over the Hq/Hkv query
+ *   heads h of group g of mean(Q[b,h,block i]) . mean(K[b,g,block j]) for
+ *   j <= i, -inf for j > i.  Means, dots and the head sum are accumulated
+ *   in float64 and rounded once to float32.  Needs a workspace of
+ *   dsa_block_scores_workspace_size() bytes.
+ *
+ * kind = DSA_SCORE_PAGE_BOUND:
+ *   q [B,Hq,D], k_or_kmin = kmin [B,Hkv,n,D], kmax [B,Hkv,n,D] (n = pages),
+ *   block ignored.  scores [B,Hkv,n] float32: sum over the group's heads h
+ *   and over d of max(q[b,h,d]*kmin[..,d], q[b,h,d]*kmax[..,d]), the
+ *   largest q.k any key inside the page's min/max box can reach, accumulated
+ *   in float64.  No workspace (pass NULL, 0).
+ */
+size_t dsa_block_scores_workspace_size(int kind, int B, int Hq, int Hkv, int n, int D, int block);
+int dsa_block_scores(int kind, int dtype, const void* q, const void* k_or_kmin, const void* kmax,
+                     int B, int Hq, int Hkv, int n, int D, int block,
+                     void* workspace, size_t workspace_bytes, float* scores, void* stream);
+
+/*
+ * Top-k selection plus local window ([DMA] §五: keep the k highest-weight
+ * history positions after the causal mask, all others become -inf).
+ *
+ * scores [rows, n_q, n_k] float32 (rows = B*Hkv).  For causal != 0, row i
+ * of each score matrix draws its top-k from key blocks 0 .. i-n_local and
+ * always keeps the window i-n_local+1 .. i (clipped at 0); n_q <= n_k.
+ * For causal == 0 the candidates are 0 .. n_k-1-n_local and the window is the
+ * last n_local blocks.  Ranking: higher score first, equal scores by lower
+ * index, NaN after every number.
+ * idx [rows, n_q, k+n_local] int32: the chosen blocks ascending, padded with
+ * -1; count [rows, n_q] int32: number of valid entries.
+ * Limits: 0 <= k, 0 <= n_local, n_k <= 8192.
+ */
+int dsa_topk_select(const float* scores, int rows, int n_q, int n_k, int k, int n_local,
+                    int causal, int32_t* idx, int32_t* count, void* stream);
+
+/*
+ * Exact softmax attention over the selected key blocks only ([DMA] §四-§五:
+ * masked positions are skipped, never multiplied; the result equals the
+ * masked dense computation).
+ *
+ * q, out [B,Hq,S,D]; k, v [B,Hkv,S,D]; query head h uses KV head
+ * h / (Hq/Hkv).  scale multiplies q.k (normally 1/sqrt(D)).
+ * Index mode (idx != NULL): idx [B,Hkv,ceil(S/block),idx_width] ascending
+ *   block lists (-1 padded) and count [B,Hkv,ceil(S/block)], as written by
+ *   dsa_topk_select; row t of query block i sees keys s <= t of the listed
+ *   key blocks.  window must be 0.
+ * Window mode (idx == NULL, count == NULL, window > 0): row t sees keys
+ *   max(0, t-window+1) .. t ([NSA] §03 sliding branch).
+ * lse [B,Hq,S] float32 (may be NULL): natural-log sum of exp of the scaled
+ * logits of each row (-inf for a row that sees no key, whose output is 0).
+ * Internal math: bf16 products with float32 accumulation (float32 for
+ * DSA_F32); out is rounded to dtype.
+ */
+int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void* v,
+                            int B, int Hq, int Hkv, int S, int D,
+                            const int32_t* idx, const int32_t* count, int idx_width, int block,
+                            int window, float scale, void* out, float* lse, void* stream);
+
+/*
+ * Per-page key summaries for decode ([DMA] §三 per-block cache summaries;
+ * [SF] §四 page granularity): kmin/kmax [B,Hkv,L/page,D] = element-wise
+ * minimum / maximum of K [B,Hkv,L,D] over each page (exact).  L % page == 0.
+ */
+int dsa_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int page,
+                    void* kmin, void* kmax, void* stream);
+
+/*
+ * Single-query decode attention over the selected pages of a full KV cache
+ * ([SF] §二-§四: the cache is kept whole, only selected pages are read).
+ *
+ * q, out [B,Hq,D]; k_cache, v_cache [B,Hkv,L,D]; idx [B,Hkv,idx_width]
+ * page lists (ascending, -1 padded), count [B,Hkv]; page = tokens per page.
+ * The query follows all L cached tokens, so every token of a selected page
+ * is visible.  Pages are split over workgroups whose partial results
+ * (max, sum, weighted values) are merged in a fixed order.  bf16 only;
+ * L % page == 0, page a multiple of 32 up to 512, Hq/Hkv in {1,2,4,8}.
+ */
+size_t dsa_sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int idx_width, int page,
+                                             int D);
+int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                           int B, int Hq, int Hkv, int L, int D,
+                           const int32_t* idx, const int32_t* count, int idx_width, int page,
+                           float scale, void* workspace, size_t workspace_bytes,
+                           void* out, void* stream);
+
+/*
+ * Compressed keys / values for the coarse branch ([NSA] §03 "compressed
+ * attention": a quick scan of summaries of the history).
+ * ck, cv [B,Hkv,n_cmp,D] with n_cmp = (S-len)/stride + 1:
+ * ck[c] = mean(K[c*stride .. c*stride+len-1]) (float32 sum, rounded once).
+ */
+int dsa_nsa_compress(int dtype, const void* k, const void* v, int B, int Hkv, int S, int D,
+                     int len, int stride, void* ck, void* cv, void* stream);
+
+/*
+ * Compressed-branch attention and the block scores that drive selection
+ * ([NSA] §03).  q, out [B,Hq,S,D]; ck, cv [B,Hkv,n_cmp,D].
+ * Row t sees summary c iff c*stride + len - 1 <= t; a row that sees none
+ * gets out = 0 and lse = -inf.  lse [B,Hq,S] float32 is required.
+ * block_scores [B,Hkv,nb,nb] float32 (nb = ceil(S/sel_block)), may be NULL:
+ * for query block i and key block j, the branch probability mass of the
+ * summaries overlapping block j, each split in proportion to its overlap
+ * with the block, summed over the block's rows and the group's heads and
+ * divided by rows x heads (values in [0,1]; 0 for j > i).
+ */
+int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv,
+                     int B, int Hq, int Hkv, int S, int D, int len, int stride, int sel_block,
+                     float scale, void* out, float* lse, float* block_scores, void* stream);
+
+/*
+ * Gated combine of the three branches ([NSA] §03: each token and head
+ * weighs the compressed, selected and sliding outputs):
+ * out[b,h,t] = sigmoid(z0)*o_cmp + sigmoid(z1)*o_sel + sigmoid(z2)*o_win with
+ * z = gate_logits[b,t,h,0..2] ([B,S,Hq,3] float32).  o_*, out [B,Hq,S,D].
+ */
+int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void* o_win,
+                    const float* gate_logits, int B, int Hq, int S, int D, void* out,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,244 @@
+"""GPU parity: every entry point of libdsa.so against the float64 oracle on
+the same seeded inputs, at sizes the oracle finishes in seconds (several
+tiles, ragged tails, degenerate cases).  Calls go through the C ABI."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from dynamic_block_sparse_head_amd import binding as L
+from dynamic_block_sparse_head_amd import configs, inputs
+from dynamic_block_sparse_head_amd.pipeline import DecodePlan, NSAPlan, PrefillPlan
+from oracle import decode as Od
+from oracle import nsa as On
+from oracle import prefill as Op
+
+from _parity import (check_bf16, check_f32, check_index_row, check_indices, check_lse, to_np)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------- selection
+@pytest.mark.parametrize("n_q,n_k,k,n_local,causal", [
+    (8, 8, 2, 1, True), (256, 256, 16, 8, True), (512, 512, 32, 8, True), (512, 512, 16, 0, True),
+    (1, 2048, 102, 0, False), (1, 300, 7, 3, False), (40, 40, 0, 2, True), (33, 33, 100, 1, True)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_bit_exact(n_q, n_k, k, n_local, causal, ties):
+    """Same float32 scores in, same indices out: selection is bit-exact."""
+    rows = 3
+    s = inputs.random_scores(rows * n_q, n_k, seed=n_k + k, ties=ties).reshape(rows, n_q, n_k)
+    if causal:   # entries above the diagonal are -inf as the scorer writes them
+        s = s.masked_fill(torch.triu(torch.ones(n_q, n_k, dtype=torch.bool), diagonal=1), float("-inf"))
+    sg = s.to(DEV)
+    idx = torch.full((rows, n_q, k + n_local), 77, dtype=torch.int32, device=DEV)
+    cnt = torch.full((rows, n_q), 77, dtype=torch.int32, device=DEV)
+    L.dsa_topk_select(sg, k, n_local, causal, idx, cnt)
+    _sync()
+    oi, oc = Op.select_blocks(s.double().numpy(), k, n_local, causal)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+    assert np.array_equal(cnt.cpu().numpy(), oc)
+
+
+def test_topk_nan_ranks_last():
+    s = torch.tensor([[[0.0, float("nan"), 1.0, 1.0, 0.5, 9.0]]])
+    idx = torch.empty((1, 1, 3), dtype=torch.int32, device=DEV)
+    cnt = torch.empty((1, 1), dtype=torch.int32, device=DEV)
+    L.dsa_topk_select(s.to(DEV), 3, 0, False, idx, cnt)
+    _sync()
+    assert idx.cpu().tolist() == [[[2, 3, 5]]] and cnt.item() == 3
+
+
+# ---------------------------------------------------------- pooled scores
+@pytest.mark.parametrize("cfg,S", [(configs.TINY_F32, 256), (configs.TINY_F32, 200),
+                                   (configs.PREFILL_16K, 2048), (configs.PREFILL_64K, 2048 + 64)])
+def test_pooled_scores(cfg, S):
+    c = cfg.with_seq(S)
+    x = inputs.prefill_inputs(c, seed=1, device=DEV)
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, x["q"].dtype, DEV)
+    plan.score(x["q"], x["k"])
+    _sync()
+    ref = Op.block_scores_pooled(to_np(x["q"]), to_np(x["k"]), c.block)
+    got = to_np(plan.scores)
+    assert (np.isneginf(got) == np.isneginf(ref)).all()
+    fin = np.isfinite(ref)
+    # float64 accumulation rounded once to float32
+    assert (np.abs(got[fin] - ref[fin]) <= 2.0 ** -23 * np.abs(ref[fin]) + 1e-30).all()
+
+
+# -------------------------------------------------------------- prefill
+def _prefill_parity(c, seed=0):
+    x = inputs.prefill_inputs(c, seed=seed, device=DEV)
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, x["q"].dtype, DEV)
+    plan.run(x["q"], x["k"], x["v"])
+    _sync()
+    q, k, v = to_np(x["q"]), to_np(x["k"]), to_np(x["v"])
+    s_ref = Op.block_scores_pooled(q, k, c.block)
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    exact = check_indices(s_ref, gi, gc, c.topk, c.n_local, True)
+    for (b, g, t, n) in x["needles"]:
+        assert n in gi[b, g, t, :gc[b, g, t]], "planted needle not selected"
+    out, lse = Op.sparse_attention(q, k, v, gi, gc, c.block, c.scale)
+    go, gl = to_np(plan.out), to_np(plan.lse)
+    if c.dtype == "f32":
+        check_f32(go, out, c.name)
+        check_lse(gl, lse, 1e-4, c.name)
+    else:
+        check_bf16(go, out, c.name)
+        check_lse(gl, lse, 2e-3, c.name)
+    return exact
+
+
+def test_prefill_tiny_f32_full_config():
+    exact = _prefill_parity(configs.TINY_F32)
+    assert exact == 1.0
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_prefill_tiny_f32_seeds(seed):
+    _prefill_parity(configs.TINY_F32, seed=seed)
+
+
+@pytest.mark.parametrize("S", [2048, 2000])
+def test_prefill_bf16_16k_shape(S):
+    _prefill_parity(configs.PREFILL_16K.with_seq(S))
+
+
+def test_prefill_bf16_64k_shape_mixture():
+    _prefill_parity(configs.PREFILL_64K.with_seq(6144))
+
+
+def test_prefill_bf16_block32_and_d64():
+    c = replace(configs.PREFILL_16K, name="b32d64", S=1024 + 32, D=64, block=32, topk=5, window=64,
+                q_std=0.125, kv_std=0.125, v_std=0.125, needles=2, needle_alpha=0.5)
+    _prefill_parity(c)
+
+
+def test_prefill_all_blocks_equals_dense():
+    """k >= number of blocks: the kernel reproduces dense causal attention."""
+    c = configs.PREFILL_16K.with_seq(1024)
+    x = inputs.prefill_inputs(c, seed=3, device=DEV)
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.n_blocks, 1, x["q"].dtype, DEV)
+    plan.run(x["q"], x["k"], x["v"])
+    _sync()
+    assert (plan.count.cpu().numpy() == np.arange(1, c.n_blocks + 1)).all()
+    q, k, v = to_np(x["q"]), to_np(x["k"]), to_np(x["v"])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k).repeat_interleave(c.G, 1),
+        torch.from_numpy(v).repeat_interleave(c.G, 1), is_causal=True, scale=c.scale).numpy()
+    check_bf16(to_np(plan.out), ref, "dense")
+
+
+def test_prefill_window_mode():
+    c = replace(configs.NSA_32K, S=1000, Hq=8, Hkv=2)
+    x = inputs.nsa_inputs(c, seed=0, device=DEV)
+    out = torch.empty_like(x["q"])
+    lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device=DEV)
+    for W in (512, 100, 1):
+        L.dsa_sparse_attn_prefill(x["q"], x["k"], x["v"], None, None, 64, W, c.scale, out, lse)
+        _sync()
+        ref, rl = On.window_attention(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), W, c.scale)
+        check_bf16(to_np(out), ref, f"window {W}")
+        check_lse(to_np(lse), rl, 2e-3, f"window {W}")
+
+
+def test_prefill_deterministic():
+    c = configs.PREFILL_16K.with_seq(2048)
+    x = inputs.prefill_inputs(c, seed=5, device=DEV)
+    p = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, x["q"].dtype, DEV)
+    p.run(x["q"], x["k"], x["v"])
+    a = (p.scores.clone(), p.idx.clone(), p.out.clone(), p.lse.clone())
+    p.run(x["q"], x["k"], x["v"])
+    _sync()
+    for u, w in zip(a, (p.scores, p.idx, p.out, p.lse)):
+        assert torch.equal(u, w)
+
+
+# --------------------------------------------------------------- decode
+def _decode_parity(B=2, L_=8192, topk=6, seed=0, page=64, Hq=32, Hkv=8):
+    c = replace(configs.DECODE_128K, B=B, L=L_, page=page, Hq=Hq, Hkv=Hkv)
+    x = inputs.decode_inputs(c, seed=seed, device=DEV)
+    plan = DecodePlan(c.B, c.Hq, c.Hkv, c.L, c.D, c.page, topk, x["q"].dtype, DEV)
+    plan.build_metadata(x["k"])
+    plan.run(x["q"], x["k"], x["v"])
+    _sync()
+    q, k, v = to_np(x["q"]), to_np(x["k"]), to_np(x["v"])
+    kmin, kmax = Od.page_minmax(k, c.page)
+    assert np.array_equal(to_np(plan.kmin), kmin) and np.array_equal(to_np(plan.kmax), kmax)
+    s = Od.page_scores(q, kmin, kmax)
+    got = to_np(plan.scores)[:, :, 0]
+    assert (np.abs(got - s) <= 2.0 ** -23 * np.abs(s) + 1e-30).all()
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    check_indices(s[:, :, None, :], gi, gc, topk, 0, False)
+    ref = Od.decode_attention(q, k, v, gi[:, :, 0], gc[:, :, 0], c.page, c.scale)
+    check_bf16(to_np(plan.out), ref, "decode")
+
+
+def test_decode_small():
+    _decode_parity()
+
+
+def test_decode_odd_counts_and_page128():
+    _decode_parity(B=1, L_=128 * 40, topk=13, page=128, seed=2)
+
+
+def test_decode_all_pages_is_dense():
+    c = replace(configs.DECODE_128K, B=1, L=2048)
+    x = inputs.decode_inputs(c, seed=4, device=DEV)
+    plan = DecodePlan(c.B, c.Hq, c.Hkv, c.L, c.D, c.page, c.L // c.page, x["q"].dtype, DEV)
+    plan.build_metadata(x["k"])
+    plan.run(x["q"], x["k"], x["v"])
+    _sync()
+    q, k, v = (torch.from_numpy(to_np(x[n])) for n in ("q", "k", "v"))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        q[:, :, None], k.repeat_interleave(c.G, 1), v.repeat_interleave(c.G, 1), scale=c.scale)[:, :, 0]
+    check_bf16(to_np(plan.out), ref.numpy(), "dense decode")
+
+
+# ------------------------------------------------------------------ NSA
+def test_nsa_pipeline_small():
+    c = replace(configs.NSA_32K, S=2048 + 64, Hq=16, Hkv=1)
+    x = inputs.nsa_inputs(c, seed=0, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    _sync()
+    q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
+    ck = On.compress(k, c.cmp_len, c.cmp_stride)
+    cv = On.compress(v, c.cmp_len, c.cmp_stride)
+    check_bf16(to_np(plan.ck), ck, "ck")
+    check_bf16(to_np(plan.cv), cv, "cv")
+    # branch 1 on the GPU's own (bf16) summaries, so this checks the attention
+    gck, gcv = to_np(plan.ck), to_np(plan.cv)
+    o1, lse1, p1 = On.cmp_attention(q, gck, gcv, c.cmp_len, c.cmp_stride, c.scale)
+    check_bf16(to_np(plan.o_cmp), o1, "o_cmp")
+    check_lse(to_np(plan.lse_cmp), lse1, 2e-3, "lse_cmp")
+    sc = On.cmp_block_scores(p1, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
+    assert np.abs(to_np(plan.scores) - sc).max() < 1e-6
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    check_indices(sc, gi, gc, c.sel_k, 0, True)
+    o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale)
+    check_bf16(to_np(plan.o_sel), o2, "o_sel")
+    o3, _ = On.window_attention(q, k, v, c.window, c.scale)
+    check_bf16(to_np(plan.o_win), o3, "o_win")
+    out = On.combine(to_np(plan.o_cmp), to_np(plan.o_sel), to_np(plan.o_win), z)
+    check_bf16(to_np(plan.out), out, "combine")
+    # and end to end against the oracle's own chain
+    full = On.combine(o1, o2, o3, z)
+    check_bf16(to_np(plan.out), full, "nsa end to end")
+
+
+def test_nsa_combine_only():
+    rng = torch.Generator().manual_seed(0)
+    o = [torch.randn(1, 4, 100, 128, generator=rng).to(torch.bfloat16) for _ in range(3)]
+    z = torch.randn(1, 100, 4, 3, generator=rng)
+    out = torch.empty_like(o[0], device=DEV)
+    L.dsa_nsa_combine(*(t.to(DEV) for t in o), z.to(DEV), out)
+    _sync()
+    ref = On.combine(*(to_np(t) for t in o), z.numpy())
+    check_bf16(to_np(out), ref, "combine")
