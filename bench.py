@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse attention paths on one MI355X.
+
+Headline (the JSON line's `value`): tokens/s of the whole prefill path —
+pooled block scores, top-k + window selection, block-sparse attention — on
+the bf16 16K workload (B=1, 32 query / 8 KV heads, D=128, S=16384, block 64,
+top-16 blocks + 512-token window), inputs resident in HBM.  The line also
+carries the attention kernel's roofline (effective FLOPs on selected blocks
+against the bf16 MFMA peak), the decode path's HBM rate on the 128K-page
+workload, the long-prefill and three-branch workloads, and the CPU oracle
+timed on a bounded sample of the headline workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--only prefill|decode|long|nsa] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 (no sparsity)
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
+METRIC = "sparse-attn prefill tokens/s + effective TFLOP/s; decode HBM GB/s (1 GPU)"
+
+
+def _timed(fn, iters, torch):
+    """Average ms per call of fn over `iters` back-to-back calls on the
+    current stream (HIP events recorded on that stream)."""
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(iters):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def bench_prefill(args, torch):
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import PrefillPlan
+
+    c = configs.PREFILL_16K
+    x = inputs.prefill_inputs(c, seed=0, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
+    for _ in range(args.warmup):
+        plan.run(q, k, v)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_step = _timed(lambda: plan.run(q, k, v), args.steps, torch)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the kernels one by one, same inputs (outputs rewritten identically)
+    reps = max(args.steps, 10)
+    ms_scores = _timed(lambda: plan.score(q, k), reps, torch)
+    ms_topk = _timed(plan.select, reps, torch)
+    ms_attn = _timed(lambda: plan.attend(q, k, v), reps, torch)
+    count = plan.count.to(torch.int64)
+    sel = int(count.sum().item())                      # (group, query block, key block) triples
+    flops = 4.0 * c.D * c.block * c.block * c.G * sel  # each selected block as a full tile
+    tokens = c.B * c.S
+    return {
+        "cfg": c, "ms_step": ms_step, "wall_s": wall, "ms_scores": ms_scores, "ms_topk": ms_topk,
+        "ms_attn": ms_attn, "selected_block_pairs": sel, "effective_flops": flops,
+        "tokens_per_step": tokens,
+    }
+
+
+def bench_long_prefill(torch, iters=5):
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import PrefillPlan
+
+    c = configs.PREFILL_64K
+    x = inputs.prefill_inputs(c, seed=0, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
+    plan.run(q, k, v)
+    ms_step = _timed(lambda: plan.run(q, k, v), iters, torch)
+    ms_attn = _timed(lambda: plan.attend(q, k, v), iters, torch)
+    sel = int(plan.count.to(torch.int64).sum().item())
+    flops = 4.0 * c.D * c.block * c.block * c.G * sel
+    del x, q, k, v, plan
+    return {"workload": f"{c.name}: B=1 Hq=32 Hkv=8 S=65536 D=128 block=128 top-32 + window 1024, "
+                        "8-cluster keys",
+            "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.S / (ms_step * 1e-3), 1),
+            "attn_ms": round(ms_attn, 4),
+            "attn_effective_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
+            "attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def bench_decode(torch, iters=20, n_query_sets=4):
+    """Decode step on the 128K cache: page bounds -> top 1/20 pages ->
+    attention.  Between timed iterations a 1 GiB buffer is rewritten (not
+    timed) so the last-level cache holds no selected pages, and the query
+    rotates among several sets with their own selections."""
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import DecodePlan
+    from dynamic_block_sparse_head_amd.metrics import decode_selected_bytes
+
+    c = configs.DECODE_128K
+    x = inputs.decode_inputs(c, seed=0, device="cuda")
+    qs = [inputs.decode_inputs(c.__class__(**{**c.__dict__, "L": c.page}), seed=s, device="cuda")["q"]
+          for s in range(1, n_query_sets + 1)]
+    plan = DecodePlan(c.B, c.Hq, c.Hkv, c.L, c.D, c.page, c.topk, x["q"].dtype, "cuda")
+    plan.build_metadata(x["k"])
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+    s = torch.cuda.current_stream()
+    t_step = t_attn = t_meta = 0.0
+    plan.run(qs[0], x["k"], x["v"])
+    for it in range(iters):
+        q = qs[it % n_query_sets]
+        flush.fill_(float(it))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(s)
+        plan.score(q)
+        plan.select()
+        e[1].record(s)
+        plan.attend(q, x["k"], x["v"])
+        e[2].record(s)
+        e[2].synchronize()
+        t_step += e[0].elapsed_time(e[2])
+        t_attn += e[1].elapsed_time(e[2])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    plan.build_metadata(x["k"])
+    e1.record(s)
+    e1.synchronize()
+    t_meta = e0.elapsed_time(e1)
+    ms_step, ms_attn = t_step / iters, t_attn / iters
+    sel_bytes = decode_selected_bytes(c.B, c.Hkv, c.topk, c.page, c.D)
+    meta_bytes = 2 * c.B * c.Hkv * c.n_pages * c.D * 2
+    cache_bytes = 2 * c.B * c.Hkv * c.L * c.D * 2
+    gbs = sel_bytes / (ms_attn * 1e-3) / 1e9
+    del x, qs, plan, flush
+    return {"workload": f"{c.name}: B=16 L=131072 page=64 Hq=32 Hkv=8 D=128, top {c.topk} of "
+                        f"{c.n_pages} pages; LLC flushed between steps",
+            "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.B / (ms_step * 1e-3), 1),
+            "attn_ms": round(ms_attn, 4), "selected_bytes": sel_bytes,
+            "attn_hbm_gbs": round(gbs, 1), "attn_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "step_gbs_incl_metadata": round((sel_bytes + meta_bytes) / (ms_step * 1e-3) / 1e9, 1),
+            "full_cache_bytes": cache_bytes,
+            "page_metadata_build_ms": round(t_meta, 3)}
+
+
+def bench_nsa(torch, iters=5):
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import NSAPlan
+
+    c = configs.NSA_32K
+    x = inputs.nsa_inputs(c, seed=0, device="cuda")
+    p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
+                x["q"].dtype, "cuda")
+    args = (x["q"], x["k"], x["v"], x["z"])
+    p.run(*args)
+    ms = _timed(lambda: p.run(*args), iters, torch)
+    # exact-pair FLOPs of branches 1 and 3, selected-block FLOPs of branch 2
+    S, G, D = c.S, c.G, c.D
+    f1 = sum(max(0, (t - (c.cmp_len - 1)) // c.cmp_stride + 1) if t >= c.cmp_len - 1 else 0
+             for t in range(S)) * 4.0 * D * c.Hq
+    f2 = 4.0 * D * c.sel_block * c.sel_block * G * int(p.count.to(torch.int64).sum().item())
+    f3 = sum(min(t + 1, c.window) for t in range(S)) * 4.0 * D * c.Hq
+    del x, p
+    return {"workload": f"{c.name}: S=32768 Hq=64 Hkv=4 D=128; summaries 32/16, top-16 of 64-token "
+                        "blocks, window 512, sigmoid gates",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(S / (ms * 1e-3), 1),
+            "branch_flops": f1 + f2 + f3,
+            "effective_tflops_whole_step": round((f1 + f2 + f3) / (ms * 1e-3) / 1e12, 2)}
+
+
+def cpu_baseline(budget_s=20.0):
+    """The oracle, untouched, on a bounded sample of the headline workload:
+    pooled scores for every block, then selection and attention (all 32 heads)
+    for query blocks spread over the sequence until the time budget is used."""
+    import numpy as np
+    import torch
+
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from oracle import prefill as Op
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    c = configs.PREFILL_16K
+    x = inputs.prefill_inputs(c, seed=0, device="cpu")
+    t0 = time.perf_counter()
+    q = x["q"].to(torch.float64).numpy()
+    k = x["k"].to(torch.float64).numpy()
+    v = x["v"].to(torch.float64).numpy()
+    s = Op.block_scores_pooled(q, k, c.block)
+    idx, cnt = Op.select_blocks(s, c.topk, c.n_local, causal=True)
+    t_sel = time.perf_counter() - t0
+    order = list(range(c.n_blocks - 1, -1, -7)) + list(range(c.n_blocks - 2, -1, -7))
+    done = 0
+    t1 = time.perf_counter()
+    for i in order:
+        Op.sparse_attention(q, k, v, idx, cnt, c.block, c.scale, q_blocks=[i])
+        done += 1
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_attn = time.perf_counter() - t1
+    per_block = t_attn / done
+    est_total = t_sel + per_block * c.n_blocks          # the whole workload at this rate
+    return {"value": round(c.S / est_total, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{c.name}: float64 numpy oracle; scores + selection for all {c.n_blocks} "
+                       f"query blocks ({t_sel:.1f} s), attention for {done} of {c.n_blocks} query "
+                       f"blocks (all 32 heads, {t_attn:.1f} s); tokens/s = S / (selection time + "
+                       f"per-block attention time x {c.n_blocks}); BLAS threads {threads}, "
+                       f"host cpus {len(os.sched_getaffinity(0))}")}
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=3):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa"], default=None)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this library's "
+              "paths run on a single MI355X; multi-GPU sharding is a design note, not a run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    from dynamic_block_sparse_head_amd import binding
+    binding.load()
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    extra = {}
+    if args.only in (None, "prefill"):
+        r = bench_prefill(args, torch)
+        c = r["cfg"]
+        tflops = r["effective_flops"] / (r["ms_attn"] * 1e-3) / 1e12
+        line = {
+            "metric": METRIC,
+            "value": round(r["tokens_per_step"] / (r["ms_step"] * 1e-3), 1),
+            "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(r["ms_step"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{c.name}: B=1 Hq=32 Hkv=8 S=16384 D=128 block=64 top-16 + "
+                                   "window 512 (scores + selection + attention)",
+                       "global_batch": c.B, "seq_len": c.S, "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "kernel": "k_attn_bf16",
+                         "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": None,
+                         "flops_per_launch": r["effective_flops"],
+                         "avg_launch_ms": round(r["ms_attn"], 4)},
+            "prefill": {"scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
+                        "attn_ms": round(r["ms_attn"], 4),
+                        "attn_tokens_per_s": round(c.S / (r["ms_attn"] * 1e-3), 1),
+                        "selected_block_pairs": r["selected_block_pairs"],
+                        "effective_tflops": round(tflops, 2)},
+        }
+    else:
+        line = {"metric": METRIC, "n_gpus": 1}
+    if args.only in (None, "decode"):
+        extra["decode"] = bench_decode(torch)
+    if args.only in (None, "long"):
+        extra["long_prefill"] = bench_long_prefill(torch)
+    if args.only in (None, "nsa"):
+        extra["nsa"] = bench_nsa(torch)
+    line.update(extra)
+    if not args.no_cpu_baseline and args.only in (None, "prefill"):
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
