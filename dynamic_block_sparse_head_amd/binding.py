@@ -13,7 +13,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# DSA_LIBRARY may name another build of the same library (e.g. a tuning variant)
+LIB_PATH = os.environ.get("DSA_LIBRARY", os.path.join(_HERE, "libdsa.so"))
 
 DSA_OK, DSA_E_ARG, DSA_E_UNSUPPORTED, DSA_E_WORKSPACE, DSA_E_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16 = 0, 1

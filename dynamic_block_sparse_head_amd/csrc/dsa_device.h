@@ -37,6 +37,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer descriptor over `bytes` bytes from `base`: buffer loads at byte
+// offsets outside [0, bytes) return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes), 0x00020000);
+}
+
 // Work-item order that keeps consecutive work ids on one XCD: the hardware
 // hands workgroup b to XCD b % 8, so id = (b % 8) * per_xcd + b / 8 puts a
 // contiguous range of work on each die (its L2 then serves their shared K/V).

@@ -27,6 +27,23 @@
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
+// Query rows per workgroup = DSA_ATTN_NW waves x 32 x DSA_ATTN_QT.
+#ifndef DSA_ATTN_NW
+#define DSA_ATTN_NW 8
+#endif
+#ifndef DSA_ATTN_QT
+#define DSA_ATTN_QT 1
+#endif
+// Wave priority while issuing matrix instructions (0 = no change): a wave
+// in its MFMA phase wins issue over a wave doing softmax on the same SIMD.
+#ifndef DSA_ATTN_PRIO
+#define DSA_ATTN_PRIO 1
+#endif
+// Minimum waves per SIMD the register allocation must allow.
+#ifndef DSA_ATTN_WAVES_PER_EU
+#define DSA_ATTN_WAVES_PER_EU 2
+#endif
+
 namespace dsa {
 namespace {
 
@@ -91,17 +108,53 @@ __device__ __forceinline__ int make_tiles(const AttnArgs& a, int bg, int i, int 
   return c_hi / kt + 1;
 }
 
+// Keys visible to row t form one interval [lo, hi] in every mode (within a
+// selected block in index mode); an empty interval has hi < lo.
+__device__ __forceinline__ void row_range(const AttnArgs& a, int t, int& lo, int& hi) {
+  if (a.mode == MODE_INDEX) {
+    lo = 0;
+    hi = min(t, a.Skv - 1);
+  } else if (a.mode == MODE_WINDOW) {
+    lo = max(0, t - a.window + 1);
+    hi = min(t, a.Skv - 1);
+  } else {
+    lo = 0;
+    hi = t >= a.cmp_len - 1 ? min(a.Skv - 1, (t - (a.cmp_len - 1)) / a.cmp_stride) : -1;
+  }
+}
+
 // ------------------------------------------------------------------ bf16
+// The two 32-lane halves of a wave hold the same 32 query columns; this
+// returns (value of lane l%32, value of lane 32 + l%32) on every lane.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A row's running maximum is only moved (and its accumulators rescaled)
+// when a new logit exceeds it by more than this many powers of two; until
+// then probabilities are exp2 of at most this value.  The result is the
+// same softmax: numerator and denominator share the reference maximum.
+constexpr float kLazyRescale = 8.0f;
+
 template <int D, int KT, int QT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
+void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
                                                        int per_xcd, int total) {
   constexpr int NT = NW * 64;
   constexpr int ROWS = NW * 32 * QT;
-  constexpr int KSTR = D + 8;   // bf16 elements per K row in LDS (16 B pad)
-  constexpr int VSTR = KT + 8;  // bf16 elements per V^T row in LDS (16 B pad)
+  constexpr int KSTR = D + 8;   // bf16 elements per K row in LDS (16 B pad: conflict-free reads)
+  constexpr int VSTR = KT + 8;  // bf16 elements per V^T row in LDS
   constexpr int CPR = D / 8;    // 16-byte chunks per row
-  constexpr int NCHUNK = KT * CPR;
-  constexpr int CH = (NCHUNK + NT - 1) / NT;  // 16-byte chunks per thread per tile
+  constexpr int KCH = KT * CPR; // K chunks per tile
+  constexpr int KCT = (KCH + NT - 1) / NT;
+  constexpr int NKG = KT / 4;   // 4-key groups per tile
+  constexpr int VGR = NKG * CPR;  // V groups (4 keys x 8 dims) per tile
+  constexpr int VGT = (VGR + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VSTR];
 
@@ -120,8 +173,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb
   const int col = lane & 31, half = lane >> 5;
 
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D;
-  const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D;
+  // K/V of this KV head through buffer descriptors: loads outside the
+  // group's rows (ragged tails, padding) return zeros without a branch
+  const uint32_t kv_bytes = uint32_t(a.Skv) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D, kv_bytes);
 
   int row_t[QT], row_h[QT];
   bool row_ok[QT];
@@ -147,50 +203,88 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb
 
   floatx16 o[QT][D / 32];
   float m[QT], l[QT];
+  int row_lo[QT], row_hi[QT];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
     m[qt] = -__builtin_inff();
     l[qt] = 0.f;
+    row_range(a, row_t[qt], row_lo[qt], row_hi[qt]);
+    // relative to this lane's key offset inside a 32-key accumulator tile
+    row_lo[qt] -= half * 4;
+    row_hi[qt] -= half * 4;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[qt][dt][r] = 0.f;
   }
+  // a tile needs no mask when every key is visible to every row of the block
+  int blk_lo, blk_hi, dummy;
+  row_range(a, t1, blk_lo, dummy);
+  row_range(a, t0, dummy, blk_hi);
 
   TileSpec ts;
   const int ntiles = make_tiles(a, bg, i, t0, t1, KT, ts);
   const float c = a.scale * kLog2e;
 
-  u32x4 kreg[CH], vreg[CH];
-  auto gload = [&](int n) {
-    const int key0 = tile_key0(ts, n);
+  // K: one 16-byte chunk per (key, 8 dims).  V: four keys x 8 dims per
+  // thread, so the transposed store writes 4 consecutive keys (8 bytes) of
+  // one V^T row; the 16 lanes of a row group write 16 different key groups
+  // (conflict-free).
+  u32x4 kreg[KCT];
+  u32x4 vreg[VGT][4];
+  // per-thread byte offsets inside a tile; the tile's start is a scalar offset
+  uint32_t koff[KCT], voff[VGT];
 #pragma unroll
-    for (int ch = 0; ch < CH; ++ch) {
-      const int e = threadIdx.x + ch * NT;
-      const int key = key0 + e / CPR, dc = e % CPR;
-      if ((NCHUNK % NT == 0 || e < NCHUNK) && key >= 0 && key < a.Skv) {
-        kreg[ch] = *reinterpret_cast<const u32x4*>(kp + size_t(key) * D + dc * 8);
-        vreg[ch] = *reinterpret_cast<const u32x4*>(vp + size_t(key) * D + dc * 8);
-      } else {
-        kreg[ch] = u32x4{0u, 0u, 0u, 0u};
-        vreg[ch] = u32x4{0u, 0u, 0u, 0u};
-      }
+  for (int ch = 0; ch < KCT; ++ch) {
+    const int e = threadIdx.x + ch * NT;
+    koff[ch] = uint32_t((e / CPR) * D + (e % CPR) * 8) * 2u;
+  }
+#pragma unroll
+  for (int ch = 0; ch < VGT; ++ch) {
+    const int e = threadIdx.x + ch * NT;
+    voff[ch] = uint32_t(((e % NKG) * 4) * D + (e / NKG) * 8) * 2u;
+  }
+  auto gload = [&](int n) {
+    const uint32_t base = uint32_t(tile_key0(ts, n)) * uint32_t(D * 2);  // wraps for key < 0: reads 0
+#pragma unroll
+    for (int ch = 0; ch < KCT; ++ch) {
+      if (KCH % NT != 0 && int(threadIdx.x) + ch * NT >= KCH) break;
+      kreg[ch] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[ch], base, 0);
+    }
+#pragma unroll
+    for (int ch = 0; ch < VGT; ++ch) {
+      if (VGR % NT != 0 && int(threadIdx.x) + ch * NT >= VGR) break;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vreg[ch][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[ch] + j * D * 2, base, 0);
     }
   };
   auto swrite = [&](int buf) {
 #pragma unroll
-    for (int ch = 0; ch < CH; ++ch) {
+    for (int ch = 0; ch < KCT; ++ch) {
       const int e = threadIdx.x + ch * NT;
-      if (NCHUNK % NT != 0 && e >= NCHUNK) break;
-      const int key = e / CPR, dc = e % CPR;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][key * KSTR + dc * 8]) = kreg[ch];
-      // V^T with bits 2 and 3 of the key offset swapped (see header comment)
-      const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+      if (KCH % NT != 0 && e >= KCH) break;
+      *reinterpret_cast<u32x4*>(&k_lds[buf][(e / CPR) * KSTR + (e % CPR) * 8]) = kreg[ch];
+    }
+#pragma unroll
+    for (int ch = 0; ch < VGT; ++ch) {
+      const int e = threadIdx.x + ch * NT;
+      if (VGR % NT != 0 && e >= VGR) break;
+      const int kg = e % NKG, dc = e / NKG;
+      // key offset -> position with bits 2 and 3 swapped, so the 8 keys one
+      // lane feeds to the P.V product are adjacent in its V^T row
+      const int k4 = kg * 4;
+      const int pos = (k4 & ~12) | ((k4 & 4) << 1) | ((k4 & 8) >> 1);
       uint16_t* vt = &v_lds[buf][dc * 8 * VSTR + pos];
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        vt[(2 * e2) * VSTR] = uint16_t(vreg[ch][e2] & 0xffffu);
-        vt[(2 * e2 + 1) * VSTR] = uint16_t(vreg[ch][e2] >> 16);
+      for (int x = 0; x < 4; ++x) {   // dims dc*8 + 2x (low halves) and 2x+1 (high halves)
+        u32x2 lo2, hi2;
+        lo2[0] = __builtin_amdgcn_perm(vreg[ch][1][x], vreg[ch][0][x], 0x05040100u);
+        lo2[1] = __builtin_amdgcn_perm(vreg[ch][3][x], vreg[ch][2][x], 0x05040100u);
+        hi2[0] = __builtin_amdgcn_perm(vreg[ch][1][x], vreg[ch][0][x], 0x07060302u);
+        hi2[1] = __builtin_amdgcn_perm(vreg[ch][3][x], vreg[ch][2][x], 0x07060302u);
+        *reinterpret_cast<u32x2*>(vt + (2 * x) * VSTR) = lo2;
+        *reinterpret_cast<u32x2*>(vt + (2 * x + 1) * VSTR) = hi2;
       }
     }
   };
@@ -212,10 +306,11 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][qt][r] = 0.f;
+    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
 #pragma unroll
-    for (int kt = 0; kt < KT / 32; ++kt) {
+    for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+      for (int kt = 0; kt < KT / 32; ++kt) {
         const bf16x8 ka =
             *reinterpret_cast<const bf16x8*>(&k_lds[buf][(kt * 32 + col) * KSTR + ks * 16 + half * 8]);
 #pragma unroll
@@ -224,19 +319,23 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     const int key0 = tile_key0(ts, n);
-    if (!tile_full(ts, key0, t0, t1)) {
+    if (key0 < blk_lo || key0 + KT - 1 > blk_hi) {   // wave-uniform
 #pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
+      for (int qt = 0; qt < QT; ++qt) {
+        const int lo = row_lo[qt] - key0, hi = row_hi[qt] - key0;
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
+        for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            if (!visible(ts, row_t[qt], key)) s[kt][qt][r] = -__builtin_inff();
+            const int off = kt * 32 + (r >> 2) * 8 + (r & 3);
+            s[kt][qt][r] = (off < lo || off > hi) ? -__builtin_inff() : s[kt][qt][r];
           }
+      }
     }
 
+    bf16x8 pb[KT / 16][QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       float mx = -__builtin_inff();
@@ -244,44 +343,47 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb
       for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m[qt], mx * c);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = fast_exp2(m[qt] - m_use);
-      m[qt] = m_new;
+      const float mt = half_max(mx) * c;
+      const bool grow = mt > m[qt] + kLazyRescale;
+      if (__any(grow)) {
+        // lanes that do not grow keep alpha = 1 (their m may still be -inf)
+        const float alpha = grow ? fast_exp2(m[qt] - mt) : 1.f;   // 0 when m was -inf
+        const float m_new = grow ? mt : m[qt];
+        m[qt] = m_new;
+        l[qt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[qt][dt][r] *= alpha;
+      }
+      const float mu = (m[qt] == -__builtin_inff()) ? 0.f : m[qt];
       float ls = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
+      for (int ks = 0; ks < KT / 16; ++ks) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kt][qt][r], c, -m_use));
-          s[kt][qt][r] = p;
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(fmaf(s[ks >> 1][qt][(ks & 1) * 8 + e], c, -mu));
           ls += p;
+          pb[ks][qt][e] = static_cast<__bf16>(p);
         }
-      l[qt] = l[qt] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[qt][dt][r] *= alpha;
+      }
+      l[qt] += ls;
     }
 
+    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
-      bf16x8 pb[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[qt][e] = static_cast<__bf16>(s[ks >> 1][qt][(ks & 1) * 8 + e]);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const bf16x8 va =
             *reinterpret_cast<const bf16x8*>(&v_lds[buf][(dt * 32 + col) * VSTR + ks * 16 + half * 8]);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
-          o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qt], o[qt][dt], 0, 0, 0);
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[ks][qt], o[qt][dt], 0, 0, 0);
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     if (n + 1 < ntiles) swrite(buf ^ 1);
     __syncthreads();
   }
@@ -289,7 +391,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_bf16(AttnArgs a, int wg_per_qb
   uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float lt = l[qt] + __shfl_xor(l[qt], 32);
+    const float lt = half_sum(l[qt]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (!row_ok[qt]) continue;
     uint16_t* dst = op + ((size_t(b) * a.Hq + row_h[qt]) * a.S + row_t[qt]) * D;
@@ -397,8 +499,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   // key tile = 64 keys unless index-mode blocks are 32 tokens long
   const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
-  if (a.D == 128) return kt32 ? run_bf16<128, 32, 1, 8>(a, s) : run_bf16<128, 64, 1, 8>(a, s);
-  return kt32 ? run_bf16<64, 32, 1, 8>(a, s) : run_bf16<64, 64, 1, 8>(a, s);
+  if (a.D == 128)
+    return kt32 ? run_bf16<128, 32, DSA_ATTN_QT, DSA_ATTN_NW>(a, s)
+                : run_bf16<128, 64, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
+  return kt32 ? run_bf16<64, 32, DSA_ATTN_QT, DSA_ATTN_NW>(a, s)
+              : run_bf16<64, 64, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
 }
 
 }  // namespace dsa
