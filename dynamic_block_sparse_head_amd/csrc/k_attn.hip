@@ -230,8 +230,10 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
   // thread, so the transposed store writes 4 consecutive keys (8 bytes) of
   // one V^T row; the 16 lanes of a row group write 16 different key groups
   // (conflict-free).
-  u32x4 kreg[KCT];
-  u32x4 vreg[VGT][4];
+  struct Stage {
+    u32x4 k[KCT];
+    u32x4 v[VGT][4];
+  };
   // per-thread byte offsets inside a tile; the tile's start is a scalar offset
   uint32_t koff[KCT], voff[VGT];
 #pragma unroll
@@ -244,27 +246,27 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
     const int e = threadIdx.x + ch * NT;
     voff[ch] = uint32_t(((e % NKG) * 4) * D + (e / NKG) * 8) * 2u;
   }
-  auto gload = [&](int n) {
+  auto gload = [&](int n, Stage& st) {
     const uint32_t base = uint32_t(tile_key0(ts, n)) * uint32_t(D * 2);  // wraps for key < 0: reads 0
 #pragma unroll
     for (int ch = 0; ch < KCT; ++ch) {
       if (KCH % NT != 0 && int(threadIdx.x) + ch * NT >= KCH) break;
-      kreg[ch] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[ch], base, 0);
+      st.k[ch] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff[ch], base, 0);
     }
 #pragma unroll
     for (int ch = 0; ch < VGT; ++ch) {
       if (VGR % NT != 0 && int(threadIdx.x) + ch * NT >= VGR) break;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        vreg[ch][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[ch] + j * D * 2, base, 0);
+        st.v[ch][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[ch] + j * D * 2, base, 0);
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int ch = 0; ch < KCT; ++ch) {
       const int e = threadIdx.x + ch * NT;
       if (KCH % NT != 0 && e >= KCH) break;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][(e / CPR) * KSTR + (e % CPR) * 8]) = kreg[ch];
+      *reinterpret_cast<u32x4*>(&k_lds[buf][(e / CPR) * KSTR + (e % CPR) * 8]) = st.k[ch];
     }
 #pragma unroll
     for (int ch = 0; ch < VGT; ++ch) {
@@ -279,26 +281,18 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
 #pragma unroll
       for (int x = 0; x < 4; ++x) {   // dims dc*8 + 2x (low halves) and 2x+1 (high halves)
         u32x2 lo2, hi2;
-        lo2[0] = __builtin_amdgcn_perm(vreg[ch][1][x], vreg[ch][0][x], 0x05040100u);
-        lo2[1] = __builtin_amdgcn_perm(vreg[ch][3][x], vreg[ch][2][x], 0x05040100u);
-        hi2[0] = __builtin_amdgcn_perm(vreg[ch][1][x], vreg[ch][0][x], 0x07060302u);
-        hi2[1] = __builtin_amdgcn_perm(vreg[ch][3][x], vreg[ch][2][x], 0x07060302u);
+        lo2[0] = __builtin_amdgcn_perm(st.v[ch][1][x], st.v[ch][0][x], 0x05040100u);
+        lo2[1] = __builtin_amdgcn_perm(st.v[ch][3][x], st.v[ch][2][x], 0x05040100u);
+        hi2[0] = __builtin_amdgcn_perm(st.v[ch][1][x], st.v[ch][0][x], 0x07060302u);
+        hi2[1] = __builtin_amdgcn_perm(st.v[ch][3][x], st.v[ch][2][x], 0x07060302u);
         *reinterpret_cast<u32x2*>(vt + (2 * x) * VSTR) = lo2;
         *reinterpret_cast<u32x2*>(vt + (2 * x + 1) * VSTR) = hi2;
       }
     }
   };
 
-  if (ntiles > 0) {
-    gload(0);
-    swrite(0);
-  }
-  __syncthreads();
-
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
-    if (n + 1 < ntiles) gload(n + 1);
-
+  // one tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T
+  auto tile = [&](int n, int buf) {
     floatx16 s[KT / 32][QT];
 #pragma unroll
     for (int kt = 0; kt < KT / 32; ++kt)
@@ -384,7 +378,26 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
     }
 
     __builtin_amdgcn_s_setprio(0);
-    if (n + 1 < ntiles) swrite(buf ^ 1);
+  };
+
+  // Global loads run two tiles ahead of the math through two register
+  // stages (A holds even tiles, B odd ones); LDS is double-buffered.
+  Stage A, B;
+  if (ntiles > 0) {
+    gload(0, A);
+    if (ntiles > 1) gload(1, B);
+    swrite(A, 0);
+  }
+  __syncthreads();
+  for (int n = 0; n < ntiles; n += 2) {
+    if (n + 2 < ntiles) gload(n + 2, A);
+    tile(n, 0);
+    if (n + 1 < ntiles) swrite(B, 1);
+    __syncthreads();
+    if (n + 1 >= ntiles) break;
+    if (n + 3 < ntiles) gload(n + 3, B);
+    tile(n + 1, 1);
+    if (n + 2 < ntiles) swrite(A, 0);
     __syncthreads();
   }
 
@@ -499,6 +512,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   // key tile = 64 keys unless index-mode blocks are 32 tokens long
   const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
+#ifdef DSA_ATTN_KT128
+  if (a.D == 128 && a.mode == MODE_INDEX && a.block % 128 == 0)
+    return run_bf16<128, 128, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
+#endif
   if (a.D == 128)
     return kt32 ? run_bf16<128, 32, DSA_ATTN_QT, DSA_ATTN_NW>(a, s)
                 : run_bf16<128, 64, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);

@@ -29,11 +29,23 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
   }
 }
 
+// Sum over the 16 lanes of a DPP row (every lane gets the total).
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // half-row mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
+  return x;
+}
+
+constexpr int kUnroll = 8;   // token rows in flight per thread
+
 // grid (nsplit, B*Hkv)
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsplit, int ppsplit) {
   constexpr int CPR = D / 8;              // lanes per token row (8 dims each)
-  constexpr int TPI = kThreads / CPR;     // tokens per iteration
+  constexpr int TPI = kThreads / CPR;     // tokens per pass
+  static_assert(CPR == 16 || CPR == 8, "row reduction assumes 8 or 16 lanes per token");
   __shared__ float sc[G][kMaxTok];
   __shared__ float red[TPI][G][D];
   __shared__ float stat[G][2];
@@ -48,8 +60,12 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
   const int dc = threadIdx.x % CPR, tg = threadIdx.x / CPR;
   const float c = a.scale * kLog2e;
 
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + size_t(bg) * a.L * D;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + size_t(bg) * a.L * D;
+  // K and V of this (sequence, KV head): out-of-range pages read as zeros
+  const uint32_t kv_bytes = uint32_t(a.L) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.L * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(bg) * a.L * D, kv_bytes);
   const int32_t* pages = a.idx + size_t(bg) * a.idx_width + p0;
 
   float q[G][8];
@@ -59,22 +75,40 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
                                                     (size_t(b) * a.Hq + g * G + h) * D + dc * 8);
     unpack8(w, q[h]);
   }
+  // byte offset of a token row inside the cache (page validity folded in)
+  auto row_off = [&](int tok, bool& ok) -> uint32_t {
+    const int pg = tok < ntok ? pages[tok / a.page] : -1;
+    ok = pg >= 0 && pg < n_pages;
+    return ok ? uint32_t((pg * a.page + tok % a.page) * D + dc * 8) * 2u : 0xffffffffu;
+  };
 
   // scores of every token of the chunk, for every head
-  for (int tok = tg; tok < ntok; tok += TPI) {
-    const int pg = pages[tok / a.page];
-    const bool okp = pg >= 0 && pg < n_pages;   // a page outside the cache is skipped
-    float kf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (okp)
-      unpack8(*reinterpret_cast<const u32x4*>(kbase + (size_t(pg) * a.page + tok % a.page) * D + dc * 8), kf);
+  for (int base = 0; base < ntok; base += TPI * kUnroll) {
+    u32x4 kw[kUnroll];
+    bool ok[kUnroll];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float s = 0.f;
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t off = row_off(base + u * TPI + tg, ok[u]);
+      kw[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(q[h][e], kf[e], s);
+    for (int u = 0; u < kUnroll; ++u) {
+      float kf[8];
+      unpack8(kw[u], kf);
 #pragma unroll
-      for (int o = CPR / 2; o > 0; o /= 2) s += __shfl_xor(s, o);
-      if (dc == 0) sc[h][tok] = okp ? s * c : -__builtin_inff();
+      for (int h = 0; h < G; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = fmaf(q[h][e], kf[e], s);
+        s = (CPR == 16) ? row16_sum(s) : s;
+        if (CPR == 8) {
+          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
+          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
+          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x141, 0xF, 0xF, false));
+        }
+        const int tok = base + u * TPI + tg;
+        if (dc == 0 && tok < ntok) sc[h][tok] = ok[u] ? s * c : -__builtin_inff();
+      }
     }
   }
   __syncthreads();
@@ -108,16 +142,26 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  for (int tok = tg; tok < ntok; tok += TPI) {
-    const int pg = pages[tok / a.page];
-    if (pg < 0 || pg >= n_pages) continue;
-    float vf[8];
-    unpack8(*reinterpret_cast<const u32x4*>(vbase + (size_t(pg) * a.page + tok % a.page) * D + dc * 8), vf);
+  for (int base = 0; base < ntok; base += TPI * kUnroll) {
+    u32x4 vw[kUnroll];
+    bool ok[kUnroll];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = sc[h][tok];
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t off = row_off(base + u * TPI + tg, ok[u]);
+      vw[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int tok = base + u * TPI + tg;
+      if (!ok[u]) continue;
+      float vf[8];
+      unpack8(vw[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = sc[h][tok];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
     }
   }
 #pragma unroll
