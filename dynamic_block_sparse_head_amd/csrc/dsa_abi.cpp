@@ -243,8 +243,8 @@ int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const 
   const int G = Hq / Hkv;
   REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, DSA_E_UNSUPPORTED,
           "decode supports 1, 2, 4 or 8 query heads per KV head (got %d)", G);
-  REQUIRE(page >= 32 && page % 32 == 0 && page <= 512, DSA_E_UNSUPPORTED,
-          "page %d not supported (a multiple of 32, at most 512)", page);
+  REQUIRE(page == 32 || page == 64 || page == 128 || page == 256 || page == 512, DSA_E_UNSUPPORTED,
+          "page %d not supported (32, 64, 128, 256 or 512)", page);
   REQUIRE(L >= page && L % page == 0, DSA_E_ARG, "L (%d) must be a positive multiple of page (%d)",
           L, page);
   REQUIRE(idx_width >= 1 && idx_width <= L / page, DSA_E_ARG,

@@ -6,10 +6,10 @@
 // streamed with coalesced 16-byte loads.
 //
 // Work split: every (sequence, KV group) row of selected pages is cut into
-// chunks of 512 tokens' worth of pages; one workgroup per chunk computes, for the
-// group's G query heads, the chunk's running max, exp-sum and unnormalised
-// weighted value sum.  A merge kernel combines the chunks of each
-// (sequence, head) in chunk order (deterministic, no atomics).
+// chunks of up to 512 tokens' worth of pages; one workgroup per chunk
+// computes, for the group's G query heads, the chunk's running max, exp-sum
+// and unnormalised weighted value sum.  A merge kernel combines the chunks
+// of each (sequence, head) in chunk order (deterministic, no atomics).
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -18,6 +18,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxTok = 512;   // tokens per workgroup: 8 pages of 64, 4 of 128, ...
+constexpr int kBatch = 4;      // token rows per thread per pipeline stage
 
 int pages_per_split(int page) { return page >= kMaxTok ? 1 : kMaxTok / page; }
 
@@ -29,195 +30,230 @@ __device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
   }
 }
 
-// Sum over the 16 lanes of a DPP row (every lane gets the total).
-__device__ __forceinline__ float row16_sum(float x) {
+// Sum over the N (8 or 16) lanes of a DPP row group; every lane gets the total.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // half-row mirror
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
+  if (N == 16)
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
   return x;
 }
 
-constexpr int kUnroll = 8;   // token rows in flight per thread
-
-// grid (nsplit, B*Hkv)
-template <int D, int G>
+// grid (nsplit, B*Hkv).  The chunk's tokens are walked in slabs of
+// kBatch * NG consecutive tokens; group tg of D/8 lanes takes rows
+// tg, tg + NG, ... of each slab, with an online softmax.  Page numbers are
+// uniform per row of a slab (pages are whole multiples of NG tokens), so
+// every load is a buffer load with a per-thread constant offset plus a
+// scalar row offset; the next slab's K and V are in flight while the
+// current one is used.  The NG group partials are merged in LDS in order.
+template <int D, int G, int PAGE>
 __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsplit, int ppsplit) {
   constexpr int CPR = D / 8;              // lanes per token row (8 dims each)
-  constexpr int TPI = kThreads / CPR;     // tokens per pass
+  constexpr int NG = kThreads / CPR;      // token groups
+  constexpr int SLAB = kBatch * NG;       // tokens per pipeline stage
   static_assert(CPR == 16 || CPR == 8, "row reduction assumes 8 or 16 lanes per token");
-  __shared__ float sc[G][kMaxTok];
-  __shared__ float red[TPI][G][D];
-  __shared__ float stat[G][2];
+  static_assert(PAGE % NG == 0, "a page holds whole rows of token groups");
+  __shared__ float g_m[NG][G], g_l[NG][G];
+  __shared__ float g_acc[NG][G][D];
 
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int cnt = min(a.count[bg], a.idx_width);
-  const int n_pages = a.L / a.page;
+  const int n_pages = a.L / PAGE;
   const int p0 = split * ppsplit;
   const int np = max(0, min(cnt, p0 + ppsplit) - p0);
-  const int ntok = np * a.page;
+  const int ntok = np * PAGE;
   const int dc = threadIdx.x % CPR, tg = threadIdx.x / CPR;
   const float c = a.scale * kLog2e;
+  const int32_t* pages = a.idx + size_t(bg) * a.idx_width + p0;
 
-  // K and V of this (sequence, KV head): out-of-range pages read as zeros
+  // K and V of this (sequence, KV head); a missing token reads zeros
   const uint32_t kv_bytes = uint32_t(a.L) * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.L * D, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs =
       make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(bg) * a.L * D, kv_bytes);
-  const int32_t* pages = a.idx + size_t(bg) * a.idx_width + p0;
+  const uint32_t lane_off = uint32_t(tg * D + dc * 8) * 2u;
 
+  // query rows pre-scaled by scale*log2(e) (float32), so scores are in log2 units
   float q[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.q) +
                                                     (size_t(b) * a.Hq + g * G + h) * D + dc * 8);
     unpack8(w, q[h]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[h][e] *= c;
   }
-  // byte offset of a token row inside the cache (page validity folded in)
-  auto row_off = [&](int tok, bool& ok) -> uint32_t {
-    const int pg = tok < ntok ? pages[tok / a.page] : -1;
-    ok = pg >= 0 && pg < n_pages;
-    return ok ? uint32_t((pg * a.page + tok % a.page) * D + dc * 8) * 2u : 0xffffffffu;
+
+  // scalar byte offset of row block u of slab sl (0xffffffff: absent, reads zeros)
+  auto row_base = [&](int sl, int u) -> uint32_t {
+    const int t = sl * SLAB + u * NG;               // first token of this row block
+    if (t >= ntok) return 0xffffffffu;
+    const int pg = pages[t / PAGE];
+    if (pg < 0 || pg >= n_pages) return 0xffffffffu;
+    return uint32_t(pg * PAGE + t % PAGE) * uint32_t(D * 2);
   };
 
-  // scores of every token of the chunk, for every head
-  for (int base = 0; base < ntok; base += TPI * kUnroll) {
-    u32x4 kw[kUnroll];
-    bool ok[kUnroll];
+  float m[G], l[G], acc[G][8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t off = row_off(base + u * TPI + tg, ok[u]);
-      kw[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+  for (int h = 0; h < G; ++h) {
+    m[h] = -__builtin_inff();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  }
+
+  struct Batch {
+    u32x4 k[kBatch], v[kBatch];
+    uint32_t base[kBatch];
+  };
+  auto fetch = [&](int sl, Batch& bt) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      bt.base[u] = row_base(sl, u);
+      bt.k[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, bt.base[u], 0);
+      bt.v[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, bt.base[u], 0);
     }
+  };
+  auto consume = [&](const Batch& bt) {
+    float sc[kBatch][G];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       float kf[8];
-      unpack8(kw[u], kf);
+      unpack8(bt.k[u], kf);
+      const bool ok = bt.base[u] != 0xffffffffu;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float s = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = fmaf(q[h][e], kf[e], s);
-        s = (CPR == 16) ? row16_sum(s) : s;
-        if (CPR == 8) {
-          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0xB1, 0xF, 0xF, false));
-          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x4E, 0xF, 0xF, false));
-          s += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s), 0x141, 0xF, 0xF, false));
-        }
-        const int tok = base + u * TPI + tg;
-        if (dc == 0 && tok < ntok) sc[h][tok] = ok[u] ? s * c : -__builtin_inff();
+        s = row_sum<CPR>(s);
+        sc[u][h] = ok ? s : -__builtin_inff();
       }
     }
-  }
-  __syncthreads();
-
-  // per-head max and exp-sum (one wave per head, fixed order)
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int h = wave; h < G; h += kThreads / 64) {
-    float mx = -__builtin_inff();
-    for (int t = lane; t < ntok; t += 64) mx = fmaxf(mx, sc[h][t]);
 #pragma unroll
-    for (int o = 32; o > 0; o /= 2) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float mu = (mx == -__builtin_inff()) ? 0.f : mx;
-    float ls = 0.f;
-    for (int t = lane; t < ntok; t += 64) {
-      const float p = fast_exp2(sc[h][t] - mu);
-      sc[h][t] = p;
-      ls += p;
+    for (int h = 0; h < G; ++h) {
+      float mt = sc[0][h];
+#pragma unroll
+      for (int u = 1; u < kBatch; ++u) mt = fmaxf(mt, sc[u][h]);
+      if (mt > m[h]) {   // uniform across the lanes of a token group
+        const float alpha = fast_exp2(m[h] - mt);
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        m[h] = mt;
+      }
     }
 #pragma unroll
-    for (int o = 32; o > 0; o /= 2) ls += __shfl_xor(ls, o);
-    if (lane == 0) {
-      stat[h][0] = mx;
-      stat[h][1] = ls;
-    }
-  }
-  __syncthreads();
-
-  // weighted value sums
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  for (int base = 0; base < ntok; base += TPI * kUnroll) {
-    u32x4 vw[kUnroll];
-    bool ok[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t off = row_off(base + u * TPI + tg, ok[u]);
-      vw[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tok = base + u * TPI + tg;
-      if (!ok[u]) continue;
+    for (int u = 0; u < kBatch; ++u) {
       float vf[8];
-      unpack8(vw[u], vf);
+      unpack8(bt.v[u], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = sc[h][tok];
+        const float p = fast_exp2(sc[u][h] - (m[h] == -__builtin_inff() ? 0.f : m[h]));
+        l[h] += p;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
       }
     }
+  };
+
+  const int nslab = (ntok + SLAB - 1) / SLAB;
+  Batch A, B;
+  if (nslab > 0) fetch(0, A);
+  for (int sl = 0; sl < nslab; sl += 2) {
+    if (sl + 1 < nslab) fetch(sl + 1, B);
+    consume(A);
+    if (sl + 1 >= nslab) break;
+    if (sl + 2 < nslab) fetch(sl + 2, A);
+    consume(B);
+  }
+
+  if (dc == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      g_m[tg][h] = m[h];
+      g_l[tg][h] = l[h];
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[tg][h][dc * 8 + e] = acc[h][e];
+    for (int e = 0; e < 8; ++e) g_acc[tg][h][dc * 8 + e] = acc[h][e];
   __syncthreads();
 
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const int h = e / D, d = e % D;
-    float s = 0.f;
-    for (int t = 0; t < TPI; ++t) s += red[t][h][d];
+    float M = -__builtin_inff();
+    for (int t = 0; t < NG; ++t) M = fmaxf(M, g_m[t][h]);
+    float Ls = 0.f, O = 0.f;
+    if (M != -__builtin_inff()) {
+      for (int t = 0; t < NG; ++t) {
+        const float w = fast_exp2(g_m[t][h] - M);
+        Ls = fmaf(g_l[t][h], w, Ls);
+        O = fmaf(g_acc[t][h][d], w, O);
+      }
+    }
     float* part = a.partial + ((size_t(b) * a.Hq + g * G + h) * nsplit + split) * (D + 2);
-    part[d] = s;
+    part[d] = O;
     if (d == 0) {
-      part[D] = ntok > 0 ? stat[h][0] : -__builtin_inff();
-      part[D + 1] = ntok > 0 ? stat[h][1] : 0.f;
+      part[D] = M;
+      part[D + 1] = Ls;
     }
   }
 }
 
-// grid (B*Hq); combine the chunks of one (sequence, head)
+// grid (B*Hq); combine the chunks of one (sequence, head) in chunk order
 template <int D>
 __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ partial, int nsplit,
                                                     uint16_t* __restrict__ out) {
   const int bh = blockIdx.x, d = threadIdx.x;
   const float* p = partial + size_t(bh) * nsplit * (D + 2);
-  float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, p[s * (D + 2) + D]);
-  float L = 0.f, o = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = fast_exp2(p[s * (D + 2) + D] - M);
-      L = fmaf(p[s * (D + 2) + D + 1], w, L);
-      o = fmaf(p[s * (D + 2) + d], w, o);
-    }
+  float M = -__builtin_inff(), L = 0.f, O = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = p[s * (D + 2) + D];
+    const float ls = p[s * (D + 2) + D + 1];
+    const float os = p[s * (D + 2) + d];
+    if (ms == -__builtin_inff()) continue;        // empty chunk
+    const float mn = fmaxf(M, ms);
+    const float wo = fast_exp2(M - mn), ws = fast_exp2(ms - mn);   // M = -inf gives wo = 0
+    L = L * wo + ls * ws;
+    O = O * wo + os * ws;
+    M = mn;
   }
-  out[size_t(bh) * D + d] = f32_to_bf16(L > 0.f ? o / L : 0.f);
+  out[size_t(bh) * D + d] = f32_to_bf16(L > 0.f ? O / L : 0.f);
+}
+
+template <int D, int G, int PAGE>
+hipError_t run(const DecodeArgs& a, hipStream_t s) {
+  const int pps = pages_per_split(PAGE);
+  const int nsplit = (a.idx_width + pps - 1) / pps;
+  k_decode_split<D, G, PAGE><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
+  k_decode_merge<D><<<a.B * a.Hq, D, 0, s>>>(a.partial, nsplit, static_cast<uint16_t*>(a.out));
+  return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t run(const DecodeArgs& a, hipStream_t s) {
-  const int pps = pages_per_split(a.page);
-  const int nsplit = (a.idx_width + pps - 1) / pps;
-  k_decode_split<D, G><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
-  k_decode_merge<D><<<a.B * a.Hq, D, 0, s>>>(a.partial, nsplit, static_cast<uint16_t*>(a.out));
-  return hipGetLastError();
+hipError_t run_p(const DecodeArgs& a, hipStream_t s) {
+  switch (a.page) {
+    case 32: return run<D, G, 32>(a, s);
+    case 64: return run<D, G, 64>(a, s);
+    case 128: return run<D, G, 128>(a, s);
+    case 256: return run<D, G, 256>(a, s);
+    default: return run<D, G, 512>(a, s);
+  }
 }
 
 template <int D>
 hipError_t run_d(const DecodeArgs& a, hipStream_t s) {
   switch (a.Hq / a.Hkv) {
-    case 1: return run<D, 1>(a, s);
-    case 2: return run<D, 2>(a, s);
-    case 4: return run<D, 4>(a, s);
-    default: return run<D, 8>(a, s);
+    case 1: return run_p<D, 1>(a, s);
+    case 2: return run_p<D, 2>(a, s);
+    case 4: return run_p<D, 4>(a, s);
+    default: return run_p<D, 8>(a, s);
   }
 }
 

@@ -147,7 +147,7 @@ int dsa_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int 
  * The query follows all L cached tokens, so every token of a selected page
  * is visible.  Pages are split over workgroups whose partial results
  * (max, sum, weighted values) are merged in a fixed order.  bf16 only;
- * L % page == 0, page a multiple of 32 up to 512, Hq/Hkv in {1,2,4,8}.
+ * L % page == 0, page in {32, 64, 128, 256, 512}, Hq/Hkv in {1,2,4,8}.
  */
 size_t dsa_sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int idx_width, int page,
                                              int D);

@@ -242,3 +242,17 @@ def test_nsa_combine_only():
     _sync()
     ref = On.combine(*(to_np(t) for t in o), z.numpy())
     check_bf16(to_np(out), ref, "combine")
+
+
+def test_decode_repeated_calls_identical():
+    """Repeated calls on one workspace give bit-identical outputs."""
+    c = replace(configs.DECODE_128K, B=3, L=8192)
+    x = inputs.decode_inputs(c, seed=7, device=DEV)
+    plan = DecodePlan(c.B, c.Hq, c.Hkv, c.L, c.D, c.page, 9, x["q"].dtype, DEV)
+    plan.build_metadata(x["k"])
+    outs = []
+    for _ in range(3):
+        plan.run(x["q"], x["k"], x["v"])
+        outs.append(plan.out.clone())
+    _sync()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
