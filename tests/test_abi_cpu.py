@@ -1,0 +1,128 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before enqueuing anything (the
+validation layer makes no HIP call, so these run on a CPU-only host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dynamic_block_sparse_head_amd import binding as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libdsa.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    names = _declared()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
+    assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
+
+
+def test_version_and_status_strings():
+    lib = L.load()
+    assert lib.dsa_version() == 100
+    for st in (0, -1, -2, -3, -4):
+        assert lib.dsa_status_string(st)
+    assert lib.dsa_status_string(12345) == b"unknown dsa status"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def _err():
+    return L.load().dsa_last_error().decode()
+
+
+def test_topk_validation():
+    lib = L.load()
+    assert lib.dsa_topk_select(None, 1, 1, 8, 2, 1, 1, FAKE, FAKE, None) == L.DSA_E_ARG
+    assert "scores" in _err()
+    assert lib.dsa_topk_select(FAKE, 1, 1, 8, -1, 1, 1, FAKE, FAKE, None) == L.DSA_E_ARG
+    assert lib.dsa_topk_select(FAKE, 1, 1, 8, 0, 0, 1, FAKE, FAKE, None) == L.DSA_E_ARG
+    assert lib.dsa_topk_select(FAKE, 1, 1, 9000, 2, 1, 1, FAKE, FAKE, None) == L.DSA_E_UNSUPPORTED
+    assert lib.dsa_topk_select(FAKE, 1, 9, 8, 2, 1, 1, FAKE, FAKE, None) == L.DSA_E_ARG  # n_q > n_k
+    assert lib.dsa_topk_select(MISALIGNED, 1, 1, 8, 2, 1, 1, FAKE, FAKE, None) == L.DSA_E_ARG
+    assert "aligned" in _err()
+
+
+def test_prefill_validation():
+    lib = L.load()
+    f = lib.dsa_sparse_attn_prefill
+    ok = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, B=1, Hq=4, Hkv=2, S=256, D=128, idx=FAKE, count=FAKE,
+              width=3, block=64, window=0, scale=0.1, out=FAKE, lse=None, stream=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["dtype"], a["q"], a["k"], a["v"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+                 a["idx"], a["count"], a["width"], a["block"], a["window"], a["scale"], a["out"],
+                 a["lse"], a["stream"])
+
+    assert call(dtype=7) == L.DSA_E_ARG
+    assert call(D=96) == L.DSA_E_UNSUPPORTED
+    assert call(Hq=3) == L.DSA_E_ARG                      # Hq % Hkv
+    assert call(block=48) == L.DSA_E_UNSUPPORTED
+    assert call(block=0) == L.DSA_E_ARG
+    assert call(q=None) == L.DSA_E_ARG
+    assert call(count=None) == L.DSA_E_ARG                # idx without count
+    assert call(window=64) == L.DSA_E_ARG                 # window in index mode
+    assert call(idx=None, count=None, window=0) == L.DSA_E_ARG
+    assert call(scale=0.0) == L.DSA_E_ARG
+    assert call(S=0) == L.DSA_E_ARG
+    assert call(B=70000) == L.DSA_E_UNSUPPORTED
+
+
+def test_scores_and_decode_validation():
+    lib = L.load()
+    need = lib.dsa_block_scores_workspace_size(0, 1, 32, 8, 16384, 128, 64)
+    assert need == 2 * 8 * 256 * 128 * 8
+    st = lib.dsa_block_scores(0, 1, FAKE, FAKE, None, 1, 32, 8, 16384, 128, 64, FAKE, need - 8,
+                              FAKE, None)
+    assert st == L.DSA_E_WORKSPACE
+    assert lib.dsa_block_scores(0, 1, FAKE, FAKE, FAKE, 1, 32, 8, 16384, 128, 64, FAKE, need,
+                                FAKE, None) == L.DSA_E_ARG       # kmax with POOLED
+    assert lib.dsa_block_scores(5, 1, FAKE, FAKE, None, 1, 32, 8, 16384, 128, 64, FAKE, need,
+                                FAKE, None) == L.DSA_E_ARG       # unknown kind
+    ws = lib.dsa_sparse_attn_decode_workspace_size(16, 32, 8, 102, 64, 128)
+    assert ws == 16 * 32 * 13 * 130 * 4
+    dec = lib.dsa_sparse_attn_decode
+    args = [1, FAKE, FAKE, FAKE, 16, 32, 8, 131072, 128, FAKE, FAKE, 102, 64, 0.1, FAKE, ws, FAKE,
+            None]
+    a = list(args); a[0] = 0
+    assert dec(*a) == L.DSA_E_UNSUPPORTED                          # float32 decode
+    a = list(args); a[12] = 96
+    assert dec(*a) == L.DSA_E_UNSUPPORTED                          # page 96
+    a = list(args); a[15] = ws - 1
+    assert dec(*a) == L.DSA_E_WORKSPACE
+    a = list(args); a[5] = 48
+    assert dec(*a) == L.DSA_E_UNSUPPORTED                          # G = 6
+    a = list(args); a[11] = 5000
+    assert dec(*a) == L.DSA_E_ARG                                  # more pages than the cache
+
+
+def test_nsa_validation():
+    lib = L.load()
+    assert lib.dsa_nsa_compress(1, FAKE, FAKE, 1, 4, 16, 128, 32, 16, FAKE, FAKE, None) == L.DSA_E_ARG
+    assert lib.dsa_nsa_cmp_attn(1, FAKE, FAKE, FAKE, 1, 64, 4, 32768, 128, 32, 16, 64, 0.1, FAKE,
+                                None, None, None) == L.DSA_E_ARG         # lse required
+    assert lib.dsa_nsa_combine(0, FAKE, FAKE, FAKE, FAKE, 1, 4, 8, 128, FAKE, None) == L.DSA_E_UNSUPPORTED
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    s = torch.zeros(1, 4, 4)
+    idx = torch.zeros(1, 4, 2, dtype=torch.int32)
+    cnt = torch.zeros(1, 4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        L.dsa_topk_select(s, 1, 1, True, idx, cnt)
