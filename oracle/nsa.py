@@ -52,22 +52,23 @@ def cmp_attention(q, ck, cv, length, stride, scale, rows=None):
     """Branch 1: each row t attends to the summaries whose last token is <= t.
 
     q [B,Hq,S,D]; ck/cv [B,Hkv,n,D].  Returns out [B,Hq,S,D], lse [B,Hq,S]
-    and the probabilities p [B,Hq,S,n] (zero where invisible).  rows: optional
-    list of positions to evaluate (others NaN / zero).
+    and the probabilities p [B,Hq,R,n] (zero where invisible) of the R
+    evaluated rows.  rows: optional list of positions to evaluate (default
+    all S, in order); other rows of out / lse are NaN.
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, S, D = q.shape
     Hkv, n = ck.shape[1], ck.shape[2]
     G = Hq // Hkv
     ends = summary_end(np.arange(n), length, stride)
-    rows = range(S) if rows is None else rows
+    rows = list(range(S)) if rows is None else list(rows)
     out = np.full((B, Hq, S, D), np.nan)
     lse = np.full((B, Hq, S), np.nan)
-    probs = np.zeros((B, Hq, S, n))
+    probs = np.zeros((B, Hq, len(rows), n))
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            for t in rows:
+            for ri, t in enumerate(rows):
                 logits = (ck[b, g] @ q[b, h, t]) * scale
                 vis = ends <= t
                 if not vis.any():
@@ -78,7 +79,7 @@ def cmp_attention(q, ck, cv, length, stride, scale, rows=None):
                 p = np.where(vis, np.exp(logits - m), 0.0)
                 l = p.sum()
                 p = p / l
-                probs[b, h, t] = p
+                probs[b, h, ri] = p
                 out[b, h, t] = p @ cv[b, g]
                 lse[b, h, t] = m + math.log(l)
     return out, lse, probs
@@ -97,25 +98,31 @@ def overlap_weights(n_cmp, length, stride, sel_block, n_blocks):
     return w
 
 
-def cmp_block_scores(probs, Hkv, length, stride, sel_block, S):
+def cmp_block_scores(probs, Hkv, length, stride, sel_block, S, q_blocks=None):
     """score[b, g, i, j]: branch-1 probability mass inside key block j, summed
     over the rows of query block i and the query heads of group g, divided by
     (rows in block i) x (heads per group).
 
-    probs [B,Hq,S,n] from cmp_attention.  Returns [B,Hkv,nB,nB].
+    probs from cmp_attention: [B,Hq,S,n] for all rows, or, with q_blocks, the
+    rows of those query blocks in order.  Returns [B,Hkv,nB,nB] (rows of
+    blocks not in q_blocks are NaN).
     """
     B, Hq, _, n = probs.shape
     G = Hq // Hkv
     nB = -(-S // sel_block)
     w = overlap_weights(n, length, stride, sel_block, nB)
-    out = np.zeros((B, Hkv, nB, nB))
+    blocks = range(nB) if q_blocks is None else q_blocks
+    out = np.full((B, Hkv, nB, nB), np.nan)
     for b in range(B):
         for g in range(Hkv):
-            for i in range(nB):
+            r0 = 0
+            for i in blocks:
                 t0, t1 = i * sel_block, min((i + 1) * sel_block, S)
+                sl = slice(t0, t1) if q_blocks is None else slice(r0, r0 + t1 - t0)
+                r0 += t1 - t0
                 mass = np.zeros(n)
                 for h in range(g * G, (g + 1) * G):
-                    mass += probs[b, h, t0:t1].sum(axis=0)
+                    mass += probs[b, h, sl].sum(axis=0)
                 out[b, g, i] = (mass @ w) / ((t1 - t0) * G)
     return out
 

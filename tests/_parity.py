@@ -55,17 +55,20 @@ def check_index_row(s_row, gpu_row, gpu_cnt, k, n_local, causal, i, n_k):
     return set(oracle_top) == top
 
 
-def check_indices(scores, gpu_idx, gpu_cnt, k, n_local, causal):
+def check_indices(scores, gpu_idx, gpu_cnt, k, n_local, causal, rows=None):
     """scores [..., nQ, nK] (oracle), gpu_idx [..., nQ, W], gpu_cnt [..., nQ].
-    Returns the fraction of rows that are bit-exact (all rows must be accepted)."""
+    rows: the query-block index of each of the nQ rows when they are a slice
+    (default 0..nQ-1).  Returns the fraction of rows that are bit-exact (all
+    rows must be accepted)."""
     nQ, nK = scores.shape[-2:]
+    rows = list(range(nQ)) if rows is None else list(rows)
     s = scores.reshape(-1, nQ, nK)
     gi = gpu_idx.reshape(-1, nQ, gpu_idx.shape[-1])
     gc = gpu_cnt.reshape(-1, nQ)
     exact = total = 0
     for r in range(s.shape[0]):
         for i in range(nQ):
-            exact += check_index_row(s[r, i], gi[r, i], int(gc[r, i]), k, n_local, causal, i, nK)
+            exact += check_index_row(s[r, i], gi[r, i], int(gc[r, i]), k, n_local, causal, rows[i], nK)
             total += 1
     return exact / total
 

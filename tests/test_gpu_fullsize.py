@@ -1,0 +1,121 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (the same plans, shapes and seeds).  The oracle checks
+every selected index row it can afford and sampled outputs: query blocks
+spread over the sequence (first, middle, last), sampled (sequence, KV head)
+pairs for decode, and sampled query blocks of one KV group for the
+three-branch path."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_block_sparse_head_amd import configs, inputs
+from dynamic_block_sparse_head_amd.pipeline import DecodePlan, NSAPlan, PrefillPlan
+from oracle import decode as Od
+from oracle import nsa as On
+from oracle import prefill as Op
+
+from _parity import check_bf16, check_indices, check_lse, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _prefill_full(c, groups, blocks):
+    x = inputs.prefill_inputs(c, seed=0, device=DEV)
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, x["q"].dtype, DEV)
+    plan.run(x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    gs, go, gl = plan.scores.cpu().numpy(), plan.out, plan.lse
+    G = c.G
+    exact = []
+    for g in groups:
+        heads = slice(g * G, (g + 1) * G)
+        q = to_np(x["q"][:, heads])
+        k = to_np(x["k"][:, g:g + 1])
+        v = to_np(x["v"][:, g:g + 1])
+        s = Op.block_scores_pooled(q, k, c.block)                         # [1,1,nb,nb]
+        fin = np.isfinite(s)
+        assert (np.abs(gs[:, g:g + 1][fin] - s[fin]) <= 2.0 ** -23 * np.abs(s[fin]) + 1e-30).all()
+        exact.append(check_indices(s, gi[:, g:g + 1], gc[:, g:g + 1], c.topk, c.n_local, True))
+        out, lse = Op.sparse_attention(q, k, v, gi[:, g:g + 1], gc[:, g:g + 1], c.block, c.scale,
+                                       q_blocks=blocks)
+        rows = np.concatenate([np.arange(i * c.block, min((i + 1) * c.block, c.S)) for i in blocks])
+        check_bf16(to_np(go[:, heads][:, :, rows]), out[:, :, rows], f"{c.name} g{g}")
+        check_lse(to_np(gl[:, heads][:, :, rows]), lse[:, :, rows], 2e-3, f"{c.name} g{g}")
+    for (b, g, t, n) in x["needles"]:
+        assert n in gi[b, g, t, :gc[b, g, t]], "planted needle not selected"
+    return float(np.mean(exact))
+
+
+def test_prefill_16k_full_size():
+    c = configs.PREFILL_16K
+    exact = _prefill_full(c, groups=range(c.Hkv), blocks=[0, 23, 24, 100, 255])
+    print(f"bit-exact index rows: {exact:.3f}")
+
+
+def test_prefill_64k_full_size():
+    c = configs.PREFILL_64K
+    exact = _prefill_full(c, groups=[0, 5], blocks=[0, 39, 40, 300, 511])
+    print(f"bit-exact index rows: {exact:.3f}")
+
+
+def test_decode_128k_full_size():
+    c = configs.DECODE_128K
+    x = inputs.decode_inputs(c, seed=0, device=DEV)
+    plan = DecodePlan(c.B, c.Hq, c.Hkv, c.L, c.D, c.page, c.topk, x["q"].dtype, DEV)
+    plan.build_metadata(x["k"])
+    plan.run(x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    gs = plan.scores.cpu().numpy()
+    for (b, g) in [(0, 0), (7, 3), (15, 7)]:
+        heads = slice(g * c.G, (g + 1) * c.G)
+        q = to_np(x["q"][b:b + 1, heads])
+        k = to_np(x["k"][b:b + 1, g:g + 1])
+        v = to_np(x["v"][b:b + 1, g:g + 1])
+        kmin, kmax = Od.page_minmax(k, c.page)
+        assert np.array_equal(to_np(plan.kmin[b:b + 1, g:g + 1]), kmin)
+        assert np.array_equal(to_np(plan.kmax[b:b + 1, g:g + 1]), kmax)
+        s = Od.page_scores(q, kmin, kmax)                                 # [1,1,nP]
+        assert (np.abs(gs[b, g, 0] - s[0, 0]) <= 2.0 ** -23 * np.abs(s[0, 0]) + 1e-30).all()
+        check_indices(s[:, :, None, :], gi[b:b + 1, g:g + 1], gc[b:b + 1, g:g + 1], c.topk, 0, False)
+        out = Od.decode_attention(q, k, v, gi[b:b + 1, g:g + 1, 0], gc[b:b + 1, g:g + 1, 0],
+                                  c.page, c.scale)
+        check_bf16(to_np(plan.out[b:b + 1, heads]), out, f"decode b{b} g{g}")
+
+
+def test_nsa_32k_full_size():
+    c = configs.NSA_32K
+    x = inputs.nsa_inputs(c, seed=0, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    torch.cuda.synchronize()
+    g = 1
+    heads = slice(g * c.G, (g + 1) * c.G)
+    q = to_np(x["q"][:, heads])
+    k = to_np(x["k"][:, g:g + 1])
+    v = to_np(x["v"][:, g:g + 1])
+    z = to_np(x["z"][:, :, heads])
+    ck, cv = On.compress(k, c.cmp_len, c.cmp_stride), On.compress(v, c.cmp_len, c.cmp_stride)
+    check_bf16(to_np(plan.ck[:, g:g + 1]), ck, "ck")
+    gck, gcv = to_np(plan.ck[:, g:g + 1]), to_np(plan.cv[:, g:g + 1])
+    blocks = [0, 1, 16, 300, 511]
+    rows = [t for i in blocks for t in range(i * c.sel_block, (i + 1) * c.sel_block)]
+    o1, lse1, p1 = On.cmp_attention(q, gck, gcv, c.cmp_len, c.cmp_stride, c.scale, rows=rows)
+    check_bf16(to_np(plan.o_cmp[:, heads][:, :, rows]), o1[:, :, rows], "o_cmp")
+    check_lse(to_np(plan.lse_cmp[:, heads][:, :, rows]), lse1[:, :, rows], 2e-3, "lse_cmp")
+    sc = On.cmp_block_scores(p1, 1, c.cmp_len, c.cmp_stride, c.sel_block, c.S, q_blocks=blocks)
+    gsc = to_np(plan.scores[:, g:g + 1])
+    gi, gc = plan.idx[:, g:g + 1].cpu().numpy(), plan.count[:, g:g + 1].cpu().numpy()
+    for i in blocks:
+        assert np.abs(gsc[0, 0, i] - sc[0, 0, i]).max() < 1e-6
+        check_indices(sc[:, :, i:i + 1, :], gi[:, :, i:i + 1], gc[:, :, i:i + 1], c.sel_k, 0, True,
+                      rows=[i])
+    o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale, q_blocks=blocks)
+    check_bf16(to_np(plan.o_sel[:, heads][:, :, rows]), o2[:, :, rows], "o_sel")
+    o3, _ = On.window_attention(q, k, v, c.window, c.scale, rows=rows)
+    check_bf16(to_np(plan.o_win[:, heads][:, :, rows]), o3[:, :, rows], "o_win")
+    ref = On.combine(o1[:, :, rows], o2[:, :, rows], o3[:, :, rows], z[:, rows])
+    check_bf16(to_np(plan.out[:, heads][:, :, rows]), ref, "nsa out")
