@@ -40,12 +40,20 @@ __device__ __forceinline__ void load8(const float* p, float* f) {
 }
 
 // out[bg, i, :] = sum over hpg heads of mean over the rows of block i.
-// grid (nb, B*Hkv); each thread owns 8 columns and a strided set of rows.
+// grid (nb, B*Hkv, 2): z = 0 pools the queries (the G heads of each group
+// summed), z = 1 the keys.  Each thread owns 8 columns and a strided set of
+// rows.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ x, int H, int S, int D,
-                                                   int block, int hpg, int Hkv,
-                                                   double* __restrict__ out) {
+__global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
+                                                   int Hq, int S, int D, int block, int G, int Hkv,
+                                                   double* __restrict__ out_q,
+                                                   double* __restrict__ out_k) {
   __shared__ double red[kThreads * 8];
+  const bool keys = blockIdx.z != 0;
+  const T* __restrict__ x = keys ? k : q;
+  const int H = keys ? Hkv : Hq;
+  const int hpg = keys ? 1 : G;
+  double* __restrict__ out = keys ? out_k : out_q;
   const int i = blockIdx.x;
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -78,37 +86,67 @@ __global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ x, int 
 }
 
 // scores[bg, i, j] = qs[bg, i, :] . kb[bg, j, :] for j <= i, -inf above the
-// diagonal.  16x16 output tile per workgroup, float64 dots from LDS.
+// diagonal.  32x32 output tile per workgroup; thread (ti, tj) owns rows
+// ti, ti+16 and columns tj, tj+16, i.e. four independent float64 dot
+// products fed from LDS (two query and two key values per step).
 __global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restrict__ qs,
                                                          const double* __restrict__ kb, int nb,
                                                          int D, float* __restrict__ scores) {
-  extern __shared__ double lds[];  // [16][D+1] queries, then [16][D+1] keys
+  extern __shared__ double lds[];  // [32][D+2] queries, then [32][D+2] keys
   const int bg = blockIdx.z;
-  const int i0 = blockIdx.y * 16, j0 = blockIdx.x * 16;
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
-  const int i = i0 + ti, j = j0 + tj;
   float* srow = scores + size_t(bg) * nb * nb;
-  if (j0 > i0 + 15) {  // whole tile above the diagonal
-    if (i < nb && j < nb) srow[size_t(i) * nb + j] = -__builtin_inff();
+  if (j0 > i0 + 31) {  // whole tile above the diagonal
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int i = i0 + ti + 16 * r, j = j0 + tj + 16 * c;
+        if (i < nb && j < nb) srow[size_t(i) * nb + j] = -__builtin_inff();
+      }
     return;
   }
-  const int ld = D + 1;
+  const int ld = D + 2;  // even: rows stay 16-byte aligned
   double* lq = lds;
-  double* lk = lds + 16 * ld;
-  for (int e = threadIdx.x; e < 16 * D; e += kThreads) {
-    const int r = e / D, d = e % D;
-    lq[r * ld + d] = (i0 + r < nb) ? qs[(size_t(bg) * nb + i0 + r) * D + d] : 0.0;
-    lk[r * ld + d] = (j0 + r < nb) ? kb[(size_t(bg) * nb + j0 + r) * D + d] : 0.0;
+  double* lk = lds + 32 * ld;
+  const int hd = D / 2;
+  for (int e = threadIdx.x; e < 32 * hd; e += kThreads) {
+    const int r = e / hd, d = (e % hd) * 2;
+    double2 a = {0.0, 0.0}, c = {0.0, 0.0};
+    if (i0 + r < nb) a = *reinterpret_cast<const double2*>(qs + (size_t(bg) * nb + i0 + r) * D + d);
+    if (j0 + r < nb) c = *reinterpret_cast<const double2*>(kb + (size_t(bg) * nb + j0 + r) * D + d);
+    *reinterpret_cast<double2*>(lq + r * ld + d) = a;
+    *reinterpret_cast<double2*>(lk + r * ld + d) = c;
   }
   __syncthreads();
-  if (i >= nb || j >= nb) return;
-  float res = -__builtin_inff();
-  if (j <= i) {
-    double s = 0.0;
-    for (int d = 0; d < D; ++d) s += lq[ti * ld + d] * lk[tj * ld + d];
-    res = float(s);
+  const double* q0 = lq + ti * ld;
+  const double* q1 = lq + (ti + 16) * ld;
+  const double* k0 = lk + tj * ld;
+  const double* k1 = lk + (tj + 16) * ld;
+  double a00 = 0.0, a01 = 0.0, a10 = 0.0, a11 = 0.0;
+  for (int d = 0; d < D; d += 2) {
+    const double2 x0 = *reinterpret_cast<const double2*>(q0 + d);
+    const double2 x1 = *reinterpret_cast<const double2*>(q1 + d);
+    const double2 y0 = *reinterpret_cast<const double2*>(k0 + d);
+    const double2 y1 = *reinterpret_cast<const double2*>(k1 + d);
+    a00 = __builtin_fma(x0.x, y0.x, a00);
+    a01 = __builtin_fma(x0.x, y1.x, a01);
+    a10 = __builtin_fma(x1.x, y0.x, a10);
+    a11 = __builtin_fma(x1.x, y1.x, a11);
+    a00 = __builtin_fma(x0.y, y0.y, a00);
+    a01 = __builtin_fma(x0.y, y1.y, a01);
+    a10 = __builtin_fma(x1.y, y0.y, a10);
+    a11 = __builtin_fma(x1.y, y1.y, a11);
   }
-  srow[size_t(i) * nb + j] = res;
+  const double acc[2][2] = {{a00, a01}, {a10, a11}};
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int i = i0 + ti + 16 * r, j = j0 + tj + 16 * c;
+      if (i < nb && j < nb) srow[size_t(i) * nb + j] = (j <= i) ? float(acc[r][c]) : -__builtin_inff();
+    }
 }
 
 // Page bound scores.  Each page is handled by D/8 lanes (8 dims each); the
@@ -205,20 +243,17 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
 hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s) {
   const int nb = (a.S + a.block - 1) / a.block;
   const int G = a.Hq / a.Hkv;
-  dim3 grid(nb, a.B * a.Hkv);
-  if (a.dtype == 1) {
-    k_pool<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(a.q), a.Hq, a.S, a.D,
-                                               a.block, G, a.Hkv, a.ws_q);
-    k_pool<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(a.k), a.Hkv, a.S, a.D,
-                                               a.block, 1, a.Hkv, a.ws_k);
-  } else {
-    k_pool<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(a.q), a.Hq, a.S, a.D,
-                                            a.block, G, a.Hkv, a.ws_q);
-    k_pool<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(a.k), a.Hkv, a.S, a.D,
-                                            a.block, 1, a.Hkv, a.ws_k);
-  }
-  const int nt = (nb + 15) / 16;
-  const size_t lds = size_t(2) * 16 * (a.D + 1) * sizeof(double);
+  dim3 grid(nb, a.B * a.Hkv, 2);
+  if (a.dtype == 1)
+    k_pool<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(a.q),
+                                               static_cast<const uint16_t*>(a.k), a.Hq, a.S, a.D,
+                                               a.block, G, a.Hkv, a.ws_q, a.ws_k);
+  else
+    k_pool<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(a.q),
+                                            static_cast<const float*>(a.k), a.Hq, a.S, a.D,
+                                            a.block, G, a.Hkv, a.ws_q, a.ws_k);
+  const int nt = (nb + 31) / 32;
+  const size_t lds = size_t(2) * 32 * (a.D + 2) * sizeof(double);
   k_pooled_dot<<<dim3(nt, nt, a.B * a.Hkv), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, a.D, a.scores);
   return hipGetLastError();
 }

@@ -1,23 +1,25 @@
 // Top-k block selection plus the local window ([DMA] §五: after the causal
 // mask keep the k highest-weight history positions, everything else -inf).
 //
-// Rows of up to 2048 candidates use one wave per row (bisection for the k-th
-// largest key, see k_topk_wave); longer rows use one workgroup per row.
-// Candidates become 64-bit keys
-//   (order-preserving bits of the score) << 32 | (0xffffffff - index)
-// so that "larger key" means "higher score, then lower index"; NaN maps to
-// the lowest score bits and therefore ranks last.  The keys are sorted
-// descending by a bitonic network in LDS; the first k are the selection.
-// Selected and window blocks are flagged in LDS and compacted in index
-// order, which writes each output row already ascending.
+// Order: higher score first, equal scores by lower index, NaN below every
+// number.  Each score becomes its order-preserving 32-bit pattern (NaN -> 0).
+// The k-th largest pattern T is found by bisection from the top bit down
+// (T grows while at least k candidates are >= T); the selection is every
+// candidate above T plus the lowest-indexed candidates equal to T, as many
+// as are still missing.  Counts come from wave ballots, so a row needs no
+// sort and no LDS traffic beyond a few counters.  The chosen and the window
+// blocks are written in index order, i.e. each output row comes out
+// ascending, padded with -1.
+//
+// Layout: W waves own one row (W = 1: four rows per 256-thread workgroup,
+// no barriers), each lane E candidates; candidate j sits in chunk j / 64,
+// chunk c = e * W + w held by wave w as element e, so loads are coalesced
+// and chunk order is index order.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kMaxN = 8192;
 
 __device__ __forceinline__ uint32_t order_bits(float f) {
   if (__builtin_isnan(f)) return 0u;
@@ -25,97 +27,91 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(kThreads) void k_topk(const float* __restrict__ scores, int n_q,
-                                                   int n_k, int k, int n_local, int causal,
-                                                   int32_t* __restrict__ idx,
-                                                   int32_t* __restrict__ count) {
-  __shared__ uint64_t keys[kMaxN];
-  __shared__ uint8_t flag[kMaxN];
-  __shared__ int part[kThreads + 1];
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
-  const int row = blockIdx.x;            // over rows * n_q
-  const int i = row % n_q;
-  const float* srow = scores + size_t(row) * n_k;
-  const int width = k + n_local;
-  int last, w0, w1;                      // candidates 0..last, window w0..w1
-  if (causal) {
-    last = i - n_local;
-    w0 = max(0, i - n_local + 1);
-    w1 = i;
+// Sum of a wave-uniform value over the W waves of the row.  `slot` alternates
+// between calls so one barrier per call suffices.
+template <int W>
+__device__ __forceinline__ int row_total(int v, int (*red)[W], int& slot) {
+  if constexpr (W == 1) {
+    return v;
   } else {
-    last = n_k - 1 - n_local;
-    w0 = n_k - n_local;
-    w1 = n_k - 1;
-  }
-  const int ncand = max(0, last + 1);
-  const int span = max(w1 + 1, ncand);   // flags needed for blocks 0..span-1
-
-  for (int j = threadIdx.x; j < span; j += kThreads)
-    flag[j] = (j >= w0 && j <= w1) || (ncand <= k && j < ncand);
-
-  if (ncand > k && k > 0) {
-    int P = 1;
-    while (P < ncand) P <<= 1;
-    for (int j = threadIdx.x; j < P; j += kThreads)
-      keys[j] = (j < ncand) ? ((uint64_t(order_bits(srow[j])) << 32) | (0xffffffffu - uint32_t(j)))
-                            : 0ull;
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[slot][w] = v;
     __syncthreads();
-    // bitonic sort, descending
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int t = threadIdx.x; t < P / 2; t += kThreads) {
-          const int lo = 2 * t - (t & (stride - 1));
-          const int hi = lo + stride;
-          const bool desc = ((lo & size) == 0);
-          const uint64_t a = keys[lo], b = keys[hi];
-          if ((a < b) == desc) {
-            keys[lo] = b;
-            keys[hi] = a;
-          }
-        }
-        __syncthreads();
-      }
-    }
-    for (int t = threadIdx.x; t < k; t += kThreads)
-      flag[0xffffffffu - uint32_t(keys[t] & 0xffffffffu)] = 1;
+    int t = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) t += red[slot][i];
+    slot ^= 1;
+    return t;
   }
-  __syncthreads();
-
-  // ascending compaction of the flagged blocks
-  const int chunk = (span + kThreads - 1) / kThreads;
-  const int c0 = threadIdx.x * chunk;
-  const int c1 = min(span, c0 + chunk);
-  int c = 0;
-  for (int j = c0; j < c1; ++j) c += flag[j];
-  part[threadIdx.x + 1] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    part[0] = 0;
-    for (int t = 1; t <= kThreads; ++t) part[t] += part[t - 1];
-  }
-  __syncthreads();
-  int32_t* orow = idx + size_t(row) * width;
-  int pos = part[threadIdx.x];
-  for (int j = c0; j < c1; ++j)
-    if (flag[j]) orow[pos++] = j;
-  const int total = part[kThreads];
-  for (int t = total + threadIdx.x; t < width; t += kThreads) orow[t] = -1;
-  if (threadIdx.x == 0) count[row] = total;
 }
 
-// Rows of up to 64*E candidates: one wave per row, no LDS and no barrier.
-// Lane l holds candidates l, l+64, ... as the same 64-bit keys.  The k-th
-// largest key T is found bit by bit from the top (T grows while at least k
-// keys are >= T); keys are unique, so exactly k candidates satisfy key >= T.
-// Chosen and window blocks are then compacted in index order with ballots.
-template <int E>
-__global__ __launch_bounds__(kThreads) void k_topk_wave(const float* __restrict__ scores, int n_rows,
-                                                        int n_q, int n_k, int k, int n_local,
-                                                        int causal, int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ count) {
+// Exclusive prefix over the row, in index order, of per-chunk counts (mine[e]
+// is this wave's count for chunk e * W + w).  Returns the bases of this
+// wave's chunks and the row total.
+template <int E, int W>
+__device__ __forceinline__ int chunk_prefix(const int (&mine)[E], int (&base)[E], int* pre) {
+  if constexpr (W == 1) {
+    int run = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      base[e] = run;
+      run += mine[e];
+    }
+    return run;
+  } else {
+    constexpr int NC = E * W;
+    constexpr int PER = (NC + 63) / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) pre[e * W + w] = mine[e];
+    }
+    __syncthreads();
+    if (w == 0) {
+      int v[PER];
+      int s = 0;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int c = lane * PER + p;
+        v[p] = (c < NC) ? pre[c] : 0;
+        s += v[p];
+      }
+      int incl = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      int run = incl - s;
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int c = lane * PER + p;
+        if (c < NC) pre[c] = run;
+        run += v[p];
+      }
+      if (lane == 63) pre[NC] = incl;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < E; ++e) base[e] = pre[e * W + w];
+    const int total = pre[NC];
+    __syncthreads();  // the table is reused by the next call
+    return total;
+  }
+}
+
+template <int E, int W>
+__global__ __launch_bounds__(W == 1 ? 256 : 64 * W) void k_topk(
+    const float* __restrict__ scores, int n_rows, int n_q, int n_k, int k, int n_local, int causal,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+  __shared__ int red[2][W];
+  __shared__ int pre[E * W + 1];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= n_rows) return;          // the whole wave leaves together
+  const int w = (W == 1) ? 0 : (threadIdx.x >> 6);
+  const int row = (W == 1) ? blockIdx.x * 4 + (threadIdx.x >> 6) : blockIdx.x;
+  if (row >= n_rows) return;  // W == 1: the whole wave; W > 1: the whole workgroup
   const int i = row % n_q;
   const float* srow = scores + size_t(row) * n_k;
   const int width = k + n_local;
@@ -130,59 +126,107 @@ __global__ __launch_bounds__(kThreads) void k_topk_wave(const float* __restrict_
     w1 = n_k - 1;
   }
   const int ncand = max(0, last + 1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  uint64_t key[E];
+  int jj[E];
+  uint32_t bits[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = e * 64 + lane;
-    key[e] = (j < ncand) ? ((uint64_t(order_bits(srow[j])) << 32) | (0xffffffffu - uint32_t(j))) : 0ull;
+    jj[e] = (e * W + w) * 64 + lane;
+    bits[e] = (jj[e] < ncand) ? order_bits(srow[jj[e]]) : 0u;
   }
-  const bool take_all = ncand <= k;
-  uint64_t T = 0;
-  if (!take_all && k > 0) {
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t cand = T | (1ull << bit);
-      int c = 0;
+
+  int slot = 0;
+  bool f[E];
+  if (ncand <= k || k == 0) {
+    const bool all = k > 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
-      if (c >= k) T = cand;
+    for (int e = 0; e < E; ++e)
+      f[e] = (all && jj[e] < ncand) || (jj[e] >= w0 && jj[e] <= w1);
+  } else {
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) n += popc(__ballot(jj[e] < ncand && bits[e] >= c));
+      if (row_total<W>(n, red, slot) >= k) T = c;
+    }
+    int gt = 0, tc[E], tb[E];
+    uint64_t tm[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gt += popc(__ballot(jj[e] < ncand && bits[e] > T));
+      tm[e] = __ballot(jj[e] < ncand && bits[e] == T);
+      tc[e] = popc(tm[e]);
+    }
+    const int need = k - row_total<W>(gt, red, slot);
+    chunk_prefix<E, W>(tc, tb, pre);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool valid = jj[e] < ncand;
+      const bool tie_in = bits[e] == T && tb[e] + popc(tm[e] & below) < need;
+      f[e] = (valid && (bits[e] > T || tie_in)) || (jj[e] >= w0 && jj[e] <= w1);
     }
   }
 
-  int32_t* orow = idx + size_t(row) * width;
-  int base = 0;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint64_t fm[E];
+  int fc[E], fb[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = e * 64 + lane;
-    const bool sel = j < ncand && (take_all || (k > 0 && key[e] >= T));
-    const bool f = sel || (j >= w0 && j <= w1);
-    const uint64_t mask = __ballot(f);
-    if (f) orow[base + __popcll(mask & below)] = j;
-    base += __popcll(mask);
+    fm[e] = __ballot(f[e]);
+    fc[e] = popc(fm[e]);
   }
-  for (int t = base + lane; t < width; t += 64) orow[t] = -1;
-  if (lane == 0) count[row] = base;
+  const int total = chunk_prefix<E, W>(fc, fb, pre);
+  int32_t* orow = idx + size_t(row) * width;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (f[e]) orow[fb[e] + popc(fm[e] & below)] = jj[e];
+  for (int t = total + w * 64 + lane; t < width; t += 64 * W) orow[t] = -1;
+  if (w == 0 && lane == 0) count[row] = total;
+}
+
+template <int W>
+hipError_t launch_w(int E, const float* scores, int n_rows, int n_q, int n_k, int k, int n_local,
+                    int causal, int32_t* idx, int32_t* count, hipStream_t s) {
+  const int threads = (W == 1) ? 256 : 64 * W;
+  const int grid = (W == 1) ? (n_rows + 3) / 4 : n_rows;
+#define DSA_TOPK(EE)                                                                          \
+  k_topk<EE, W><<<grid, threads, 0, s>>>(scores, n_rows, n_q, n_k, k, n_local, causal, idx, \
+                                         count)
+  switch (E) {
+    case 1: DSA_TOPK(1); break;
+    case 2: DSA_TOPK(2); break;
+    case 4: DSA_TOPK(4); break;
+    case 8: DSA_TOPK(8); break;
+    case 16: DSA_TOPK(16); break;
+    case 32: DSA_TOPK(32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef DSA_TOPK
+  return hipGetLastError();
+}
+
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
 }
 
 }  // namespace
 
+// One wave per row when there are enough rows to fill the chip (or the rows
+// are short); otherwise eight waves share a row so that few long rows (decode:
+// one per sequence and KV head) still spread over many CUs.
 hipError_t launch_topk(const float* scores, int rows, int n_q, int n_k, int k, int n_local,
                        int causal, int32_t* idx, int32_t* count, hipStream_t s) {
   const int n_rows = rows * n_q;
-  const int grid = (n_rows + kThreads / 64 - 1) / (kThreads / 64);
-#define DSA_TOPK_WAVE(E)                                                                    \
-  k_topk_wave<E><<<grid, kThreads, 0, s>>>(scores, n_rows, n_q, n_k, k, n_local, causal, idx, \
-                                           count)
-  if (n_k <= 64) DSA_TOPK_WAVE(1);
-  else if (n_k <= 128) DSA_TOPK_WAVE(2);
-  else if (n_k <= 256) DSA_TOPK_WAVE(4);
-  else if (n_k <= 512) DSA_TOPK_WAVE(8);
-  else if (n_k <= 1024) DSA_TOPK_WAVE(16);
-  else if (n_k <= 2048) DSA_TOPK_WAVE(32);
-  else k_topk<<<n_rows, kThreads, 0, s>>>(scores, n_q, n_k, k, n_local, causal, idx, count);
-#undef DSA_TOPK_WAVE
-  return hipGetLastError();
+  if (n_rows == 0) return hipSuccess;
+  if ((n_rows >= 512 && n_k <= 2048) || n_k <= 256)
+    return launch_w<1>(pow2_at_least((n_k + 63) / 64), scores, n_rows, n_q, n_k, k, n_local,
+                       causal, idx, count, s);
+  return launch_w<8>(pow2_at_least((n_k + 511) / 512), scores, n_rows, n_q, n_k, k, n_local,
+                     causal, idx, count, s);
 }
 
 }  // namespace dsa

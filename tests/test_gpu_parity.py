@@ -29,7 +29,7 @@ def _sync():
     (8, 8, 2, 1, True), (256, 256, 16, 8, True), (512, 512, 32, 8, True), (512, 512, 16, 0, True),
     (1, 2048, 102, 0, False), (1, 300, 7, 3, False), (40, 40, 0, 2, True), (33, 33, 100, 1, True),
     (64, 64, 5, 2, True), (65, 65, 5, 2, True), (2, 1024, 51, 1, False), (2, 2049, 102, 0, False),
-    (1, 8192, 409, 4, False)])
+    (1, 8192, 409, 4, False), (512, 2048, 64, 4, False), (300, 1000, 40, 2, True)])
 @pytest.mark.parametrize("ties", [False, True])
 def test_topk_bit_exact(n_q, n_k, k, n_local, causal, ties):
     """Same float32 scores in, same indices out: selection is bit-exact."""
