@@ -213,16 +213,31 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
   const int bh = blockIdx.x, d = threadIdx.x;
   const float* p = partial + size_t(bh) * nsplit * (D + 2);
   float M = -__builtin_inff(), L = 0.f, O = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = p[s * (D + 2) + D];
-    const float ls = p[s * (D + 2) + D + 1];
-    const float os = p[s * (D + 2) + d];
-    if (ms == -__builtin_inff()) continue;        // empty chunk
-    const float mn = fmaxf(M, ms);
-    const float wo = fast_exp2(M - mn), ws = fast_exp2(ms - mn);   // M = -inf gives wo = 0
-    L = L * wo + ls * ws;
-    O = O * wo + os * ws;
-    M = mn;
+  // Splits are read eight at a time so their loads overlap; the combine
+  // still runs in split order.
+  constexpr int kChunk = 8;
+  for (int s0 = 0; s0 < nsplit; s0 += kChunk) {
+    float ms[kChunk], ls[kChunk], os[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const int s = s0 + c;
+      ms[c] = -__builtin_inff();
+      ls[c] = os[c] = 0.f;
+      if (s < nsplit) {
+        ms[c] = p[s * (D + 2) + D];
+        ls[c] = p[s * (D + 2) + D + 1];
+        os[c] = p[s * (D + 2) + d];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      if (ms[c] == -__builtin_inff()) continue;        // empty chunk or past the end
+      const float mn = fmaxf(M, ms[c]);
+      const float wo = fast_exp2(M - mn), ws = fast_exp2(ms[c] - mn);   // M = -inf gives wo = 0
+      L = L * wo + ls[c] * ws;
+      O = O * wo + os[c] * ws;
+      M = mn;
+    }
   }
   out[size_t(bh) * D + d] = f32_to_bf16(L > 0.f ? O / L : 0.f);
 }

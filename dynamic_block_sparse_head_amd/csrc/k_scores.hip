@@ -12,6 +12,8 @@
 //
 // All sums are float64 in a fixed order, so results are deterministic and
 // agree with an exact float64 evaluation to ~1e-15 relative.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -19,6 +21,7 @@ namespace dsa {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float floatx8 __attribute__((ext_vector_type(8)));
 
 // Load 8 consecutive elements as float.
 __device__ __forceinline__ void load8(const uint16_t* p, float* f) {
@@ -149,8 +152,11 @@ __global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restric
     }
 }
 
-// Page bound scores.  Each page is handled by D/8 lanes (8 dims each); the
-// group's G query vectors sit in LDS as float.
+// Page bound scores.  Each page is handled by D/8 lanes (8 dims each) and
+// each lane covers kPagesPerThread pages, whose bound loads are issued before
+// the group's G query vectors are staged in LDS, so the two latencies overlap.
+constexpr int kPagesPerThread = 4;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_page_scores(const T* __restrict__ q,
                                                           const T* __restrict__ kmin,
@@ -161,32 +167,62 @@ __global__ __launch_bounds__(kThreads) void k_page_scores(const T* __restrict__ 
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int G = Hq / Hkv;
+  const int lpp = D / 8;                 // lanes per page
+  const int ppw = kThreads / lpp;        // pages per workgroup and slot
+  const int sub = threadIdx.x % lpp;
+  // Raw 16-byte (bf16) or 32-byte (float) chunks, converted when used.
+  using Raw = typename std::conditional<sizeof(T) == 2, u32x4, floatx8>::type;
+  int pg[kPagesPerThread];
+  Raw rlo[kPagesPerThread], rhi[kPagesPerThread];
+#pragma unroll
+  for (int t = 0; t < kPagesPerThread; ++t) {
+    pg[t] = (blockIdx.x * kPagesPerThread + t) * ppw + threadIdx.x / lpp;
+    if (pg[t] < nP) {
+      const size_t off = (size_t(bg) * nP + pg[t]) * D + sub * 8;
+      rlo[t] = *reinterpret_cast<const Raw*>(kmin + off);
+      rhi[t] = *reinterpret_cast<const Raw*>(kmax + off);
+    }
+  }
   for (int e = threadIdx.x; e < G * D; e += kThreads) {
     const size_t off = (size_t(b) * Hq + size_t(g) * G) * D + e;
     if constexpr (sizeof(T) == 2) lq[e] = bf16_to_f32(q[off]);
     else lq[e] = q[off];
   }
   __syncthreads();
-  const int lpp = D / 8;                 // lanes per page
-  const int ppw = kThreads / lpp;        // pages per workgroup
-  const int sub = threadIdx.x % lpp;
-  const int p = blockIdx.x * ppw + threadIdx.x / lpp;
-  double acc = 0.0;
-  if (p < nP) {
-    const size_t off = (size_t(bg) * nP + p) * D + sub * 8;
-    float lo[8], hi[8];
-    load8(kmin + off, lo);
-    load8(kmax + off, hi);
-    for (int h = 0; h < G; ++h) {
+#pragma unroll
+  for (int t = 0; t < kPagesPerThread; ++t) {
+    double acc = 0.0;
+    if (pg[t] < nP) {
+      float lo[8], hi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const double qd = double(lq[h * D + sub * 8 + e]);
-        acc += fmax(qd * double(lo[e]), qd * double(hi[e]));
+        if constexpr (sizeof(T) == 2) {
+          lo[e] = (e & 1) ? bf16hi(rlo[t][e / 2]) : bf16lo(rlo[t][e / 2]);
+          hi[e] = (e & 1) ? bf16hi(rhi[t][e / 2]) : bf16lo(rhi[t][e / 2]);
+        } else {
+          lo[e] = rlo[t][e];
+          hi[e] = rhi[t][e];
+        }
+      }
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float qf = lq[h * D + sub * 8 + e];
+          if constexpr (sizeof(T) == 2) {
+            // bf16 x bf16 fits a float mantissa: products (in float's normal
+            // range) and their max are exact in float; only the sum needs
+            // float64.
+            acc += double(fmaxf(qf * lo[e], qf * hi[e]));
+          } else {
+            const double qd = double(qf);
+            acc += fmax(qd * double(lo[e]), qd * double(hi[e]));
+          }
+        }
       }
     }
+    for (int o = lpp / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
+    if (pg[t] < nP && sub == 0) scores[size_t(bg) * nP + pg[t]] = float(acc);
   }
-  for (int o = lpp / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
-  if (p < nP && sub == 0) scores[size_t(bg) * nP + p] = float(acc);
 }
 
 // Element-wise min and max over each page.  grid (nP, B*Hkv).
@@ -259,8 +295,8 @@ hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s) {
-  const int ppw = kThreads / (a.D / 8);
-  dim3 grid((a.nP + ppw - 1) / ppw, a.B * a.Hkv);
+  const int ppb = kThreads / (a.D / 8) * kPagesPerThread;
+  dim3 grid((a.nP + ppb - 1) / ppb, a.B * a.Hkv);
   const size_t lds = size_t(a.Hq / a.Hkv) * a.D * sizeof(float);
   if (a.dtype == 1)
     k_page_scores<uint16_t><<<grid, kThreads, lds, s>>>(
