@@ -24,6 +24,8 @@
 //     (group, query block) pairs and its L2 holds that group's K/V.
 //
 // float32 kernel: one thread per query row, K/V tiles in LDS, VALU math.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -67,15 +69,6 @@ __device__ __forceinline__ bool visible(const TileSpec& ts, int t, int s) {
   if (ts.mode == MODE_INDEX) return s <= t;
   if (ts.mode == MODE_WINDOW) return s <= t && s > t - ts.window;
   return s * ts.stride + ts.len - 1 <= t;
-}
-
-// True when every key of the tile is visible to every row in [t0, t1].
-__device__ __forceinline__ bool tile_full(const TileSpec& ts, int key0, int t0, int t1) {
-  const int k1 = key0 + ts.kt - 1;
-  if (k1 >= ts.Skv) return false;
-  if (ts.mode == MODE_INDEX) return k1 <= t0;
-  if (ts.mode == MODE_WINDOW) return k1 <= t0 && key0 > t1 - ts.window;
-  return k1 * ts.stride + ts.len - 1 <= t0;
 }
 
 // Number of key tiles for query rows [t0, t1] and the spec to walk them.
@@ -423,6 +416,317 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
   }
 }
 
+// ---------------------------------------- bf16, D = 128, 64-key tiles, ping-pong
+// Same math as k_attn_bf16, different data layout and schedule:
+//  * Two wave groups alternate ("ping-pong"): waves 0-3 and 4-7 hold one
+//    wave per SIMD each.  Time is cut into slots by workgroup barriers; in a
+//    slot one group runs the matrix products of a tile (P.V of tile n-1 and
+//    Q.K of tile n, 32 MFMAs) while the other runs a softmax, so each SIMD's
+//    matrix core and vector ALU serve different waves at the same time.
+//    Group 1 trails group 0 by one slot.
+//  * K[n+1] and V[n] are loaded into registers at the start of slot 2n and
+//    stored to LDS at the end of slot 2n+1 (16 bytes x 4 per thread), so the
+//    loads have two slots to arrive.
+//  * LDS holds K and V row-major in 1 KB chunks of four 256-byte key rows;
+//    the rows a chunk holds make the operand reads free of bank conflicts
+//    without padded rows: K chunk j (0..15) holds keys j, j+16, j+32, j+48
+//    and starts at byte j * 1040 (the 16 keys of one ds_read_b128 phase lie
+//    in chunks whose starts differ by 16 bytes modulo 256); V chunk j holds
+//    keys 16 (j / 4) + 4 q + j % 4 (q = 0..3) and starts at byte j * 1088
+//    (the four keys of one transposed read lie 64 bytes apart modulo 256).
+//  * The P.V operand V^T comes from transposed LDS reads (ds_read_b64_tr_b16:
+//    four keys of one dimension per lane), so V needs no register shuffle.
+namespace pp {
+constexpr int D = 128, KT = 64, NW = 8, NT = NW * 64;
+constexpr int KCH = 1040, VCH = 1088;  // chunk pitch in bytes
+constexpr int KBYTES = 16 * KCH, VBYTES = 16 * VCH;
+constexpr int kMaxTiles = 128;         // key tiles per query block (lane table)
+}  // namespace pp
+
+#define DSA_LDS_BF16X4(p) ((__attribute__((address_space(3))) bf16x4*)(p))
+
+__global__ __launch_bounds__(pp::NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
+void k_attn_bf16_pp(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
+  using namespace pp;
+  constexpr int ROWS = NW * 32;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VBYTES];
+
+  const int w = xcd_work_id(per_xcd);
+  if (w >= total) return;
+  const int sub = w % wg_per_qb;
+  const int rest = w / wg_per_qb;
+  const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
+  const int bg = rest / nqb;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int t0 = i * a.block;
+  const int t1 = min(a.S, t0 + a.block) - 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;
+  const int col = lane & 31, half = lane >> 5;
+
+  const uint32_t kv_bytes = uint32_t(a.Skv) * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D, kv_bytes);
+
+  // this lane's query row; rows past the group or the sequence read zeros
+  const int r = sub * ROWS + wave * 32 + col;
+  const int hh = r / a.block;
+  const int row_t = t0 + r % a.block;
+  const bool row_ok = hh < G && row_t < a.S;
+  const int row_h = g * G + (row_ok ? hh : 0);
+  bf16x8 qf[D / 16];
+  {
+    // one descriptor over the group's query heads; rows that are not ours
+    // get an offset past its end and read zeros
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+        static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(g) * G) * a.S * D,
+        uint32_t(G) * a.S * D * 2);
+    const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + half * 8) * 2) : 0x80000000u;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, ks * 32, 0));
+  }
+
+  floatx16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float m = -__builtin_inff(), l = 0.f;
+  int row_lo, row_hi;
+  row_range(a, row_t, row_lo, row_hi);
+  row_lo -= half * 4;
+  row_hi -= half * 4;
+  int blk_lo, blk_hi, dummy;
+  row_range(a, t1, blk_lo, dummy);
+  row_range(a, t0, dummy, blk_hi);
+
+  TileSpec ts;
+  const int ntiles = make_tiles(a, bg, i, t0, t1, KT, ts);
+  const float c = a.scale * kLog2e;
+  // First key of every tile, held across lanes (tile n in lane n % 64 of
+  // word n / 64) and read back with v_readlane: no memory access and no wait
+  // inside the tile loop.  The launcher sends query blocks with more than
+  // kMaxTiles tiles to k_attn_bf16.
+  const int key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
+  const int key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
+  auto key0_of = [&](int n) __attribute__((always_inline)) -> int {
+    const int lo = __builtin_amdgcn_readlane(key0_w0, n & 63);
+    const int hi = __builtin_amdgcn_readlane(key0_w1, n & 63);
+    return n < 64 ? lo : hi;
+  };
+
+  // Staging: wave w moves K chunks and V chunks 2w and 2w + 1 of a tile;
+  // lane l carries bytes [16 l, 16 l + 16) of each.
+  uint32_t kvo[2], vvo[2];
+  {
+    const int q = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const int j = 2 * wave + j2;
+      kvo[j2] = uint32_t((16 * q + j) * 256 + c16 * 16);
+      vvo[j2] = uint32_t((16 * (j / 4) + 4 * q + (j % 4)) * 256 + c16 * 16);
+    }
+  }
+  u32x4 stk[2], stv[2];
+  auto load_k = [&](int n) __attribute__((always_inline)) {
+    const uint32_t base = uint32_t(key0_of(n)) * uint32_t(D * 2);
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) stk[j2] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvo[j2], base, 0);
+  };
+  auto load_v = [&](int n) __attribute__((always_inline)) {
+    const uint32_t base = uint32_t(key0_of(n)) * uint32_t(D * 2);
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) stv[j2] = __builtin_amdgcn_raw_buffer_load_b128(vrs, vvo[j2], base, 0);
+  };
+  auto store_k = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2)
+      *reinterpret_cast<u32x4*>(&kbuf[buf][(2 * wave + j2) * KCH + lane * 16]) = stk[j2];
+  };
+  auto store_v = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2)
+      *reinterpret_cast<u32x4*>(&vbuf[buf][(2 * wave + j2) * VCH + lane * 16]) = stv[j2];
+  };
+
+  // per-lane byte offsets of the operand reads (the rest are immediates)
+  const uint32_t k_rd = (col & 15) * KCH + (col >> 4) * 256 + half * 16;
+  const uint32_t v_rd = ((lane & 15) >> 2) * VCH + half * 256 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+
+  float alpha = 1.f;     // pending rescale of o (lazy softmax)
+  bool rescale = false;
+  floatx16 s[KT / 32];   // S^T of the tile between its Q.K and its softmax
+  bf16x8 pb[KT / 16];    // P^T of the tile between its softmax and its P.V
+#pragma unroll
+  for (int ks = 0; ks < KT / 16; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[ks][e] = static_cast<__bf16>(0.0f);
+
+  // Operand reads run one k-step ahead of the MFMAs that use them; the
+  // scheduling barriers keep the compiler from hoisting every read of the
+  // phase to its top (which would need ~128 more registers).
+  auto qk = [&](int buf) __attribute__((always_inline)) {
+    const uint8_t* kb = &kbuf[buf][0] + k_rd;
+    constexpr int KS2 = D / 32;   // steps of two k-slices: 4 MFMAs each
+    bf16x8 ka[2][2][KT / 32];
+    auto rd = [&](int st, bf16x8 (&dst)[2][KT / 32]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kt = 0; kt < KT / 32; ++kt)
+          dst[h][kt] = *reinterpret_cast<const bf16x8*>(kb + kt * 512 + (2 * st + h) * 32);
+    };
+    rd(0, ka[0]);
+#pragma unroll
+    for (int st = 0; st < KS2; ++st) {
+      if (st + 1 < KS2) rd(st + 1, ka[(st + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kt = 0; kt < KT / 32; ++kt)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1][h][kt], qf[2 * st + h],
+                                                          st == 0 && h == 0 ? floatx16{} : s[kt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto pv = [&](int buf) __attribute__((always_inline)) {
+    if (rescale) {   // wave-uniform
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      alpha = 1.f;
+      rescale = false;
+    }
+    const uint8_t* vb = &vbuf[buf][0] + v_rd;
+    bf16x8 va[2][D / 32];
+    auto rd = [&](int ks, bf16x8 (&dst)[D / 32]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DSA_LDS_BF16X4(vb + ks * 4352 + dt * 64));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DSA_LDS_BF16X4(vb + ks * 4352 + 512 + dt * 64));
+        dst[dt] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    };
+    rd(0, va[0]);
+#pragma unroll
+    for (int ks = 0; ks < KT / 16; ++ks) {
+      if (ks + 1 < KT / 16) rd(ks + 1, va[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks & 1][dt], pb[ks], o[dt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto softmax = [&](int n) __attribute__((always_inline)) {
+    const int key0 = key0_of(n);
+    if (key0 < blk_lo || key0 + KT - 1 > blk_hi) {   // wave-uniform
+      asm volatile("");   // a real branch: if-converting it would copy s
+      const int lo = row_lo - key0, hi = row_hi - key0;
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int off = kt * 32 + (e >> 2) * 8 + (e & 3);
+          s[kt][e] = (off < lo || off > hi) ? -__builtin_inff() : s[kt][e];
+        }
+    }
+    // four independent chains: with one softmax wave per SIMD, latency and
+    // not issue rate would bound a single chain
+    float mx4[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+    for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx4[e & 3] = fmaxf(mx4[e & 3], s[kt][e]);
+    const float mt = half_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * c;
+    const bool grow = mt > m + kLazyRescale;
+    if (__any(grow)) {
+      // o is rescaled at the start of the next matrix phase, before the
+      // P.V of this tile adds to it
+      const float a_ = grow ? fast_exp2(m - mt) : 1.f;   // 0 when m was -inf
+      m = grow ? mt : m;
+      l *= a_;
+      alpha *= a_;
+      rescale = true;
+    }
+    const float mu = (m == -__builtin_inff()) ? 0.f : m;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KT / 16; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + e], c, -mu));
+        ls[e & 3] += p;
+        pb[ks][e] = static_cast<__bf16>(p);
+      }
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+
+  // The first matrix phase multiplies zero probabilities with V buffer 1:
+  // make sure it holds numbers.
+  for (int e = threadIdx.x; e < VBYTES / 16; e += NT)
+    *reinterpret_cast<u32x4*>(&vbuf[1][e * 16]) = u32x4{0u, 0u, 0u, 0u};
+  if (ntiles > 0) {
+    load_k(0);
+    store_k(0);
+  }
+  __syncthreads();
+  // Slot t: group 0 handles u = t, group 1 u = t - 1.  Even u = 2n: matrix
+  // phase of tile n (P.V of tile n-1 from V buffer (n-1)&1, Q.K of tile n
+  // from K buffer n&1; for n = 0 the probabilities are still zero, for
+  // n = ntiles the Q.K result is never used).  Odd u = 2n+1: softmax of tile n.
+  const int nslots = ntiles > 0 ? 2 * ntiles + 2 : 0;
+  for (int t = 0; t < nslots; ++t) {
+    const int n2 = t >> 1;
+    if ((t & 1) == 0) {
+      if (n2 + 1 < ntiles) load_k(n2 + 1);
+      if (n2 < ntiles) load_v(n2);
+    }
+    const int u = t - grp;
+    if (u >= 0) {
+      const int n = u >> 1;
+      if ((u & 1) == 0) {
+        __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+        pv((n + 1) & 1);
+        qk(n & 1);
+        __builtin_amdgcn_s_setprio(0);
+      } else if (n < ntiles) {
+        softmax(n);
+      }
+    }
+    if (t & 1) {
+      if (n2 + 1 < ntiles) store_k((n2 + 1) & 1);
+      if (n2 < ntiles) store_v(n2 & 1);
+    }
+    __syncthreads();
+  }
+
+  uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
+  const float lt = half_sum(l);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (!row_ok) return;
+  uint16_t* dst = op + ((size_t(b) * a.Hq + row_h) * a.S + row_t) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+      pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+    }
+  if (a.lse && half == 0)
+    a.lse[(size_t(b) * a.Hq + row_h) * a.S + row_t] =
+        lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+}
+
 // ----------------------------------------------------------------- float32
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
@@ -487,6 +791,13 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
   if (a.lse) a.lse[(size_t(b) * a.Hq + h) * a.S + t] = l > 0.f ? m + logf(l) : -__builtin_inff();
 }
 
+// Upper bound on the key tiles of one query block (as make_tiles counts them).
+int attn_max_tiles(const AttnArgs& a, int kt) {
+  if (a.mode == MODE_INDEX) return a.idx_width * (a.block / kt);
+  if (a.mode == MODE_WINDOW) return (a.window + a.block) / kt + 2;
+  return (a.Skv + kt - 1) / kt;
+}
+
 template <int D, int KT, int QT, int NW>
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int ROWS = NW * 32 * QT;
@@ -515,6 +826,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 #ifdef DSA_ATTN_KT128
   if (a.D == 128 && a.mode == MODE_INDEX && a.block % 128 == 0)
     return run_bf16<128, 128, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
+#endif
+#ifndef DSA_ATTN_LEGACY
+  if (a.D == 128 && !kt32 && attn_max_tiles(a, 64) <= pp::kMaxTiles) {
+    constexpr int ROWS = pp::NW * 32;
+    const int G = a.Hq / a.Hkv;
+    const int wg_per_qb = (G * a.block + ROWS - 1) / ROWS;
+    const int total = a.B * a.Hkv * nqb * wg_per_qb;
+    const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+    k_attn_bf16_pp<<<per_xcd * kNumXcd, pp::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    return hipGetLastError();
+  }
 #endif
   if (a.D == 128)
     return kt32 ? run_bf16<128, 32, DSA_ATTN_QT, DSA_ATTN_NW>(a, s)
