@@ -30,6 +30,33 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 METRIC = "sparse-attn prefill tokens/s + effective TFLOP/s; decode HBM GB/s (1 GPU)"
 
 
+ATTN_KERNEL = "k_attn_bf16_pp"
+ATTN_SOURCE = os.path.join(ROOT, "dynamic_block_sparse_head_amd", "csrc", "k_attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_pp_prefill16k_traffic.txt")
+
+
+def _measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read
+    for a plain copy of known size), or None when the summary is missing or
+    was taken on a different version of the kernel source."""
+    import hashlib
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    kv[key.strip()] = val.strip()
+        with open(ATTN_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if kv.get("source_sha256") != sha:
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def _timed(fn, iters, torch):
     """Average ms per call of fn over `iters` back-to-back calls on the
     current stream (HIP events recorded on that stream)."""
@@ -281,10 +308,10 @@ def main():
             "config": {"workload": f"{c.name}: B=1 Hq=32 Hkv=8 S=16384 D=128 block=64 top-16 + "
                                    "window 512 (scores + selection + attention)",
                        "global_batch": c.B, "seq_len": c.S, "parallelism": "single GPU"},
-            "roofline": {"bound": "mfma", "kernel": "k_attn_bf16",
+            "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL,
                          "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": None,
+                         "traffic": _measured_traffic(),
                          "flops_per_launch": r["effective_flops"],
                          "avg_launch_ms": round(r["ms_attn"], 4)},
             "prefill": {"scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
