@@ -299,7 +299,7 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, i
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   const int n_cmp = (S - len) / stride + 1;
-  REQUIRE(n_cmp <= 24576, DSA_E_UNSUPPORTED, "at most 24576 summaries (got %d)", n_cmp);
+  REQUIRE(n_cmp <= 8192, DSA_E_UNSUPPORTED, "at most 8192 summaries (got %d)", n_cmp);
   REQUIRE_PTR(q);
   REQUIRE_PTR(ck);
   REQUIRE_PTR(cv);

@@ -51,12 +51,14 @@ constexpr int kNW = 4;      // waves per workgroup
 constexpr int kQT = 2;      // 32-row tiles per wave
 constexpr int kRows = kNW * 32 * kQT;
 
-// grid (B*Hkv*nqb); dynamic LDS: colsum[n_cmp] floats
+// grid (B*Hkv*nqb); dynamic LDS: colsum[kNW][n_cmp] floats (one row per wave,
+// so a wave adds its partial column sums without waiting for the others)
 template <int D>
 __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
   constexpr int CSTR = D + 8;
+  constexpr int CPR = D / 8;                                  // 16-byte chunks per summary
+  constexpr int CPT = (32 * CPR + kNW * 64 - 1) / (kNW * 64); // chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][32 * CSTR];
-  __shared__ float wpart[kNW][32];
   extern __shared__ float colsum[];
 
   const int bg = blockIdx.x / nqb, i = blockIdx.x % nqb;
@@ -68,100 +70,118 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
   const int col = lane & 31, half = lane >> 5;
   const float c = a.scale * kLog2e;
 
-  for (int x = threadIdx.x; x < a.n_cmp; x += kNW * 64) colsum[x] = 0.f;
+  for (int x = threadIdx.x; x < kNW * a.n_cmp; x += kNW * 64) colsum[x] = 0.f;
+  float* my_colsum = colsum + wave * a.n_cmp;
 
   int c_hi = -1;
   if (t1 >= a.len - 1) c_hi = min(a.n_cmp - 1, (t1 - (a.len - 1)) / a.stride);
   const int nkt = c_hi < 0 ? 0 : c_hi / 32 + 1;
-  const uint16_t* ckp = static_cast<const uint16_t*>(a.ck) + size_t(bg) * a.n_cmp * D;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(static_cast<const uint16_t*>(a.ck) + size_t(bg) * a.n_cmp * D,
+                                               uint32_t(a.n_cmp) * D * 2);
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+
+  // summary tile staging: global -> registers one tile ahead -> LDS
+  u32x4 st[CPT];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int e = threadIdx.x + cc * kNW * 64;
+      if (e < 32 * CPR)   // past n_cmp the buffer range check returns zeros
+        st[cc] = __builtin_amdgcn_raw_buffer_load_b128(crs, uint32_t(((kt * 32 + e / CPR) * D + (e % CPR) * 8) * 2), 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int e = threadIdx.x + cc * kNW * 64;
+      if (e < 32 * CPR) *reinterpret_cast<u32x4*>(&c_lds[buf][(e / CPR) * CSTR + (e % CPR) * 8]) = st[cc];
+    }
+  };
 
   const int total_rows = G * sb;
   const int nchunks = (total_rows + kRows - 1) / kRows;
   for (int chunk = 0; chunk < nchunks; ++chunk) {
-    // this wave's query rows, their Q operands and base-2 log-sum-exp
+    // this wave's query rows, their Q operands, base-2 log-sum-exp and the
+    // last token each accumulator row may see (-1: not a row of this block)
     bf16x8 qf[kQT][D / 16];
     float lse2[kQT][16];
-    int rt[kQT];
+    int tlim[kQT][16];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const int r = chunk * kRows + wave * 32 * kQT + qt * 32 + col;
       const int hh = r / sb;
       const int t = t0 + r % sb;
       const bool ok = hh < G && t <= t1;
-      const uint16_t* src = qp + ((size_t(b) * a.Hq + g * G + hh) * a.S + t) * D + half * 8;
+      const uint16_t* src = qp + ((size_t(b) * a.Hq + g * G + (ok ? hh : 0)) * a.S + (ok ? t : t0)) * D + half * 8;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        if (ok) {
-          qf[qt][ks] = *reinterpret_cast<const bf16x8*>(src + ks * 16);
-        } else {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + ks * 16);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[qt][ks][e] = static_cast<__bf16>(0.0f);
-        }
+        for (int e = 0; e < 8; ++e) qf[qt][ks][e] = ok ? v[e] : static_cast<__bf16>(0.0f);
       }
-      // rows of the accumulator tile held by this lane: (r/4)*8 + half*4 + r%4
+      // rows of the accumulator tile held by this lane: (rr/4)*8 + half*4 + rr%4
       const int rbase = chunk * kRows + wave * 32 * kQT + qt * 32;
-      rt[qt] = rbase;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int r2 = rbase + (rr >> 2) * 8 + half * 4 + (rr & 3);
         const int h2 = r2 / sb, tt = t0 + r2 % sb;
-        float v = -__builtin_inff();
-        if (h2 < G && tt <= t1) v = a.lse[(size_t(b) * a.Hq + g * G + h2) * a.S + tt] * kLog2e;
-        lse2[qt][rr] = v;
+        const bool ok2 = h2 < G && tt <= t1;
+        const float l2 = ok2 ? a.lse[(size_t(b) * a.Hq + g * G + h2) * a.S + tt] * kLog2e : 0.f;
+        // rows outside the block get +inf (probability 0 everywhere); rows
+        // that see no summary have lse -inf and are cut by tlim
+        lse2[qt][rr] = !ok2 ? __builtin_inff() : (l2 == -__builtin_inff() ? 0.f : l2);
+        tlim[qt][rr] = ok2 ? tt : -1;
       }
     }
 
-    auto stage = [&](int kt, int buf) {
-      for (int e = threadIdx.x; e < 32 * (D / 8); e += kNW * 64) {
-        const int key = kt * 32 + e / (D / 8), dc = e % (D / 8);
-        u32x4 w = u32x4{0u, 0u, 0u, 0u};
-        if (key < a.n_cmp) w = *reinterpret_cast<const u32x4*>(ckp + size_t(key) * D + dc * 8);
-        *reinterpret_cast<u32x4*>(&c_lds[buf][(e / (D / 8)) * CSTR + dc * 8]) = w;
-      }
-    };
-    if (nkt > 0) stage(0, 0);
+    if (nkt > 0) {
+      load(0);
+      store(0);
+    }
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < nkt) stage(kt + 1, buf ^ 1);
+      if (kt + 1 < nkt) load(kt + 1);
       floatx16 s[kQT];
-#pragma unroll
-      for (int qt = 0; qt < kQT; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qt][r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 cb = *reinterpret_cast<const bf16x8*>(&c_lds[buf][col * CSTR + ks * 16 + half * 8]);
 #pragma unroll
         for (int qt = 0; qt < kQT; ++qt)
-          s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], cb, s[qt], 0, 0, 0);
+          s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], cb, ks == 0 ? floatx16{} : s[qt], 0, 0, 0);
       }
       // lane holds summary kt*32+col for 16 rows of each row tile
       const int cs = kt * 32 + col;
-      const int cend = cs * a.stride + a.len - 1;
+      const int cend = cs * a.stride + a.len - 1;   // its last token
       float part = 0.f;
+      if ((kt * 32 + 31) * a.stride + a.len - 1 <= t0) {
+        // every summary of the tile ends before the block's first row: all
+        // rows of the block see all of them (rows outside it add 0)
 #pragma unroll
-      for (int qt = 0; qt < kQT; ++qt)
+        for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int r2 = rt[qt] + (rr >> 2) * 8 + half * 4 + (rr & 3);
-          const int tt = t0 + r2 % sb;
-          const bool vis = cs < a.n_cmp && cend <= tt && lse2[qt][rr] != -__builtin_inff();
-          if (vis) part += fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
-        }
-      part += __shfl_xor(part, 32);
-      if (half == 0) wpart[wave][col] = part;
-      __syncthreads();
-      if (threadIdx.x < 32) {
-        float t = 0.f;
+          for (int rr = 0; rr < 16; ++rr) part += fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
+      } else {
 #pragma unroll
-        for (int w2 = 0; w2 < kNW; ++w2) t += wpart[w2][threadIdx.x];
-        const int cc = kt * 32 + threadIdx.x;
-        if (cc < a.n_cmp) colsum[cc] += t;
+        for (int qt = 0; qt < kQT; ++qt)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const float p = fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
+            part += (cend <= tlim[qt][rr]) ? p : 0.f;
+          }
       }
+      part += __shfl_xor(part, 32);
+      if (half == 0 && cs < a.n_cmp) my_colsum[cs] += part;
+      if (kt + 1 < nkt) store(buf ^ 1);
       __syncthreads();
     }
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < a.n_cmp; x += kNW * 64) {
+    float t = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kNW; ++w2) t += colsum[w2 * a.n_cmp + x];
+    colsum[x] = t;   // row 0 now holds the block's column sums
   }
   __syncthreads();
 
@@ -229,7 +249,7 @@ hipError_t launch_nsa_compress(const void* k, const void* v, int B, int Hkv, int
 
 hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s) {
   const int nqb = (a.S + a.sel_block - 1) / a.sel_block;
-  const size_t lds = size_t(a.n_cmp) * sizeof(float);
+  const size_t lds = size_t(kNW) * a.n_cmp * sizeof(float);
   if (a.D == 128)
     k_cmp_block_scores<128><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
   else

@@ -176,6 +176,7 @@ int dsa_nsa_compress(int dtype, const void* k, const void* v, int B, int Hkv, in
  * summaries overlapping block j, each split in proportion to its overlap
  * with the block, summed over the block's rows and the group's heads and
  * divided by rows x heads (values in [0,1]; 0 for j > i).
+ * Limits: n_cmp <= 8192 (else DSA_E_UNSUPPORTED).
  */
 int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv,
                      int B, int Hq, int Hkv, int S, int D, int len, int stride, int sel_block,
