@@ -225,6 +225,78 @@ __global__ __launch_bounds__(kThreads) void k_page_scores(const T* __restrict__ 
   }
 }
 
+// bf16 page bound scores for a compile-time group size.  Since kmax >= kmin,
+// max(q kmin, q kmax) is q kmax for q >= 0 and q kmin otherwise, so a page's
+// score is sum over d of kmax_d P_d + kmin_d N_d with P_d (N_d) the sum of the
+// group's non-negative (negative) query components in dimension d.  P and N
+// are formed once per lane in float64 (exact for bf16 inputs); each page then
+// costs two float64 FMAs per dimension instead of a float64 add per head and
+// dimension.  Each workgroup walks kIters slots of pages with the next slot's
+// bound loads in flight while the current one is reduced; no LDS, no barrier.
+constexpr int kIters = 4;
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ kmin,
+                                                               const uint16_t* __restrict__ kmax,
+                                                               int Hq, int Hkv, int nP, int D,
+                                                               float* __restrict__ scores) {
+  const int bg = blockIdx.y;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int lpp = D / 8;
+  const int ppw = kThreads / lpp;
+  const int sub = threadIdx.x % lpp;
+  double pos[8], neg[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) pos[e] = neg[e] = 0.0;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(q + (size_t(b) * Hq + size_t(g) * G + h) * D + sub * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (e & 1) ? bf16hi(w[e / 2]) : bf16lo(w[e / 2]);
+      if (x >= 0.f) pos[e] += double(x);
+      else neg[e] += double(x);
+    }
+  }
+  u32x4 rlo[2][kPagesPerThread], rhi[2][kPagesPerThread];
+  auto page_of = [&](int it, int t) {
+    return ((blockIdx.x * kIters + it) * kPagesPerThread + t) * ppw + int(threadIdx.x) / lpp;
+  };
+  auto load = [&](int it, int buf) {
+#pragma unroll
+    for (int t = 0; t < kPagesPerThread; ++t) {
+      const int p = page_of(it, t);
+      if (p < nP) {
+        const size_t off = (size_t(bg) * nP + p) * D + sub * 8;
+        rlo[buf][t] = *reinterpret_cast<const u32x4*>(kmin + off);
+        rhi[buf][t] = *reinterpret_cast<const u32x4*>(kmax + off);
+      }
+    }
+  };
+  load(0, 0);
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    if (it + 1 < kIters) load(it + 1, (it + 1) & 1);
+#pragma unroll
+    for (int t = 0; t < kPagesPerThread; ++t) {
+      const int p = page_of(it, t);
+      double acc = 0.0;
+      if (p < nP) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lo = (e & 1) ? bf16hi(rlo[it & 1][t][e / 2]) : bf16lo(rlo[it & 1][t][e / 2]);
+          const float hi = (e & 1) ? bf16hi(rhi[it & 1][t][e / 2]) : bf16lo(rhi[it & 1][t][e / 2]);
+          acc = __builtin_fma(double(hi), pos[e], acc);
+          acc = __builtin_fma(double(lo), neg[e], acc);
+        }
+      }
+      for (int o = lpp / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
+      if (p < nP && sub == 0) scores[size_t(bg) * nP + p] = float(acc);
+    }
+  }
+}
+
 // Element-wise min and max over each page.  grid (nP, B*Hkv).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ k, int L, int D,
@@ -295,6 +367,21 @@ hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  if (a.dtype == 1 && (G == 1 || G == 2 || G == 4 || G == 8)) {
+    const int ppb = kThreads / (a.D / 8) * kPagesPerThread * kIters;
+    dim3 grid((a.nP + ppb - 1) / ppb, a.B * a.Hkv);
+    const auto* q = static_cast<const uint16_t*>(a.q);
+    const auto* lo = static_cast<const uint16_t*>(a.kmin);
+    const auto* hi = static_cast<const uint16_t*>(a.kmax);
+    switch (G) {
+      case 1: k_page_scores_bf16<1><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
+      case 2: k_page_scores_bf16<2><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
+      case 4: k_page_scores_bf16<4><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
+      default: k_page_scores_bf16<8><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
+    }
+    return hipGetLastError();
+  }
   const int ppb = kThreads / (a.D / 8) * kPagesPerThread;
   dim3 grid((a.nP + ppb - 1) / ppb, a.B * a.Hkv);
   const size_t lds = size_t(a.Hq / a.Hkv) * a.D * sizeof(float);
