@@ -72,7 +72,7 @@ def _timed(fn, iters, torch):
 
 def bench_prefill(args, torch):
     from dynamic_block_sparse_head_amd import configs, inputs
-    from dynamic_block_sparse_head_amd.pipeline import PrefillPlan
+    from dynamic_block_sparse_head_amd.pipeline import GraphedStep, PrefillPlan
 
     c = configs.PREFILL_16K
     x = inputs.prefill_inputs(c, seed=0, device="cuda")
@@ -85,6 +85,11 @@ def bench_prefill(args, torch):
     ms_step = _timed(lambda: plan.run(q, k, v), args.steps, torch)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same step replayed as one HIP graph, for reference (the launches
+    # are not what separates the kernels: the gaps stay)
+    step = GraphedStep(lambda: plan.run(q, k, v), warmup=args.warmup)
+    ms_graph = _timed(step, args.steps, torch)
+    torch.cuda.synchronize()
     # the kernels one by one, same inputs (outputs rewritten identically)
     reps = max(args.steps, 10)
     ms_scores = _timed(lambda: plan.score(q, k), reps, torch)
@@ -96,7 +101,7 @@ def bench_prefill(args, torch):
     tokens = c.B * c.S
     return {
         "cfg": c, "ms_step": ms_step, "wall_s": wall, "ms_scores": ms_scores, "ms_topk": ms_topk,
-        "ms_attn": ms_attn, "selected_block_pairs": sel, "effective_flops": flops,
+        "ms_attn": ms_attn, "ms_graph": ms_graph, "selected_block_pairs": sel, "effective_flops": flops,
         "tokens_per_step": tokens,
     }
 
@@ -131,7 +136,7 @@ def bench_decode(torch, iters=20, n_query_sets=4):
     timed step.  The query rotates among several sets with their own
     selections."""
     from dynamic_block_sparse_head_amd import configs, inputs
-    from dynamic_block_sparse_head_amd.pipeline import DecodePlan
+    from dynamic_block_sparse_head_amd.pipeline import DecodePlan, GraphedStep
     from dynamic_block_sparse_head_amd.metrics import decode_selected_bytes
 
     c = configs.DECODE_128K
@@ -142,7 +147,7 @@ def bench_decode(torch, iters=20, n_query_sets=4):
     plan.build_metadata(x["k"])
     flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
     s = torch.cuda.current_stream()
-    t_step = t_attn = t_meta = 0.0
+    t_step = t_attn = t_meta = t_graph = 0.0
     plan.run(qs[0], x["k"], x["v"])
     for it in range(iters):
         q = qs[it % n_query_sets]
@@ -157,6 +162,18 @@ def bench_decode(torch, iters=20, n_query_sets=4):
         e[2].synchronize()
         t_step += e[0].elapsed_time(e[2])
         t_attn += e[1].elapsed_time(e[2])
+    # the whole step as one HIP graph; the query is copied into its input first
+    q_in = qs[0].clone()
+    step = GraphedStep(lambda: plan.run(q_in, x["k"], x["v"]))
+    for it in range(iters):
+        q_in.copy_(qs[it % n_query_sets])
+        flush.max()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(s)
+        step()
+        e[1].record(s)
+        e[1].synchronize()
+        t_graph += e[0].elapsed_time(e[1])
     # reference: a plain device copy of 1 GiB (read + write) on the same GPU
     src = flush[: (1 << 27)]
     dst = torch.empty_like(src)
@@ -174,10 +191,12 @@ def bench_decode(torch, iters=20, n_query_sets=4):
     cache_bytes = 2 * c.B * c.Hkv * c.L * c.D * 2
     gbs = sel_bytes / (ms_attn * 1e-3) / 1e9
     copy_gbs = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
-    del x, qs, plan, flush, src, dst
+    ms_graph = t_graph / iters
+    del x, qs, plan, flush, src, dst, step, q_in
     return {"workload": f"{c.name}: B=16 L=131072 page=64 Hq=32 Hkv=8 D=128, top {c.topk} of "
                         f"{c.n_pages} pages; LLC swept by a 1 GiB read between steps",
             "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.B / (ms_step * 1e-3), 1),
+            "ms_per_step_graph_replay": round(ms_graph, 4),
             "attn_ms": round(ms_attn, 4), "selected_bytes": sel_bytes,
             "attn_hbm_gbs": round(gbs, 1), "attn_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "step_gbs_incl_metadata": round((sel_bytes + meta_bytes) / (ms_step * 1e-3) / 1e9, 1),
@@ -314,7 +333,8 @@ def main():
                          "traffic": _measured_traffic(),
                          "flops_per_launch": r["effective_flops"],
                          "avg_launch_ms": round(r["ms_attn"], 4)},
-            "prefill": {"scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
+            "prefill": {"step_ms_graph_replay": round(r["ms_graph"], 4),
+                        "scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
                         "attn_ms": round(r["ms_attn"], 4),
                         "attn_tokens_per_s": round(c.S / (r["ms_attn"] * 1e-3), 1),
                         "selected_block_pairs": r["selected_block_pairs"],

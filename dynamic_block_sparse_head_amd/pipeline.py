@@ -122,3 +122,26 @@ class NSAPlan:
                                   self.o_win)
         L.dsa_nsa_combine(self.o_cmp, self.o_sel, self.o_win, z, self.out)
         return self.out
+
+
+class GraphedStep:
+    """One step (a zero-argument callable issuing library calls on the current
+    stream) captured once into a HIP graph and replayed: the step's launches
+    then cost one graph launch.  The library allocates nothing, synchronizes
+    nothing and clears no memory with memset inside its calls, so its kernels
+    capture as plain kernel nodes.  Inputs and outputs are the tensors the
+    callable closes over; refill those in place between replays."""
+
+    def __init__(self, fn, warmup=2):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            fn()
+
+    def __call__(self):
+        self.graph.replay()
