@@ -30,9 +30,9 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 METRIC = "sparse-attn prefill tokens/s + effective TFLOP/s; decode HBM GB/s (1 GPU)"
 
 
-ATTN_KERNEL = "k_attn_bf16_pp"
+ATTN_KERNEL = "k_attn_bf16_d128"
 ATTN_SOURCE = os.path.join(ROOT, "dynamic_block_sparse_head_amd", "csrc", "k_attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_pp_prefill16k_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_d128_prefill16k_traffic.txt")
 
 
 def _measured_traffic():

@@ -416,17 +416,12 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
   }
 }
 
-// ---------------------------------------- bf16, D = 128, 64-key tiles, ping-pong
-// Same math as k_attn_bf16, different data layout and schedule:
-//  * Two wave groups alternate ("ping-pong"): waves 0-3 and 4-7 hold one
-//    wave per SIMD each.  Time is cut into slots by workgroup barriers; in a
-//    slot one group runs the matrix products of a tile (P.V of tile n-1 and
-//    Q.K of tile n, 32 MFMAs) while the other runs a softmax, so each SIMD's
-//    matrix core and vector ALU serve different waves at the same time.
-//    Group 1 trails group 0 by one slot.
-//  * K[n+1] and V[n] are loaded into registers at the start of slot 2n and
-//    stored to LDS at the end of slot 2n+1 (16 bytes x 4 per thread), so the
-//    loads have two slots to arrive.
+// ---------------------------------------------- bf16, D = 128, 64-key tiles
+// Same math as k_attn_bf16, different data layout and staging:
+//  * Per tile every wave runs Q.K, the softmax and P.V of its 32 rows; one
+//    barrier per tile.  K and V of tile n+1 are loaded into registers at the
+//    start of tile n (16 bytes x 4 per thread) and stored to the other LDS
+//    buffer at its end.
 //  * LDS holds K and V row-major in 1 KB chunks of four 256-byte key rows;
 //    the rows a chunk holds make the operand reads free of bank conflicts
 //    without padded rows: K chunk j (0..15) holds keys j, j+16, j+32, j+48
@@ -436,18 +431,21 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
 //    (the four keys of one transposed read lie 64 bytes apart modulo 256).
 //  * The P.V operand V^T comes from transposed LDS reads (ds_read_b64_tr_b16:
 //    four keys of one dimension per lane), so V needs no register shuffle.
-namespace pp {
+//  * Query rows load through one buffer descriptor per group, and the first
+//    key of every tile is kept in a lane and read with v_readlane, so the
+//    tile loop touches memory only for the K/V stream.
+namespace d128 {
 constexpr int D = 128, KT = 64, NW = 8, NT = NW * 64;
 constexpr int KCH = 1040, VCH = 1088;  // chunk pitch in bytes
 constexpr int KBYTES = 16 * KCH, VBYTES = 16 * VCH;
 constexpr int kMaxTiles = 128;         // key tiles per query block (lane table)
-}  // namespace pp
+}  // namespace d128
 
 #define DSA_LDS_BF16X4(p) ((__attribute__((address_space(3))) bf16x4*)(p))
 
-__global__ __launch_bounds__(pp::NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
-void k_attn_bf16_pp(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
-  using namespace pp;
+__global__ __launch_bounds__(d128::NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
+void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
+  using namespace d128;
   constexpr int ROWS = NW * 32;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VBYTES];
@@ -465,7 +463,6 @@ void k_attn_bf16_pp(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = wave >> 2;
   const int col = lane & 31, half = lane >> 5;
 
   const uint32_t kv_bytes = uint32_t(a.Skv) * D * 2;
@@ -562,10 +559,6 @@ void k_attn_bf16_pp(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) 
   bool rescale = false;
   floatx16 s[KT / 32];   // S^T of the tile between its Q.K and its softmax
   bf16x8 pb[KT / 16];    // P^T of the tile between its softmax and its P.V
-#pragma unroll
-  for (int ks = 0; ks < KT / 16; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[ks][e] = static_cast<__bf16>(0.0f);
 
   // Operand reads run one k-step ahead of the MFMAs that use them; the
   // scheduling barriers keep the compiler from hoisting every read of the
@@ -648,8 +641,8 @@ void k_attn_bf16_pp(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) 
     const float mt = half_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]))) * c;
     const bool grow = mt > m + kLazyRescale;
     if (__any(grow)) {
-      // o is rescaled at the start of the next matrix phase, before the
-      // P.V of this tile adds to it
+      // o is rescaled at the start of the P.V of this tile, before the
+      // tile adds to it
       const float a_ = grow ? fast_exp2(m - mt) : 1.f;   // 0 when m was -inf
       m = grow ? mt : m;
       l *= a_;
@@ -669,41 +662,29 @@ void k_attn_bf16_pp(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) 
     l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
-  // The first matrix phase multiplies zero probabilities with V buffer 1:
-  // make sure it holds numbers.
-  for (int e = threadIdx.x; e < VBYTES / 16; e += NT)
-    *reinterpret_cast<u32x4*>(&vbuf[1][e * 16]) = u32x4{0u, 0u, 0u, 0u};
   if (ntiles > 0) {
     load_k(0);
+    load_v(0);
     store_k(0);
+    store_v(0);
   }
   __syncthreads();
-  // Slot t: group 0 handles u = t, group 1 u = t - 1.  Even u = 2n: matrix
-  // phase of tile n (P.V of tile n-1 from V buffer (n-1)&1, Q.K of tile n
-  // from K buffer n&1; for n = 0 the probabilities are still zero, for
-  // n = ntiles the Q.K result is never used).  Odd u = 2n+1: softmax of tile n.
-  const int nslots = ntiles > 0 ? 2 * ntiles + 2 : 0;
-  for (int t = 0; t < nslots; ++t) {
-    const int n2 = t >> 1;
-    if ((t & 1) == 0) {
-      if (n2 + 1 < ntiles) load_k(n2 + 1);
-      if (n2 < ntiles) load_v(n2);
+  for (int n = 0; n < ntiles; ++n) {
+    const bool more = n + 1 < ntiles;
+    if (more) {
+      load_k(n + 1);
+      load_v(n + 1);
     }
-    const int u = t - grp;
-    if (u >= 0) {
-      const int n = u >> 1;
-      if ((u & 1) == 0) {
-        __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
-        pv((n + 1) & 1);
-        qk(n & 1);
-        __builtin_amdgcn_s_setprio(0);
-      } else if (n < ntiles) {
-        softmax(n);
-      }
-    }
-    if (t & 1) {
-      if (n2 + 1 < ntiles) store_k((n2 + 1) & 1);
-      if (n2 < ntiles) store_v(n2 & 1);
+    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+    qk(n & 1);
+    __builtin_amdgcn_s_setprio(0);
+    softmax(n);
+    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+    pv(n & 1);
+    __builtin_amdgcn_s_setprio(0);
+    if (more) {
+      store_k((n + 1) & 1);
+      store_v((n + 1) & 1);
     }
     __syncthreads();
   }
@@ -828,13 +809,13 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     return run_bf16<128, 128, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
 #endif
 #ifndef DSA_ATTN_LEGACY
-  if (a.D == 128 && !kt32 && attn_max_tiles(a, 64) <= pp::kMaxTiles) {
-    constexpr int ROWS = pp::NW * 32;
+  if (a.D == 128 && !kt32 && attn_max_tiles(a, 64) <= d128::kMaxTiles) {
+    constexpr int ROWS = d128::NW * 32;
     const int G = a.Hq / a.Hkv;
     const int wg_per_qb = (G * a.block + ROWS - 1) / ROWS;
     const int total = a.B * a.Hkv * nqb * wg_per_qb;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
-    k_attn_bf16_pp<<<per_xcd * kNumXcd, pp::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    k_attn_bf16_d128<<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();
   }
 #endif
