@@ -30,5 +30,9 @@ something other than itself):
                                                        by those two (documented as partly pinned)
   nsa.window_attention                               — W >= S dense limit, W = 1 identity
   nsa.combine                                        — closed form when branches coincide
+  backward.sparse_attention_backward                 — central finite differences of the
+                                                       forward oracle, autograd of a dense masked
+                                                       formulation, exact zeros off the mask,
+                                                       softmax identities
 """
-from . import decode, nsa, prefill  # noqa: F401
+from . import backward, decode, nsa, prefill  # noqa: F401
