@@ -33,6 +33,10 @@ SIGNATURES = {
     "dsa_topk_select": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
     "dsa_sparse_attn_prefill": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
                                 + [_c_int] * 3 + [_c_float, _vp, _vp, _vp]),
+    "dsa_sparse_attn_prefill_backward_workspace_size": (_c_size, [_c_int] * 6),
+    "dsa_sparse_attn_prefill_backward": (_c_int, [_c_int] + [_vp] * 4 + [_vp, _vp]
+                                         + [_c_int] * 5 + [_vp, _vp] + [_c_int] * 2
+                                         + [_c_float, _vp, _c_size, _vp, _vp, _vp, _vp]),
     "dsa_page_minmax": (_c_int, [_c_int, _vp] + [_c_int] * 5 + [_vp, _vp, _vp]),
     "dsa_sparse_attn_decode_workspace_size": (_c_size, [_c_int] * 6),
     "dsa_sparse_attn_decode": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
@@ -148,6 +152,24 @@ def dsa_sparse_attn_prefill(q, k, v, idx, count, block, window, scale, out, lse=
         _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), width, block, window,
         float(scale), _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream))
     _check(st, "dsa_sparse_attn_prefill")
+
+
+def dsa_sparse_attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D, block) -> int:
+    return load().dsa_sparse_attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D, block)
+
+
+def dsa_sparse_attn_prefill_backward(q, k, v, out, lse, dout, idx, count, block, scale, workspace,
+                                     dq, dk, dv, stream=None):
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    st = load().dsa_sparse_attn_prefill_backward(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
+        _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _ptr(dout, "dout", q.dtype),
+        B, Hq, Hkv, S, D, _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32),
+        idx.shape[-1], block, float(scale), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(dq, "dq", q.dtype),
+        _ptr(dk, "dk", q.dtype), _ptr(dv, "dv", q.dtype), _stream(stream))
+    _check(st, "dsa_sparse_attn_prefill_backward")
 
 
 def dsa_page_minmax(k, page, kmin, kmax, stream=None):

@@ -209,6 +209,51 @@ int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void*
                     "dsa_sparse_attn_prefill");
 }
 
+size_t dsa_sparse_attn_prefill_backward_workspace_size(int B, int Hq, int Hkv, int S, int D,
+                                                       int block) {
+  (void)D;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || block <= 0) return 0;
+  return dsa::attn_backward_workspace_bytes(B, Hq, Hkv, S, block);
+}
+
+int dsa_sparse_attn_prefill_backward(int dtype, const void* q, const void* k, const void* v,
+                                     const void* out, const float* lse, const void* dout, int B,
+                                     int Hq, int Hkv, int S, int D, const int32_t* idx,
+                                     const int32_t* count, int idx_width, int block, float scale,
+                                     void* workspace, size_t workspace_bytes, void* dq, void* dk,
+                                     void* dv, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  TRY(check_block(block, "block"));
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE(idx_width >= 1, DSA_E_ARG, "idx_width must be >= 1 (got %d)", idx_width);
+  const long long nb = (S + block - 1) / block;
+  REQUIRE((long long)B * Hkv * nb * nb < (1ll << 31), DSA_E_UNSUPPORTED,
+          "B*Hkv*nb*nb too large for the inverted block lists");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(dout);
+  REQUIRE_PTR(dq);
+  REQUIRE_PTR(dk);
+  REQUIRE_PTR(dv);
+  REQUIRE(lse != nullptr, DSA_E_ARG, "lse must not be NULL");
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  const size_t need = dsa::attn_backward_workspace_bytes(B, Hq, Hkv, S, block);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
+          "the backward needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  dsa::AttnBwdArgs a{q,     k,   v,     out,   lse, dout, idx,       count,   B,  Hq, Hkv,
+                     S,     D,   block, idx_width, scale, workspace, dq, dk, dv};
+  return hip_status(dsa::launch_attn_backward(a, static_cast<hipStream_t>(stream)),
+                    "dsa_sparse_attn_prefill_backward");
+}
+
 int dsa_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int page, void* kmin,
                     void* kmax, void* stream) {
   g_err.clear();

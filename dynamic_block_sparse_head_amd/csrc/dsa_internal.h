@@ -61,6 +61,23 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+struct AttnBwdArgs {
+  const void* q;        // [B,Hq,S,D] bf16
+  const void* k;        // [B,Hkv,S,D]
+  const void* v;
+  const void* out;      // forward output [B,Hq,S,D]
+  const float* lse;     // forward log-sum-exp [B,Hq,S]
+  const void* dout;     // [B,Hq,S,D]
+  const int32_t* idx;   // [B,Hkv,nqb,idx_width]
+  const int32_t* count; // [B,Hkv,nqb]
+  int B, Hq, Hkv, S, D, block, idx_width;
+  float scale;
+  void* workspace;      // attn_backward_workspace_bytes()
+  void *dq, *dk, *dv;   // [B,Hq,S,D], [B,Hkv,S,D], [B,Hkv,S,D]
+};
+size_t attn_backward_workspace_bytes(int B, int Hq, int Hkv, int S, int block);
+hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t s);
+
 struct DecodeArgs {
   const void* q;        // [B,Hq,D] bf16
   const void* k;        // [B,Hkv,L,D]

@@ -17,7 +17,7 @@ import torch
 
 from .configs import DecodeConfig, NSAConfig, PrefillConfig
 
-_TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gates": 3, "needles": 4, "clusters": 5}
+_TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gates": 3, "needles": 4, "clusters": 5, "dout": 6}
 
 
 def _dtype(name: str) -> torch.dtype:
@@ -127,6 +127,13 @@ def prefill_inputs(cfg: PrefillConfig, seed: int = 0, device="cpu"):
         k[b, g, n * blk:(n + 1) * blk, :] += (cfg.needle_alpha * direction).to(torch.float32)
     return {"q": q.contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous(),
             "needles": needles}
+
+
+def grad_output(cfg: PrefillConfig, seed: int = 0, device="cpu"):
+    """Upstream gradient dout [B,Hq,S,D] ~ N(0,1) in cfg.dtype, for the backward."""
+    dev = torch.device(device)
+    d = _normal((cfg.B, cfg.Hq, cfg.S, cfg.D), 1.0, _gen(dev, seed, cfg.name, "dout"), dev)
+    return d.to(_dtype(cfg.dtype)).contiguous()
 
 
 def decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):

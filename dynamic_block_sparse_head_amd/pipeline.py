@@ -50,6 +50,21 @@ class PrefillPlan:
         self.attend(q, k, v)
         return self.out
 
+    def backward(self, q, k, v, dout):
+        """dq, dk, dv of the last run's attention for the upstream gradient
+        dout ([DMA] §四-§五); the run's index lists are held fixed."""
+        if not hasattr(self, "dq"):
+            B, Hq, Hkv, S, D = self.B, self.Hq, self.Hkv, self.S, self.D
+            ws = L.dsa_sparse_attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D, self.block)
+            self.bwd_ws = _empty((ws,), torch.uint8, q.device)
+            self.dq = _empty((B, Hq, S, D), q.dtype, q.device)
+            self.dk = _empty((B, Hkv, S, D), q.dtype, q.device)
+            self.dv = _empty((B, Hkv, S, D), q.dtype, q.device)
+        L.dsa_sparse_attn_prefill_backward(q, k, v, self.out, self.lse, dout, self.idx, self.count,
+                                           self.block, self.scale, self.bwd_ws, self.dq, self.dk,
+                                           self.dv)
+        return self.dq, self.dk, self.dv
+
 
 class DecodePlan:
     """Page bounds -> top pages -> attention over the selected pages ([SF] §二-§四)."""

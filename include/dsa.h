@@ -131,6 +131,37 @@ int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void*
                             int window, float scale, void* out, float* lse, void* stream);
 
 /*
+ * Gradients of dsa_sparse_attn_prefill in index mode ([DMA] §四-§五: the
+ * masked computation stays differentiable; a position the mask removes gets
+ * exactly zero gradient, the kept positions the ordinary softmax gradient).
+ * The index lists are constants of the backward: selection is a discrete
+ * choice and passes no gradient.
+ *
+ * q, out, dout, dq [B,Hq,S,D]; k, v, dk, dv [B,Hkv,S,D]; idx, count,
+ * idx_width, block and scale exactly as given to the forward; out and lse
+ * [B,Hq,S] are the forward's results for these inputs.  With P the
+ * forward's softmax weights (recomputed from lse), dP = dout . v and
+ * Dt = dout . out per row:
+ *   dS = P (dP - Dt),  dq = scale dS k,  dk = scale dS^T q,  dv = P^T dout,
+ * summed over every row of the group's query heads that sees the key.
+ * Keys that no row sees get zero.  Every output element is written.
+ * Internal math: bf16 products (P and dS rounded to bf16) with float32
+ * accumulation; sums run in a fixed order, so results are reproducible.
+ * Needs a workspace of dsa_sparse_attn_prefill_backward_workspace_size()
+ * bytes (row terms and the inverted block lists); its contents on entry do
+ * not matter.  bf16 only; idx rows strictly ascending within count.
+ */
+size_t dsa_sparse_attn_prefill_backward_workspace_size(int B, int Hq, int Hkv, int S, int D,
+                                                       int block);
+int dsa_sparse_attn_prefill_backward(int dtype, const void* q, const void* k, const void* v,
+                                     const void* out, const float* lse, const void* dout,
+                                     int B, int Hq, int Hkv, int S, int D,
+                                     const int32_t* idx, const int32_t* count, int idx_width,
+                                     int block, float scale, void* workspace,
+                                     size_t workspace_bytes, void* dq, void* dk, void* dv,
+                                     void* stream);
+
+/*
  * Per-page key summaries for decode ([DMA] §三 per-block cache summaries;
  * [SF] §四 page granularity): kmin/kmax [B,Hkv,L/page,D] = element-wise
  * minimum / maximum of K [B,Hkv,L,D] over each page (exact).  L % page == 0.

@@ -10,6 +10,13 @@ Acceptance rules (the bar every GPU result is held to):
     be far smaller than 2e-2, also max-abs <= 2^-6 * max|oracle| (eight bf16
     unit roundoffs: P and O are rounded to bf16 once each).
   * float32 outputs: max-abs <= 1e-4.
+  * bf16 gradients (dq, dk, dv of the backward): max-abs <= 2^-6 * max|oracle|
+    and ||gpu - oracle||_2 <= 2^-7 * ||oracle||_2.  P and dS enter the
+    second products rounded to bf16 and the results are rounded to bf16,
+    about three unit roundoffs (2^-9 each) per term; the norm bound leaves
+    a factor ~5 over that and catches a systematic error that the max test
+    alone could hide.  Gradient magnitudes (dq ~ 1e-4 at the 16K shape)
+    make fixed absolute bounds meaningless, so both bounds are relative.
 """
 from __future__ import annotations
 
@@ -85,6 +92,21 @@ def check_bf16(gpu, ref, what=""):
     assert err.mean() <= BF16_MEAN_ABS, f"{what}: mean-abs {err.mean():.3e}"
     assert err.max() <= BF16_REL_TO_MAX * scale, f"{what}: max-abs {err.max():.3e} > 2^-6 * {scale:.3e}"
     return err.max(), err.mean()
+
+
+GRAD_REL_TO_MAX, GRAD_REL_NORM = 2.0 ** -6, 2.0 ** -7
+
+
+def check_grad(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.isfinite(gpu).all(), f"{what}: non-finite GPU values"
+    err = np.abs(gpu - ref)
+    scale = np.abs(ref).max()
+    assert err.max() <= GRAD_REL_TO_MAX * scale, f"{what}: max-abs {err.max():.3e} > 2^-6 * {scale:.3e}"
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= GRAD_REL_NORM, f"{what}: relative norm error {rel:.3e}"
+    return err.max() / scale, rel
 
 
 def check_f32(gpu, ref, what=""):

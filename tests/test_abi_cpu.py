@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -109,6 +109,36 @@ def test_scores_and_decode_validation():
     assert dec(*a) == L.DSA_E_UNSUPPORTED                          # G = 6
     a = list(args); a[11] = 5000
     assert dec(*a) == L.DSA_E_ARG                                  # more pages than the cache
+
+
+def test_backward_validation():
+    lib = L.load()
+    ws = lib.dsa_sparse_attn_prefill_backward_workspace_size(1, 32, 8, 16384, 128, 64)
+    nb = 256
+    assert ws == 32 * 16384 * 4 + 8 * nb * nb * 4 + 8 * nb * 4
+    f = lib.dsa_sparse_attn_prefill_backward
+    ok = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, B=1, Hq=32, Hkv=8,
+              S=16384, D=128, idx=FAKE, count=FAKE, width=24, block=64, scale=0.1, ws=FAKE,
+              ws_bytes=ws, dq=FAKE, dk=FAKE, dv=FAKE, stream=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(a["dtype"], a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["B"],
+                 a["Hq"], a["Hkv"], a["S"], a["D"], a["idx"], a["count"], a["width"], a["block"],
+                 a["scale"], a["ws"], a["ws_bytes"], a["dq"], a["dk"], a["dv"], a["stream"])
+
+    assert call(dtype=0) == L.DSA_E_UNSUPPORTED           # float32 backward
+    assert call(D=96) == L.DSA_E_UNSUPPORTED
+    assert call(block=40) == L.DSA_E_UNSUPPORTED
+    assert call(ws_bytes=ws - 1) == L.DSA_E_WORKSPACE
+    assert call(ws=None) == L.DSA_E_WORKSPACE
+    assert call(lse=None) == L.DSA_E_ARG
+    assert call(count=None) == L.DSA_E_ARG
+    assert call(dk=MISALIGNED) == L.DSA_E_ARG
+    assert "dk" in _err()
+    assert call(width=0) == L.DSA_E_ARG
+    assert call(scale=-1.0) == L.DSA_E_ARG
+    assert call(Hq=12) == L.DSA_E_ARG                     # Hq % Hkv
 
 
 def test_nsa_validation():
