@@ -7,11 +7,12 @@ the bf16 16K workload (B=1, 32 query / 8 KV heads, D=128, S=16384, block 64,
 top-16 blocks + 512-token window), inputs resident in HBM.  The line also
 carries the attention kernel's roofline (effective FLOPs on selected blocks
 against the bf16 MFMA peak), the decode path's HBM rate on the 128K-page
-workload, the long-prefill and three-branch workloads, and the CPU oracle
-timed on a bounded sample of the headline workload.
+workload, the long-prefill and three-branch workloads, the backward of the
+headline attention, and the CPU oracle timed on a bounded sample of the
+headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|long|nsa] [--copy-calibration]
+                    [--only prefill|decode|long|nsa|backward] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -205,6 +206,32 @@ def bench_decode(torch, iters=20, n_query_sets=4):
             "page_metadata_build_ms": round(t_meta, 3)}
 
 
+def bench_backward(torch, iters=10):
+    """Gradients of the 16K prefill's attention (dq, dk, dv) for an N(0,1)
+    upstream gradient, the forward's selection held fixed.  Effective FLOPs
+    count the five products of each selected (query block, key block, head)
+    tile once: S = QK^T, dP = dO V^T, dQ, dK, dV, 2 D block^2 each."""
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import PrefillPlan
+
+    c = configs.PREFILL_16K
+    x = inputs.prefill_inputs(c, seed=0, device="cuda")
+    dout = inputs.grad_output(c, seed=0, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
+    plan.run(q, k, v)
+    plan.backward(q, k, v, dout)
+    ms = _timed(lambda: plan.backward(q, k, v, dout), iters, torch)
+    sel = int(plan.count.to(torch.int64).sum().item())
+    flops = 10.0 * c.D * c.block * c.block * c.G * sel
+    del x, q, k, v, plan, dout
+    return {"workload": f"{c.name}: gradients of the attention step (selection held fixed)",
+            "ms_per_call": round(ms, 4), "tokens_per_s": round(c.S / (ms * 1e-3), 1),
+            "effective_flops": flops,
+            "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_nsa(torch, iters=5):
     from dynamic_block_sparse_head_amd import configs, inputs
     from dynamic_block_sparse_head_amd.pipeline import NSAPlan
@@ -290,7 +317,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward"],
+                    default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -348,6 +376,8 @@ def main():
         extra["long_prefill"] = bench_long_prefill(torch)
     if args.only in (None, "nsa"):
         extra["nsa"] = bench_nsa(torch)
+    if args.only in (None, "backward"):
+        extra["backward"] = bench_backward(torch)
     line.update(extra)
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         line["cpu_baseline"] = cpu_baseline()

@@ -333,7 +333,407 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdK a, int per_xcd, int total
     }
 }
 
+// ------------------------------------------------ D = 128, blocks of 64 / 128
+// Tiles of 256-byte rows (128 bf16) are staged with direct-to-LDS loads
+// (global_load_lds_dwordx4: lane l of a wave fills bytes 16 l .. 16 l + 15 of
+// a 1 KB run, so one instruction moves four rows) into double buffers: the
+// next tile streams in while the current one is used, one barrier per tile.
+// Chunk c (16 bytes) of row r sits at byte r * 256 + ((c ^ swz(r)) << 4).
+// With swz(r) = 4 (r mod 4) + (r / 4 mod 4):
+//  * 16 lanes reading the same chunk of 16 consecutive rows (an MFMA operand
+//    row per lane) hit 16 different 16-byte bank groups;
+//  * a transposed read (ds_read_b64_tr_b16: 4 consecutive rows x 64 bytes
+//    per 32 lanes) puts the four rows in four different 64-byte groups;
+// so both ways of reading a tile are free of bank conflicts, and as the
+// swizzle is an XOR, each read costs one v_xor on a per-lane base.
+namespace f128 {
+constexpr int D = 128, ROWB = 256;
+
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Rows 0..63 of a tile (src = row 0; rows >= nvalid read row nvalid - 1,
+// which may lie before the tile when nvalid <= 0 but is always a real row)
+// into dst[0 .. 16 KB); wave `wave` of `nw` issues runs wave, wave + nw, ...
+__device__ __forceinline__ void dma_rows64(const uint16_t* src, int nvalid, uint8_t* dst, int wave,
+                                           int nw, int lane) {
+  const int cl = (lane & 15) ^ ((lane >> 4) << 2);
+  for (int k = wave; k < 16; k += nw) {
+    const int r = min(4 * k + (lane >> 4), nvalid - 1);
+    const int c = cl ^ (k & 3);
+    __builtin_amdgcn_global_load_lds(src + ptrdiff_t(r) * D + c * 8, (lds_ptr)(dst + k * 1024), 16, 0, 0);
+  }
+}
+
+// MFMA operand (8 bf16 of one row) at per-lane base `base` (row * 256 with
+// the row's swizzle and the lane half folded in) for k-step ks.
+__device__ __forceinline__ bf16x8 rd_row(const uint8_t* buf, uint32_t base, int ks) {
+  return *reinterpret_cast<const bf16x8*>(buf + (base ^ uint32_t(ks << 5)));
+}
+
+// Per-lane base of rd_row for tile row `row`.
+__device__ __forceinline__ uint32_t row_base(int row, int half) {
+  return uint32_t(row * ROWB) | uint32_t((swz(row) ^ half) << 4);
+}
+
+// Transposed operand (see tr_operand) from a swizzled tile: rows
+// r0 + ks2 * 16 + {h*4 .. h*4+3, 8 + h*4 ..}, dims dt * 32 + lane % 32.
+// lt0 / lt8 are the per-lane bases of the two row groups (tr_bases).
+__device__ __forceinline__ bf16x8 rd_tr(const uint8_t* buf, uint32_t lt0, uint32_t lt8, int ks2, int dt) {
+  const uint32_t x = uint32_t(dt << 6);
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      DSA_LDS_BF16X4(buf + ks2 * 16 * ROWB + (lt0 ^ x)));
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      DSA_LDS_BF16X4(buf + ks2 * 16 * ROWB + (lt8 ^ x)));
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void tr_bases(int r0, int lane, uint32_t& lt0, uint32_t& lt8) {
+  const int h = lane >> 5, g2 = (lane >> 4) & 1, r4 = (lane & 15) >> 2, c4 = lane & 3;
+  const int low = g2 * 2 + (c4 >> 1);
+  const int ra = r0 + h * 4 + r4, rb = ra + 8;
+  lt0 = uint32_t(ra * ROWB) | uint32_t((low ^ swz(ra)) << 4) | uint32_t((c4 & 1) << 3);
+  lt8 = uint32_t(rb * ROWB) | uint32_t((low ^ swz(rb)) << 4) | uint32_t((c4 & 1) << 3);
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+}  // namespace f128
+
+// dq, D = 128: as k_bwd_dq, with 64-key steps (two 32-key halves per wave)
+// and K/V tiles staged by direct-to-LDS loads into double buffers.
+template <int BLK>
+__global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int per_xcd, int total) {
+  using namespace f128;
+  constexpr int NW = 8, SPB = BLK / 64;   // 64-key steps per selected block
+  __shared__ __attribute__((aligned(1024))) uint8_t kv0[2 * 64 * ROWB];   // K rows, then V rows
+  __shared__ __attribute__((aligned(1024))) uint8_t kv1[2 * 64 * ROWB];
+
+  const int w = xcd_work_id(per_xcd);
+  if (w >= total) return;
+  const int sub = w % wg_per_qb;
+  const int i = (w / wg_per_qb) % a.nqb, bg = (w / wg_per_qb) / a.nqb;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int col = lane & 31, half = lane >> 5;
+  const float c = a.scale * kLog2e;
+
+  const int r = (sub * NW + wave) * 32 + col;
+  const int hh = r / BLK;
+  const int t = i * BLK + r % BLK;
+  const bool row_ok = hh < G && t < a.S;
+  const size_t row = (size_t(b) * a.Hq + g * G + (row_ok ? hh : 0)) * a.S + (row_ok ? t : 0);
+  bf16x8 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qf[ks] = ld_row8(a.q + row * D + ks * 16 + half * 8, row_ok);
+    df[ks] = ld_row8(a.dout + row * D + ks * 16 + half * 8, row_ok);
+  }
+  const float lse2 = row_ok ? a.lse[row] * kLog2e : 0.f;
+  const float dterm = row_ok ? a.dt[row] : 0.f;
+
+  floatx16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  const int32_t* irow = a.idx + (size_t(bg) * a.nqb + i) * a.idx_width;
+  const int cnt = min(a.count[size_t(bg) * a.nqb + i], a.idx_width);
+  const int nsteps = cnt * SPB;
+  const uint16_t* kg = a.k + size_t(bg) * a.S * D;
+  const uint16_t* vg = a.v + size_t(bg) * a.S * D;
+  auto key0_of = [&](int n) __attribute__((always_inline)) {
+    return irow[n / SPB] * BLK + (n % SPB) * 64;
+  };
+  auto stage = [&](int key0, uint8_t* dst) __attribute__((always_inline)) {
+    const int k0 = min(max(key0, 0), a.S - 1);   // a bad list entry reads in bounds
+    dma_rows64(kg + size_t(k0) * D, a.S - k0, dst, wave, NW, lane);
+    dma_rows64(vg + size_t(k0) * D, a.S - k0, dst + 64 * ROWB, wave, NW, lane);
+  };
+
+  auto step = [&](int key0, const uint8_t* cur) __attribute__((always_inline)) {
+#pragma unroll 1
+    for (int kh = 0; kh < 2; ++kh) {
+      const uint32_t la = row_base(kh * 32 + col, half);
+      uint32_t lt0, lt8;
+      tr_bases(kh * 32, lane, lt0, lt8);
+      floatx16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur, la, ks), qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur + 64 * ROWB, la, ks), df[ks], dp, 0, 0, 0);
+      }
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = key0 + kh * 32 + acc_row(rr, half);
+        const bool vis = row_ok && key <= t && unsigned(key) < unsigned(a.S);
+        const float p = vis ? fast_exp2(fmaf(s[rr], c, -lse2)) : 0.f;
+        dsb[rr >> 3][rr & 7] = static_cast<__bf16>(p * (dp[rr] - dterm));
+      }
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(cur, lt0, lt8, ks2, dt), dsb[ks2], acc[dt], 0, 0, 0);
+    }
+  };
+
+  if (nsteps > 0) {
+    int key_cur = key0_of(0);
+    stage(key_cur, kv0);
+    wait_dma();
+    __syncthreads();
+    for (int n = 0; n < nsteps; n += 2) {
+      // even step: tile in kv0, next into kv1
+      int key_nxt = n + 1 < nsteps ? key0_of(n + 1) : 0;
+      if (n + 1 < nsteps) stage(key_nxt, kv1);
+      step(key_cur, kv0);
+      wait_dma();
+      __syncthreads();
+      if (n + 1 >= nsteps) break;
+      // odd step: tile in kv1, next into kv0
+      key_cur = key_nxt;
+      key_nxt = n + 2 < nsteps ? key0_of(n + 2) : 0;
+      if (n + 2 < nsteps) stage(key_nxt, kv0);
+      step(key_cur, kv1);
+      wait_dma();
+      __syncthreads();
+      key_cur = key_nxt;
+    }
+  }
+
+  if (!row_ok) return;
+  uint16_t* dst = a.dq + row * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[dt][r4 * 4 + 0] * a.scale, acc[dt][r4 * 4 + 1] * a.scale);
+      pk[1] = pack_bf16x2(acc[dt][r4 * 4 + 2] * a.scale, acc[dt][r4 * 4 + 3] * a.scale);
+      *reinterpret_cast<u32x2*>(dst + dt * 32 + r4 * 8 + half * 4) = pk;
+    }
+}
+
+// dk, dv, D = 128: as k_bwd_dkdv, with 64-row steps shared by four waves
+// (wave w: keys 32 (w mod BLK/32) .. and the rows 32 r .. of each step with
+// r = w div (BLK/32) for BLK 64, both halves in turn for BLK 128); K and V
+// stay in LDS, Q and dO tiles stream through direct-to-LDS double buffers,
+// the row terms through registers of wave 0.
+template <int BLK>
+__global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int total) {
+  using namespace f128;
+  // four waves: BLK 64 -> 2 key tiles x 2 row halves; BLK 128 -> 4 key tiles,
+  // each wave taking both row halves of a step in turn
+  constexpr int NKT = BLK / 32, NW = 4, RH = NW / NKT, RTP = BLK / 64;
+  __shared__ __attribute__((aligned(1024))) uint8_t kv[2 * BLK * ROWB];   // K rows, then V rows
+  __shared__ __attribute__((aligned(1024))) uint8_t qd0[2 * 64 * ROWB];   // Q rows, then dO rows
+  __shared__ __attribute__((aligned(1024))) uint8_t qd1[2 * 64 * ROWB];
+  __shared__ __attribute__((aligned(16))) float rt0[2 * 64];             // base-2 lse, then D
+  __shared__ __attribute__((aligned(16))) float rt1[2 * 64];
+
+  const int w = xcd_work_id(per_xcd);
+  if (w >= total) return;
+  const int j = w % a.nqb, bg = w / a.nqb;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int kt = wave % NKT, rh0 = wave / NKT;
+  const int col = lane & 31, half = lane >> 5;
+  const float c = a.scale * kLog2e;
+  const int kb0 = j * BLK;
+
+  floatx16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dka[dt][e] = 0.f;
+      dva[dt][e] = 0.f;
+    }
+
+  const int key = kb0 + kt * 32 + col;          // this lane's key
+  const int32_t* inv = a.inv + (size_t(bg) * a.nqb + j) * a.nqb;
+  const int nsteps = a.inv_cnt[size_t(bg) * a.nqb + j] * G * RTP;
+
+  // tile n: query block inv[n / (G RTP)], head (n / RTP) mod G, rows 64 (n mod RTP) ..
+  struct Tile { int t0; size_t row0; };
+  auto tile_of = [&](int n) __attribute__((always_inline)) -> Tile {
+    const int i = inv[n / (G * RTP)];
+    const int h = (n / RTP) % G;
+    return Tile{i * BLK + (n % RTP) * 64, (size_t(b) * a.Hq + g * G + h) * a.S};
+  };
+  auto stage = [&](const Tile& tl, uint8_t* dst) __attribute__((always_inline)) {
+    const int nv = a.S - tl.t0;
+    dma_rows64(a.q + (tl.row0 + tl.t0) * D, nv, dst, wave, NW, lane);
+    dma_rows64(a.dout + (tl.row0 + tl.t0) * D, nv, dst + 64 * ROWB, wave, NW, lane);
+  };
+  // row terms of a tile: wave 0, one row per lane (past S: +inf / 0)
+  auto load_rt = [&](const Tile& tl, float& l2, float& dv_) __attribute__((always_inline)) {
+    const bool ok = tl.t0 + lane < a.S;
+    const size_t rr = tl.row0 + (ok ? tl.t0 + lane : 0);
+    l2 = ok ? a.lse[rr] * kLog2e : __builtin_inff();
+    dv_ = ok ? a.dt[rr] : 0.f;
+  };
+
+  const uint32_t lb = row_base(kt * 32 + col, half);       // K / V rows (B operand)
+
+  auto step = [&](int t0, const uint8_t* cur, const float* rtc) __attribute__((always_inline)) {
+#pragma unroll 1
+   for (int rh = rh0; rh < 2; rh += RH) {
+    const uint32_t la = row_base(rh * 32 + col, half);     // Q / dO rows (A operand)
+    uint32_t lt0, lt8;
+    tr_bases(rh * 32, lane, lt0, lt8);                     // Q^T / dO^T (transposed A)
+    floatx16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur, la, ks), rd_row(kv, lb, ks), s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur + 64 * ROWB, la, ks),
+                                                   rd_row(kv + BLK * ROWB, lb, ks), dp, 0, 0, 0);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int qr0 = rh * 32 + q4 * 8 + half * 4;
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(rtc + qr0);
+      const floatx4 d4 = *reinterpret_cast<const floatx4*>(rtc + 64 + qr0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = q4 * 4 + e;
+        const int tt = t0 + qr0 + e;
+        const bool vis = key <= tt && key < a.S && tt < a.S;
+        const float p = vis ? fast_exp2(fmaf(s[rr], c, -l4[e])) : 0.f;
+        pb[rr >> 3][rr & 7] = static_cast<__bf16>(p);
+        dsb[rr >> 3][rr & 7] = static_cast<__bf16>(p * (dp[rr] - d4[e]));
+      }
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(cur + 64 * ROWB, lt0, lt8, ks2, dt), pb[ks2], dva[dt], 0, 0, 0);
+        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(cur, lt0, lt8, ks2, dt), dsb[ks2], dka[dt], 0, 0, 0);
+      }
+   }
+  };
+
+  if (nsteps > 0) {
+    const int nv = a.S - kb0;
+    const uint16_t* kg = a.k + (size_t(bg) * a.S + kb0) * D;
+    const uint16_t* vg = a.v + (size_t(bg) * a.S + kb0) * D;
+#pragma unroll
+    for (int part = 0; part < RTP; ++part) {
+      dma_rows64(kg + size_t(part) * 64 * D, nv - part * 64, kv + part * 64 * ROWB, wave, NW, lane);
+      dma_rows64(vg + size_t(part) * 64 * D, nv - part * 64, kv + (BLK + part * 64) * ROWB, wave, NW, lane);
+    }
+    Tile cur = tile_of(0);
+    stage(cur, qd0);
+    if (wave == 0) {
+      float l2, d_;
+      load_rt(cur, l2, d_);
+      rt0[lane] = l2;
+      rt0[64 + lane] = d_;
+    }
+    wait_dma();
+    __syncthreads();
+    float nl2 = 0.f, nd = 0.f;
+    for (int n = 0; n < nsteps; n += 2) {
+      Tile nxt = cur;
+      if (n + 1 < nsteps) {
+        nxt = tile_of(n + 1);
+        stage(nxt, qd1);
+        if (wave == 0) load_rt(nxt, nl2, nd);
+      }
+      step(cur.t0, qd0, rt0);
+      if (n + 1 < nsteps && wave == 0) {
+        rt1[lane] = nl2;
+        rt1[64 + lane] = nd;
+      }
+      wait_dma();
+      __syncthreads();
+      if (n + 1 >= nsteps) break;
+      cur = nxt;
+      if (n + 2 < nsteps) {
+        nxt = tile_of(n + 2);
+        stage(nxt, qd0);
+        if (wave == 0) load_rt(nxt, nl2, nd);
+      }
+      step(cur.t0, qd1, rt1);
+      if (n + 2 < nsteps && wave == 0) {
+        rt0[lane] = nl2;
+        rt0[64 + lane] = nd;
+      }
+      wait_dma();
+      __syncthreads();
+      cur = nxt;
+    }
+  }
+
+  if constexpr (RH == 2) {
+    // the second row half's waves hand their sums to the first half's
+    // (the Q/dO buffers are free: the last step ended with a barrier)
+    float* xk = reinterpret_cast<float*>(qd0) + kt * 64 * 64 + lane;
+    float* xv = reinterpret_cast<float*>(qd1) + kt * 64 * 64 + lane;
+    if (rh0 == 1) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          xk[(dt * 16 + e) * 64] = dka[dt][e];
+          xv[(dt * 16 + e) * 64] = dva[dt][e];
+        }
+    }
+    __syncthreads();
+    if (rh0 == 1) return;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        dka[dt][e] += xk[(dt * 16 + e) * 64];
+        dva[dt][e] += xv[(dt * 16 + e) * 64];
+      }
+  }
+
+  if (key >= a.S) return;
+  uint16_t* dko = a.dk + (size_t(bg) * a.S + key) * D;
+  uint16_t* dvo = a.dv + (size_t(bg) * a.S + key) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x2 pk, pv;
+      pk[0] = pack_bf16x2(dka[dt][r4 * 4 + 0] * a.scale, dka[dt][r4 * 4 + 1] * a.scale);
+      pk[1] = pack_bf16x2(dka[dt][r4 * 4 + 2] * a.scale, dka[dt][r4 * 4 + 3] * a.scale);
+      pv[0] = pack_bf16x2(dva[dt][r4 * 4 + 0], dva[dt][r4 * 4 + 1]);
+      pv[1] = pack_bf16x2(dva[dt][r4 * 4 + 2], dva[dt][r4 * 4 + 3]);
+      *reinterpret_cast<u32x2*>(dko + dt * 32 + r4 * 8 + half * 4) = pk;
+      *reinterpret_cast<u32x2*>(dvo + dt * 32 + r4 * 8 + half * 4) = pv;
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+template <int BLK>
+hipError_t launch_d128(const BwdK& k, hipStream_t s) {
+  const int nbg = k.B * k.Hkv;
+  const int rows = (k.Hq / k.Hkv) * BLK;
+  const int wg_per_qb = (rows + 255) / 256;
+  const int total_q = nbg * k.nqb * wg_per_qb;
+  const int per_xcd_q = (total_q + kNumXcd - 1) / kNumXcd;
+  k_bwd_dq_d128<BLK><<<per_xcd_q * kNumXcd, 512, 0, s>>>(k, wg_per_qb, per_xcd_q, total_q);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int total_k = nbg * k.nqb;
+  const int per_xcd_k = (total_k + kNumXcd - 1) / kNumXcd;
+  k_bwd_dkdv_d128<BLK><<<per_xcd_k * kNumXcd, 256, 0, s>>>(k, per_xcd_k, total_k);
+  return hipGetLastError();
+}
 
 template <int D>
 hipError_t launch_d(const BwdK& k, hipStream_t s) {
@@ -390,6 +790,8 @@ hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t s) {
          a.lse, dt, a.idx, a.count, inv, inv_cnt,
          a.B, a.Hq, a.Hkv, a.S, a.block, a.idx_width, nqb, a.scale,
          static_cast<uint16_t*>(a.dq), static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv)};
+  if (a.D == 128 && a.block == 64) return launch_d128<64>(k, s);
+  if (a.D == 128 && a.block == 128) return launch_d128<128>(k, s);
   return a.D == 128 ? launch_d<128>(k, s) : launch_d<64>(k, s);
 }
 
