@@ -47,10 +47,13 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t* base, int pitch, in
 // Accumulator row of register r for lane half h (32x32 tile).
 __device__ __forceinline__ int acc_row(int r, int h) { return (r >> 2) * 8 + h * 4 + (r & 3); }
 
-// D_t = sum_d dO[t,d] O[t,d] over rows = B*Hq*S; D/8 lanes per row.
+// Per row (rows = B*Hq*S; D/8 lanes per row): D_t = sum_d dO[t,d] O[t,d]
+// and the forward's log-sum-exp in base 2, lse2_t = lse_t log2(e).
 __global__ __launch_bounds__(256) void k_bwd_rowterm(const uint16_t* __restrict__ out,
-                                                     const uint16_t* __restrict__ dout, int rows,
-                                                     int D, float* __restrict__ dt) {
+                                                     const uint16_t* __restrict__ dout,
+                                                     const float* __restrict__ lse, int rows,
+                                                     int D, float* __restrict__ dt,
+                                                     float* __restrict__ lse2) {
   const int lpr = D / 8;
   const int r = int((size_t(blockIdx.x) * 256 + threadIdx.x) / lpr);
   const int sub = threadIdx.x % lpr;
@@ -62,7 +65,10 @@ __global__ __launch_bounds__(256) void k_bwd_rowterm(const uint16_t* __restrict_
     for (int e = 0; e < 4; ++e) acc += bf16lo(a[e]) * bf16lo(b[e]) + bf16hi(a[e]) * bf16hi(b[e]);
   }
   for (int o = lpr / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
-  if (r < rows && sub == 0) dt[r] = acc;
+  if (r < rows && sub == 0) {
+    dt[r] = acc;
+    lse2[r] = lse[r] * kLog2e;
+  }
 }
 
 // inv[bg, j, :inv_cnt] = ascending query blocks i whose index row lists key
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(256) void k_bwd_invert(const int32_t* __restrict__ 
 // workspace pieces (row terms and inverted lists).
 struct BwdK {
   const uint16_t *q, *k, *v, *dout;
-  const float* lse;      // [B,Hq,S] natural log
+  const float* lse2;     // [B,Hq,S] forward log-sum-exp, base 2
   const float* dt;       // [B,Hq,S]
   const int32_t *idx, *count, *inv, *inv_cnt;
   int B, Hq, Hkv, S, block, idx_width, nqb;
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdK a, int wg_per_qb, int per_x
     qf[ks] = ld_row8(a.q + row * D + ks * 16 + half * 8, row_ok);
     df[ks] = ld_row8(a.dout + row * D + ks * 16 + half * 8, row_ok);
   }
-  const float lse2 = row_ok ? a.lse[row] * kLog2e : 0.f;
+  const float lse2 = row_ok ? a.lse2[row] : 0.f;
   const float dterm = row_ok ? a.dt[row] : 0.f;
 
   floatx16 acc[D / 32];
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdK a, int per_xcd, int total
     }
     for (int rr = threadIdx.x; rr < kT; rr += nt) {
       const bool ok = t0 + rr < a.S;
-      lsel[rr] = ok ? a.lse[row0 + t0 + rr] * kLog2e : __builtin_inff();
+      lsel[rr] = ok ? a.lse2[row0 + t0 + rr] : __builtin_inff();
       dtl[rr] = ok ? a.dt[row0 + t0 + rr] : 0.f;
     }
     __syncthreads();
@@ -348,6 +354,8 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdK a, int per_xcd, int total
 // swizzle is an XOR, each read costs one v_xor on a per-lane base.
 namespace f128 {
 constexpr int D = 128, ROWB = 256;
+constexpr int kDqList = 256;     // index-list entries a dq workgroup keeps in LDS
+constexpr int kDkdvList = 1024;  // inverted-list entries a dk/dv workgroup keeps in LDS
 
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
@@ -364,6 +372,20 @@ __device__ __forceinline__ void dma_rows64(const uint16_t* src, int nvalid, uint
     const int c = cl ^ (k & 3);
     __builtin_amdgcn_global_load_lds(src + ptrdiff_t(r) * D + c * 8, (lds_ptr)(dst + k * 1024), 16, 0, 0);
   }
+}
+
+// Rows 0..63 of a tile that lies wholly inside the sequence.  Wave w of nw
+// issues runs w + nw j; with nw a multiple of 4 the swizzle of every run is
+// the same per lane, so one per-lane offset (dma_lane_off) serves them all.
+__device__ __forceinline__ uint32_t dma_lane_off(int wave, int lane) {
+  const int cl = (lane & 15) ^ ((lane >> 4) << 2);
+  return uint32_t((4 * wave + (lane >> 4)) * ROWB + ((cl ^ (wave & 3)) << 4));
+}
+__device__ __forceinline__ void dma_rows64_full(const uint16_t* src, uint8_t* dst, int wave, int nw,
+                                                uint32_t lane_off) {
+  const uint8_t* s8 = reinterpret_cast<const uint8_t*>(src) + lane_off;
+  for (int k = wave, j = 0; k < 16; k += nw, ++j)
+    __builtin_amdgcn_global_load_lds(s8 + j * nw * 4 * ROWB, (lds_ptr)(dst + k * 1024), 16, 0, 0);
 }
 
 // MFMA operand (8 bf16 of one row) at per-lane base `base` (row * 256 with
@@ -397,18 +419,34 @@ __device__ __forceinline__ void tr_bases(int r0, int lane, uint32_t& lt0, uint32
   lt8 = uint32_t(rb * ROWB) | uint32_t((low ^ swz(rb)) << 4) | uint32_t((c4 & 1) << 3);
 }
 
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// Workgroup barrier for the staged loops: waits for this wave's LDS
+// operations only.  The direct-to-LDS loads are waited for explicitly
+// (wait_vm) before it, so a load still streaming into another buffer does
+// not hold the barrier, as a full fence would.  The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) (N < 16): all but this wave's last N vector-memory
+// operations have completed (they complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 }  // namespace f128
 
 // dq, D = 128: as k_bwd_dq, with 64-key steps (two 32-key halves per wave)
-// and K/V tiles staged by direct-to-LDS loads into double buffers.
+// and K/V tiles staged by direct-to-LDS loads into two buffers.
 template <int BLK>
 __global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int per_xcd, int total) {
   using namespace f128;
   constexpr int NW = 8, SPB = BLK / 64;   // 64-key steps per selected block
   __shared__ __attribute__((aligned(1024))) uint8_t kv0[2 * 64 * ROWB];   // K rows, then V rows
   __shared__ __attribute__((aligned(1024))) uint8_t kv1[2 * 64 * ROWB];
+  __shared__ int lst[kDqList];            // the selected blocks (the launcher checks they fit)
 
   const int w = xcd_work_id(per_xcd);
   if (w >= total) return;
@@ -432,8 +470,9 @@ __global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int 
     qf[ks] = ld_row8(a.q + row * D + ks * 16 + half * 8, row_ok);
     df[ks] = ld_row8(a.dout + row * D + ks * 16 + half * 8, row_ok);
   }
-  const float lse2 = row_ok ? a.lse[row] * kLog2e : 0.f;
+  const float lse2 = row_ok ? a.lse2[row] : 0.f;
   const float dterm = row_ok ? a.dt[row] : 0.f;
+  const int tlim = row_ok ? min(t, a.S - 1) : -1;   // last visible key of this row
 
   floatx16 acc[D / 32];
 #pragma unroll
@@ -446,13 +485,19 @@ __global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int 
   const int nsteps = cnt * SPB;
   const uint16_t* kg = a.k + size_t(bg) * a.S * D;
   const uint16_t* vg = a.v + size_t(bg) * a.S * D;
-  auto key0_of = [&](int n) __attribute__((always_inline)) {
-    return irow[n / SPB] * BLK + (n % SPB) * 64;
+  auto key0_of = [&](int entry, int n) __attribute__((always_inline)) {
+    return entry * BLK + (n % SPB) * 64;
   };
+  const uint32_t dma_off = dma_lane_off(wave, lane);
   auto stage = [&](int key0, uint8_t* dst) __attribute__((always_inline)) {
-    const int k0 = min(max(key0, 0), a.S - 1);   // a bad list entry reads in bounds
-    dma_rows64(kg + size_t(k0) * D, a.S - k0, dst, wave, NW, lane);
-    dma_rows64(vg + size_t(k0) * D, a.S - k0, dst + 64 * ROWB, wave, NW, lane);
+    if (key0 >= 0 && key0 + 64 <= a.S) {
+      dma_rows64_full(kg + size_t(key0) * D, dst, wave, NW, dma_off);
+      dma_rows64_full(vg + size_t(key0) * D, dst + 64 * ROWB, wave, NW, dma_off);
+    } else {
+      const int k0 = min(max(key0, 0), a.S - 1);   // a bad list entry reads in bounds
+      dma_rows64(kg + size_t(k0) * D, a.S - k0, dst, wave, NW, lane);
+      dma_rows64(vg + size_t(k0) * D, a.S - k0, dst + 64 * ROWB, wave, NW, lane);
+    }
   };
 
   auto step = [&](int key0, const uint8_t* cur) __attribute__((always_inline)) {
@@ -468,10 +513,11 @@ __global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int 
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur + 64 * ROWB, la, ks), df[ks], dp, 0, 0, 0);
       }
       bf16x8 dsb[2];
+      // key key0 + 32 kh + acc_row(rr, half) is visible iff it is <= tlim
+      const int lim = tlim - key0 - kh * 32 - half * 4;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int key = key0 + kh * 32 + acc_row(rr, half);
-        const bool vis = row_ok && key <= t && unsigned(key) < unsigned(a.S);
+        const bool vis = (rr >> 2) * 8 + (rr & 3) <= lim;
         const float p = vis ? fast_exp2(fmaf(s[rr], c, -lse2)) : 0.f;
         dsb[rr >> 3][rr & 7] = static_cast<__bf16>(p * (dp[rr] - dterm));
       }
@@ -483,27 +529,30 @@ __global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int 
     }
   };
 
+  // Two buffers: tile n + 1 streams in while tile n is used.  The list
+  // sits in LDS, so finding a tile's keys costs no memory round trip.
   if (nsteps > 0) {
-    int key_cur = key0_of(0);
-    stage(key_cur, kv0);
-    wait_dma();
+    for (int e = threadIdx.x; e < cnt; e += NW * 64) lst[e] = irow[e];
     __syncthreads();
+    auto entry = [&](int n) __attribute__((always_inline)) { return lst[n / SPB]; };
+    int k0 = key0_of(entry(0), 0), k1 = 0;
+    stage(k0, kv0);
+    wait_vm<0>();
+    __syncthreads();
+    auto phase = [&](int n, int& kc, const uint8_t* cb, int& kp, uint8_t* pb) __attribute__((always_inline)) {
+      const bool pf = n + 1 < nsteps;
+      if (pf) {
+        kp = key0_of(entry(n + 1), n + 1);
+        stage(kp, pb);
+      }
+      step(kc, cb);
+      wait_vm<0>();   // tile n + 1 has landed (each wave waits for its own loads)
+      lds_barrier();
+    };
     for (int n = 0; n < nsteps; n += 2) {
-      // even step: tile in kv0, next into kv1
-      int key_nxt = n + 1 < nsteps ? key0_of(n + 1) : 0;
-      if (n + 1 < nsteps) stage(key_nxt, kv1);
-      step(key_cur, kv0);
-      wait_dma();
-      __syncthreads();
+      phase(n, k0, kv0, k1, kv1);
       if (n + 1 >= nsteps) break;
-      // odd step: tile in kv1, next into kv0
-      key_cur = key_nxt;
-      key_nxt = n + 2 < nsteps ? key0_of(n + 2) : 0;
-      if (n + 2 < nsteps) stage(key_nxt, kv0);
-      step(key_cur, kv1);
-      wait_dma();
-      __syncthreads();
-      key_cur = key_nxt;
+      phase(n + 1, k1, kv1, k0, kv0);
     }
   }
 
@@ -523,19 +572,25 @@ __global__ __launch_bounds__(512) void k_bwd_dq_d128(BwdK a, int wg_per_qb, int 
 // dk, dv, D = 128: as k_bwd_dkdv, with 64-row steps shared by four waves
 // (wave w: keys 32 (w mod BLK/32) .. and the rows 32 r .. of each step with
 // r = w div (BLK/32) for BLK 64, both halves in turn for BLK 128); K and V
-// stay in LDS, Q and dO tiles stream through direct-to-LDS double buffers,
-// the row terms through registers of wave 0.
+// stay in LDS, Q and dO tiles stream through direct-to-LDS buffers (three
+// for BLK 64, two for BLK 128), the row terms through registers of wave 0.
 template <int BLK>
 __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int total) {
   using namespace f128;
   // four waves: BLK 64 -> 2 key tiles x 2 row halves; BLK 128 -> 4 key tiles,
   // each wave taking both row halves of a step in turn
   constexpr int NKT = BLK / 32, NW = 4, RH = NW / NKT, RTP = BLK / 64;
+  constexpr int NB = BLK == 64 ? 3 : 2;   // Q/dO buffers (LDS: 2 BLK + 64 NB rows of 512 B)
   __shared__ __attribute__((aligned(1024))) uint8_t kv[2 * BLK * ROWB];   // K rows, then V rows
-  __shared__ __attribute__((aligned(1024))) uint8_t qd0[2 * 64 * ROWB];   // Q rows, then dO rows
-  __shared__ __attribute__((aligned(1024))) uint8_t qd1[2 * 64 * ROWB];
-  __shared__ __attribute__((aligned(16))) float rt0[2 * 64];             // base-2 lse, then D
-  __shared__ __attribute__((aligned(16))) float rt1[2 * 64];
+  // a tile buffer: Q rows, dO rows, then the row terms (lse, D) of its rows
+  constexpr int QDB = 2 * 64 * ROWB + 2 * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t qd0[QDB];
+  __shared__ __attribute__((aligned(1024))) uint8_t qd1[QDB];
+  __shared__ __attribute__((aligned(1024))) uint8_t qd2[NB == 3 ? QDB : 1024];
+  float* const rt0 = reinterpret_cast<float*>(qd0 + 2 * 64 * ROWB);
+  float* const rt1 = reinterpret_cast<float*>(qd1 + 2 * 64 * ROWB);
+  float* const rt2 = reinterpret_cast<float*>(qd2 + (NB == 3 ? 2 * 64 * ROWB : 0));
+  __shared__ int lst[kDkdvList];          // the inverted list (the launcher checks it fits)
 
   const int w = xcd_work_id(per_xcd);
   if (w >= total) return;
@@ -564,40 +619,72 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int 
 
   // tile n: query block inv[n / (G RTP)], head (n / RTP) mod G, rows 64 (n mod RTP) ..
   struct Tile { int t0; size_t row0; };
-  auto tile_of = [&](int n) __attribute__((always_inline)) -> Tile {
-    const int i = inv[n / (G * RTP)];
+  auto tile_of = [&](int i, int n) __attribute__((always_inline)) -> Tile {
     const int h = (n / RTP) % G;
     return Tile{i * BLK + (n % RTP) * 64, (size_t(b) * a.Hq + g * G + h) * a.S};
   };
+  const uint32_t dma_off = dma_lane_off(wave, lane);
   auto stage = [&](const Tile& tl, uint8_t* dst) __attribute__((always_inline)) {
     const int nv = a.S - tl.t0;
-    dma_rows64(a.q + (tl.row0 + tl.t0) * D, nv, dst, wave, NW, lane);
-    dma_rows64(a.dout + (tl.row0 + tl.t0) * D, nv, dst + 64 * ROWB, wave, NW, lane);
+    if (nv >= 64) {
+      dma_rows64_full(a.q + (tl.row0 + tl.t0) * D, dst, wave, NW, dma_off);
+      dma_rows64_full(a.dout + (tl.row0 + tl.t0) * D, dst + 64 * ROWB, wave, NW, dma_off);
+    } else {
+      dma_rows64(a.q + (tl.row0 + tl.t0) * D, nv, dst, wave, NW, lane);
+      dma_rows64(a.dout + (tl.row0 + tl.t0) * D, nv, dst + 64 * ROWB, wave, NW, lane);
+    }
   };
-  // row terms of a tile: wave 0, one row per lane (past S: +inf / 0)
-  auto load_rt = [&](const Tile& tl, float& l2, float& dv_) __attribute__((always_inline)) {
-    const bool ok = tl.t0 + lane < a.S;
-    const size_t rr = tl.row0 + (ok ? tl.t0 + lane : 0);
-    l2 = ok ? a.lse[rr] * kLog2e : __builtin_inff();
-    dv_ = ok ? a.dt[rr] : 0.f;
+  // row terms of a tile (base-2 lse, then D), streamed by wave 0: one row
+  // per lane, rows past S read row S - 1 (their weights are masked)
+  auto stage_rt = [&](const Tile& tl, float* dst) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const size_t rr = tl.row0 + min(tl.t0 + lane, a.S - 1);
+      __builtin_amdgcn_global_load_lds(a.lse2 + rr, (lds_ptr)dst, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(a.dt + rr, (lds_ptr)(dst + 64), 4, 0, 0);
+    }
   };
 
   const uint32_t lb = row_base(kt * 32 + col, half);       // K / V rows (B operand)
 
+  // this wave's K and V rows (the B operands of every step), loaded once
+  bf16x8 kf[D / 16], vf[D / 16];
+
+  // One step: every LDS operand of a product is requested before the
+  // product starts, so a single wave per SIMD is not left waiting on LDS
+  // latency between the MFMAs.
   auto step = [&](int t0, const uint8_t* cur, const float* rtc) __attribute__((always_inline)) {
 #pragma unroll 1
    for (int rh = rh0; rh < 2; rh += RH) {
     const uint32_t la = row_base(rh * 32 + col, half);     // Q / dO rows (A operand)
     uint32_t lt0, lt8;
     tr_bases(rh * 32, lane, lt0, lt8);                     // Q^T / dO^T (transposed A)
+    bf16x8 qa[D / 16], da[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qa[ks] = rd_row(cur, la, ks);
+      da[ks] = rd_row(cur + 64 * ROWB, la, ks);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the requests ahead of the products
     floatx16 s = {}, dp = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur, la, ks), rd_row(kv, lb, ks), s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_row(cur + 64 * ROWB, la, ks),
-                                                   rd_row(kv + BLK * ROWB, lb, ks), dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], dp, 0, 0, 0);
     }
+    bf16x8 tq[2][D / 32], td[2][D / 32];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        td[ks2][dt] = rd_tr(cur + 64 * ROWB, lt0, lt8, ks2, dt);
+        tq[ks2][dt] = rd_tr(cur, lt0, lt8, ks2, dt);
+      }
+    __builtin_amdgcn_sched_barrier(0);   // ... and ahead of the softmax arithmetic
     bf16x8 pb[2], dsb[2];
+    // every row of this wave's half at or after every key of its tile, all
+    // inside the sequence: no masking
+    const int r_lo = t0 + rh * 32, k_hi = kb0 + kt * 32 + 31;
+    const bool full = k_hi <= r_lo && r_lo + 31 < a.S && k_hi < a.S;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int qr0 = rh * 32 + q4 * 8 + half * 4;
@@ -606,19 +693,25 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int rr = q4 * 4 + e;
-        const int tt = t0 + qr0 + e;
-        const bool vis = key <= tt && key < a.S && tt < a.S;
-        const float p = vis ? fast_exp2(fmaf(s[rr], c, -l4[e])) : 0.f;
-        pb[rr >> 3][rr & 7] = static_cast<__bf16>(p);
-        dsb[rr >> 3][rr & 7] = static_cast<__bf16>(p * (dp[rr] - d4[e]));
+        if (full) {
+          const float p = fast_exp2(fmaf(s[rr], c, -l4[e]));
+          pb[rr >> 3][rr & 7] = static_cast<__bf16>(p);
+          dsb[rr >> 3][rr & 7] = static_cast<__bf16>(p * (dp[rr] - d4[e]));
+        } else {
+          const int tt = t0 + qr0 + e;
+          const bool vis = key <= tt && key < a.S && tt < a.S;
+          const float p = vis ? fast_exp2(fmaf(s[rr], c, -l4[e])) : 0.f;
+          pb[rr >> 3][rr & 7] = static_cast<__bf16>(p);
+          dsb[rr >> 3][rr & 7] = static_cast<__bf16>(vis ? p * (dp[rr] - d4[e]) : 0.f);
+        }
       }
     }
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(cur + 64 * ROWB, lt0, lt8, ks2, dt), pb[ks2], dva[dt], 0, 0, 0);
-        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(cur, lt0, lt8, ks2, dt), dsb[ks2], dka[dt], 0, 0, 0);
+        dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(td[ks2][dt], pb[ks2], dva[dt], 0, 0, 0);
+        dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[ks2][dt], dsb[ks2], dka[dt], 0, 0, 0);
       }
    }
   };
@@ -632,46 +725,58 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int 
       dma_rows64(kg + size_t(part) * 64 * D, nv - part * 64, kv + part * 64 * ROWB, wave, NW, lane);
       dma_rows64(vg + size_t(part) * 64 * D, nv - part * 64, kv + (BLK + part * 64) * ROWB, wave, NW, lane);
     }
-    Tile cur = tile_of(0);
-    stage(cur, qd0);
-    if (wave == 0) {
-      float l2, d_;
-      load_rt(cur, l2, d_);
-      rt0[lane] = l2;
-      rt0[64 + lane] = d_;
-    }
-    wait_dma();
+    // NB buffers: tile n + NB - 1 streams in while tile n is used.  The
+    // list sits in LDS, so finding a tile's rows costs no memory round trip;
+    // the row terms stream like the rows (direct-to-LDS, one float a lane).
+    const int ninv = nsteps / (G * RTP);
+    for (int e = threadIdx.x; e < ninv; e += NW * 64) lst[e] = inv[e];
     __syncthreads();
-    float nl2 = 0.f, nd = 0.f;
-    for (int n = 0; n < nsteps; n += 2) {
-      Tile nxt = cur;
-      if (n + 1 < nsteps) {
-        nxt = tile_of(n + 1);
-        stage(nxt, qd1);
-        if (wave == 0) load_rt(nxt, nl2, nd);
+    auto entry = [&](int n) __attribute__((always_inline)) { return lst[n / (G * RTP)]; };
+    constexpr int kOps = 8;   // direct-to-LDS loads per wave and tile (16 runs each of Q, dO over 4 waves)
+    Tile T0 = tile_of(entry(0), 0), T1 = T0, T2 = T0;
+    stage_rt(T0, rt0);
+    stage(T0, qd0);
+    if (NB == 3 && nsteps > 1) {
+      T1 = tile_of(entry(1), 1);
+      stage_rt(T1, rt1);
+      stage(T1, qd1);
+    }
+    wait_vm<0>();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = rd_row(kv, lb, ks);
+      vf[ks] = rd_row(kv + BLK * ROWB, lb, ks);
+    }
+    auto phase = [&](int n, const Tile& tc, const uint8_t* cb, const float* cr, Tile& tp, uint8_t* pb,
+                     float* pr) __attribute__((always_inline)) {
+      const int m = n + NB - 1;
+      const bool pf = m < nsteps;
+      if (pf) {
+        tp = tile_of(entry(m), m);
+        stage_rt(tp, pr);
+        stage(tp, pb);
       }
-      step(cur.t0, qd0, rt0);
-      if (n + 1 < nsteps && wave == 0) {
-        rt1[lane] = nl2;
-        rt1[64 + lane] = nd;
+      step(tc.t0, cb, cr);
+      // tile n + 1 has landed (each wave waits for its own loads); with three
+      // buffers the eight row loads of tile n + 2, issued last, may still be
+      // in flight
+      if (NB == 3 && pf) wait_vm<kOps>();
+      else wait_vm<0>();
+      lds_barrier();
+    };
+    for (int n = 0; n < nsteps; n += NB) {
+      if constexpr (NB == 3) {
+        phase(n, T0, qd0, rt0, T2, qd2, rt2);
+        if (n + 1 >= nsteps) break;
+        phase(n + 1, T1, qd1, rt1, T0, qd0, rt0);
+        if (n + 2 >= nsteps) break;
+        phase(n + 2, T2, qd2, rt2, T1, qd1, rt1);
+      } else {
+        phase(n, T0, qd0, rt0, T1, qd1, rt1);
+        if (n + 1 >= nsteps) break;
+        phase(n + 1, T1, qd1, rt1, T0, qd0, rt0);
       }
-      wait_dma();
-      __syncthreads();
-      if (n + 1 >= nsteps) break;
-      cur = nxt;
-      if (n + 2 < nsteps) {
-        nxt = tile_of(n + 2);
-        stage(nxt, qd0);
-        if (wave == 0) load_rt(nxt, nl2, nd);
-      }
-      step(cur.t0, qd1, rt1);
-      if (n + 2 < nsteps && wave == 0) {
-        rt0[lane] = nl2;
-        rt0[64 + lane] = nd;
-      }
-      wait_dma();
-      __syncthreads();
-      cur = nxt;
     }
   }
 
@@ -759,7 +864,7 @@ hipError_t launch_d(const BwdK& k, hipStream_t s) {
 
 size_t attn_backward_workspace_bytes(int B, int Hq, int Hkv, int S, int block) {
   const size_t nb = (size_t(S) + block - 1) / block;
-  return align256(size_t(B) * Hq * S * sizeof(float)) +
+  return 2 * align256(size_t(B) * Hq * S * sizeof(float)) +
          align256(size_t(B) * Hkv * nb * nb * sizeof(int32_t)) +
          align256(size_t(B) * Hkv * nb * sizeof(int32_t));
 }
@@ -769,6 +874,8 @@ hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t s) {
   char* ws = static_cast<char*>(a.workspace);
   float* dt = reinterpret_cast<float*>(ws);
   ws += align256(size_t(a.B) * a.Hq * a.S * sizeof(float));
+  float* lse2 = reinterpret_cast<float*>(ws);
+  ws += align256(size_t(a.B) * a.Hq * a.S * sizeof(float));
   int32_t* inv = reinterpret_cast<int32_t*>(ws);
   ws += align256(size_t(a.B) * a.Hkv * nqb * nqb * sizeof(int32_t));
   int32_t* inv_cnt = reinterpret_cast<int32_t*>(ws);
@@ -776,7 +883,8 @@ hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t s) {
   const int rows = a.B * a.Hq * a.S;
   const int lpr = a.D / 8;
   k_bwd_rowterm<<<int((size_t(rows) * lpr + 255) / 256), 256, 0, s>>>(
-      static_cast<const uint16_t*>(a.out), static_cast<const uint16_t*>(a.dout), rows, a.D, dt);
+      static_cast<const uint16_t*>(a.out), static_cast<const uint16_t*>(a.dout), a.lse, rows, a.D, dt,
+      lse2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nbg = a.B * a.Hkv;
@@ -787,11 +895,15 @@ hipError_t launch_attn_backward(const AttnBwdArgs& a, hipStream_t s) {
 
   BwdK k{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
          static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout),
-         a.lse, dt, a.idx, a.count, inv, inv_cnt,
+         lse2, dt, a.idx, a.count, inv, inv_cnt,
          a.B, a.Hq, a.Hkv, a.S, a.block, a.idx_width, nqb, a.scale,
          static_cast<uint16_t*>(a.dq), static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv)};
-  if (a.D == 128 && a.block == 64) return launch_d128<64>(k, s);
-  if (a.D == 128 && a.block == 128) return launch_d128<128>(k, s);
+  // the staged kernels keep the index lists in LDS and read row terms of a
+  // 64-row tile by clamping to row S - 1
+  const bool staged = a.D == 128 && a.idx_width <= f128::kDqList && nqb <= f128::kDkdvList &&
+                      a.S >= 64;
+  if (staged && a.block == 64) return launch_d128<64>(k, s);
+  if (staged && a.block == 128) return launch_d128<128>(k, s);
   return a.D == 128 ? launch_d<128>(k, s) : launch_d<64>(k, s);
 }
 

@@ -115,7 +115,7 @@ def test_backward_validation():
     lib = L.load()
     ws = lib.dsa_sparse_attn_prefill_backward_workspace_size(1, 32, 8, 16384, 128, 64)
     nb = 256
-    assert ws == 32 * 16384 * 4 + 8 * nb * nb * 4 + 8 * nb * 4
+    assert ws == 2 * 32 * 16384 * 4 + 8 * nb * nb * 4 + 8 * nb * 4
     f = lib.dsa_sparse_attn_prefill_backward
     ok = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, dout=FAKE, B=1, Hq=32, Hkv=8,
               S=16384, D=128, idx=FAKE, count=FAKE, width=24, block=64, scale=0.1, ws=FAKE,
