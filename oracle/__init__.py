@@ -16,10 +16,15 @@ Page key used in citations:
 
 Pinning status (the tests under tests/ that check each function against
 something other than itself):
-  prefill.pool_blocks, prefill.block_scores_pooled   — bilinearity, needles
+  prefill.pool_blocks, prefill.block_scores_pooled   — bilinearity, needles; per-head units
+                                                       (sel_heads = 1): pairwise means, heads
+                                                       summing to the group score
   prefill.select_blocks                              — brute-force subsets, counts
   prefill.sparse_attention                           — dense causal SDPA, block-diagonal limit,
-                                                       softmax invariants, hand worked example
+                                                       softmax invariants, hand worked example;
+                                                       per-head lists: explicit per-head dense
+                                                       masks from a brute-force top-k, identical
+                                                       heads reproducing the group selection
   decode.page_minmax, decode.page_scores             — bound >= true max, equality cases
   decode.decode_attention                            — dense single-query limit
   nsa.compress                                       — stride = len = 1 identity, hand example

@@ -9,7 +9,10 @@ and [SF] §二 (unit of sparsification = blocks, dynamic content-aware
 importance, uniform budget) fix the block granularity.  Readings taken where
 the pages are silent:
   * selection unit under grouped-query attention: the KV head; the group's
-    block score is the sum of its query heads' scores;
+    block score is the sum of its query heads' scores (`sel_heads`, the
+    number of query heads sharing one selection, defaults to the group size;
+    sel_heads = 1 is the per-query-head variant: every head ranks blocks by
+    its own score and keeps its own list);
   * block score: mean-pooled query block · mean-pooled key block, no 1/sqrt(D);
   * the local window is the n_local most recent key blocks (diagonal
     included); top-k is drawn from the blocks before the window;
@@ -38,27 +41,40 @@ def pool_blocks(x: np.ndarray, block: int) -> np.ndarray:
     return out
 
 
-def block_scores_pooled(q: np.ndarray, k: np.ndarray, block: int) -> np.ndarray:
-    """Group block scores s[b, g, i, j] for key block j against query block i.
+def _units(Hq: int, Hkv: int, sel_heads):
+    """(heads per selection unit, number of units per sequence)."""
+    G = Hq // Hkv
+    u = G if sel_heads is None else int(sel_heads)
+    if u < 1 or G % u:
+        raise ValueError(f"sel_heads {u} must divide the group size {G}")
+    return u, Hq // u
 
-    s = sum over the query heads h of KV group g of qbar[b,h,i] · kbar[b,g,j],
-    defined for j <= i (causal, [DMA] §五: causal mask before top-k);
-    entries j > i are -inf.  q [B,Hq,S,D], k [B,Hkv,S,D].
+
+def block_scores_pooled(q: np.ndarray, k: np.ndarray, block: int, sel_heads=None) -> np.ndarray:
+    """Block scores s[b, u, i, j] for key block j against query block i, per
+    selection unit u (sel_heads consecutive query heads; default: the KV group).
+
+    s = sum over the query heads h of unit u of qbar[b,h,i] · kbar[b,g,j],
+    with g the KV head of those query heads; defined for j <= i (causal,
+    [DMA] §五: causal mask before top-k); entries j > i are -inf.
+    q [B,Hq,S,D], k [B,Hkv,S,D] -> [B, Hq/sel_heads, nb, nb].
     """
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
+    uh, U = _units(Hq, Hkv, sel_heads)
     qbar = pool_blocks(q, block)
     kbar = pool_blocks(k, block)
     n = qbar.shape[-2]
-    s = np.full((B, Hkv, n, n), -np.inf)
+    s = np.full((B, U, n, n), -np.inf)
     for b in range(B):
-        for g in range(Hkv):
+        for u in range(U):
+            g = (u * uh) // G
             for i in range(n):
                 acc = np.zeros(i + 1)
-                for h in range(g * G, (g + 1) * G):
+                for h in range(u * uh, (u + 1) * uh):
                     acc += kbar[b, g, :i + 1, :] @ qbar[b, h, i, :]
-                s[b, g, i, :i + 1] = acc
+                s[b, u, i, :i + 1] = acc
     return s
 
 
@@ -138,15 +154,16 @@ def masked_softmax_attention(q_rows, t_rows, keys, k, v, scale):
     return out, lse
 
 
-def sparse_attention(q, k, v, idx, count, block, scale, q_blocks=None):
+def sparse_attention(q, k, v, idx, count, block, scale, q_blocks=None, sel_heads=None):
     """Block-sparse causal attention over the selected key blocks.
 
-    q [B,Hq,S,D], k/v [B,Hkv,S,D]; idx [B,Hkv,nB,W] (ascending, -1 padded),
-    count [B,Hkv,nB].  Every query head of group g uses the group's index
-    rows.  Row t of query block i attends to keys s <= t lying in the
-    selected blocks of row i.  q_blocks: optional list of query blocks to
-    evaluate (others are left as NaN), for sampled checks at full size.
-    Returns out [B,Hq,S,D], lse [B,Hq,S] (float64).
+    q [B,Hq,S,D], k/v [B,Hkv,S,D]; idx [B,U,nB,W] (ascending, -1 padded),
+    count [B,U,nB] with U = Hq / sel_heads selection units (default: one per
+    KV group).  Query head h uses the index rows of unit h // sel_heads and
+    the K/V of its group.  Row t of query block i attends to keys s <= t
+    lying in the selected blocks of row i.  q_blocks: optional list of query
+    blocks to evaluate (others are left as NaN), for sampled checks at full
+    size.  Returns out [B,Hq,S,D], lse [B,Hq,S] (float64).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -154,6 +171,7 @@ def sparse_attention(q, k, v, idx, count, block, scale, q_blocks=None):
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
+    uh, _ = _units(Hq, Hkv, sel_heads)
     n = -(-S // block)
     blocks = range(n) if q_blocks is None else q_blocks
     out = np.full((B, Hq, S, v.shape[-1]), np.nan)   # value width may differ from D
@@ -161,18 +179,19 @@ def sparse_attention(q, k, v, idx, count, block, scale, q_blocks=None):
     for b in range(B):
         for h in range(Hq):
             g = h // G
+            u = h // uh
             for i in blocks:
                 t = np.arange(i * block, min((i + 1) * block, S))
-                keys = visible_keys(idx[b, g, i], int(count[b, g, i]), block, S)
+                keys = visible_keys(idx[b, u, i], int(count[b, u, i]), block, S)
                 o, l = masked_softmax_attention(q[b, h, t], t, keys, k[b, g], v[b, g], scale)
                 out[b, h, t] = o
                 lse[b, h, t] = l
     return out, lse
 
 
-def prefill(q, k, v, block, topk, n_local, scale):
+def prefill(q, k, v, block, topk, n_local, scale, sel_heads=None):
     """The whole prefill path: pooled scores -> selection -> attention."""
-    s = block_scores_pooled(q, k, block)
+    s = block_scores_pooled(q, k, block, sel_heads)
     idx, cnt = select_blocks(s, topk, n_local, causal=True)
-    out, lse = sparse_attention(q, k, v, idx, cnt, block, scale)
+    out, lse = sparse_attention(q, k, v, idx, cnt, block, scale, sel_heads=sel_heads)
     return {"scores": s, "idx": idx, "count": cnt, "out": out, "lse": lse}

@@ -281,3 +281,81 @@ def test_worked_example_numbers_match_their_closed_forms():
         ex = json.load(f)
     for expr, row in zip(ex["out_expr"], ex["out"]):
         assert abs(eval(expr, {"e": math.e}) - row[0]) < 1e-15 and row[1] == 1.0
+
+
+# --------------------------------------- per-query-head selection (sel_heads)
+def test_per_head_scores_are_pairwise_means_and_sum_to_group_score():
+    """sel_heads = 1: each head's score is the mean of its own q·k pairs of
+    the two blocks; summing the heads of a group gives the group score."""
+    c, q, k, _ = _small_inputs(configs.PREFILL_16K, 256)
+    sh = P.block_scores_pooled(q, k, c.block, sel_heads=1)
+    assert sh.shape == (1, c.Hq, c.n_blocks, c.n_blocks)
+    B = c.block
+    for h in (0, 5, c.Hq - 1):
+        g = h // c.G
+        for i in range(c.n_blocks):
+            for j in range(i + 1):
+                qa = q[0, h, i * B:(i + 1) * B]
+                ka = k[0, g, j * B:(j + 1) * B]
+                assert abs(sh[0, h, i, j] - (qa @ ka.T).sum() / (B * B)) < 1e-14
+    sg = P.block_scores_pooled(q, k, c.block)
+    fin = np.isfinite(sg)
+    summed = sh.reshape(1, c.Hkv, c.G, c.n_blocks, c.n_blocks).sum(axis=2)
+    assert np.max(np.abs(summed[fin] - sg[fin])) < 1e-14
+    two = P.block_scores_pooled(q, k, c.block, sel_heads=2)    # pairs of heads
+    assert np.max(np.abs(two[np.isfinite(two)] -
+                         sh.reshape(1, c.Hq // 2, 2, c.n_blocks, c.n_blocks).sum(axis=2)[np.isfinite(two)])) < 1e-14
+
+
+def test_per_head_selection_attention_equals_masked_dense():
+    """sel_heads = 1 under GQA: each query head attends over its own chosen
+    blocks — the same as dense softmax with that head's explicit -inf mask,
+    built here from a brute-force top-k over the head's own scores."""
+    c, q, k, v = _small_inputs(configs.PREFILL_16K, 384, seed=4)
+    topk, n_local = 2, 1
+    res = P.prefill(q, k, v, c.block, topk, n_local, c.scale, sel_heads=1)
+    S, nb = c.S, c.n_blocks
+    differs = False
+    for h in range(c.Hq):
+        g = h // c.G
+        allowed = np.zeros((S, S), bool)
+        for i in range(nb):
+            cands = list(range(0, i - n_local + 1))
+            sc = [float((q[0, h, i * c.block:(i + 1) * c.block].mean(0)) @
+                        (k[0, g, j * c.block:(j + 1) * c.block].mean(0))) for j in cands]
+            best = set()
+            if cands:
+                best = set(max(itertools.combinations(range(len(cands)), min(topk, len(cands))),
+                               key=lambda cmb: (sum(sc[x] for x in cmb), [-x for x in cmb])))
+                best = {cands[x] for x in best}
+            chosen = sorted(best | set(range(max(0, i - n_local + 1), i + 1)))
+            assert list(res["idx"][0, h, i, :res["count"][0, h, i]]) == chosen
+            for j in chosen:
+                allowed[i * c.block:(i + 1) * c.block, j * c.block:(j + 1) * c.block] = True
+        allowed &= np.tril(np.ones((S, S), bool))
+        logits = (q[0, h] @ k[0, g].T) * c.scale
+        logits[~allowed] = -np.inf
+        p = np.exp(logits - logits.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        assert np.max(np.abs(p @ v[0, g] - res["out"][0, h])) < 1e-12
+        if h % c.G and not np.array_equal(res["idx"][0, h], res["idx"][0, h - 1]):
+            differs = True
+    assert differs      # the heads of a group really chose differently somewhere
+
+
+def test_per_head_selection_of_identical_heads_is_the_group_selection():
+    """Heads of a group that are identical rank blocks identically, so the
+    per-head lists and outputs equal the per-group ones."""
+    c, q, k, v = _small_inputs(configs.PREFILL_16K, 512)
+    qrep = np.repeat(q[:, ::c.G], c.G, axis=1)
+    grp = P.prefill(qrep, k, v, c.block, c.topk, c.n_local, c.scale)
+    per = P.prefill(qrep, k, v, c.block, c.topk, c.n_local, c.scale, sel_heads=1)
+    for h in range(c.Hq):
+        assert np.array_equal(per["idx"][0, h], grp["idx"][0, h // c.G])
+    assert np.max(np.abs(per["out"] - grp["out"])) == 0.0
+
+
+def test_per_head_all_blocks_equals_dense_causal():
+    c, q, k, v = _small_inputs(configs.PREFILL_16K, 320)
+    res = P.prefill(q, k, v, c.block, topk=c.n_blocks, n_local=1, scale=c.scale, sel_heads=1)
+    assert np.max(np.abs(res["out"] - _sdpa_causal(q, k, v, c.scale))) < 1e-12
