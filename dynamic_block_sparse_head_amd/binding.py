@@ -18,7 +18,7 @@ LIB_PATH = os.environ.get("DSA_LIBRARY", os.path.join(_HERE, "libdsa.so"))
 
 DSA_OK, DSA_E_ARG, DSA_E_UNSUPPORTED, DSA_E_WORKSPACE, DSA_E_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16 = 0, 1
-DSA_SCORE_POOLED, DSA_SCORE_PAGE_BOUND = 0, 1
+DSA_SCORE_POOLED, DSA_SCORE_PAGE_BOUND, DSA_SCORE_POOLED_HEAD = 0, 1, 2
 
 _c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
@@ -37,6 +37,8 @@ SIGNATURES = {
     "dsa_sparse_attn_prefill_backward": (_c_int, [_c_int] + [_vp] * 4 + [_vp, _vp]
                                          + [_c_int] * 5 + [_vp, _vp] + [_c_int] * 2
                                          + [_c_float, _vp, _c_size, _vp, _vp, _vp, _vp]),
+    "dsa_sparse_attn_prefill_sel": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                                    + [_c_int] * 3 + [_c_float, _vp, _vp, _vp]),
     "dsa_page_minmax": (_c_int, [_c_int, _vp] + [_c_int] * 5 + [_vp, _vp, _vp]),
     "dsa_sparse_attn_decode_workspace_size": (_c_size, [_c_int] * 6),
     "dsa_sparse_attn_decode": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
@@ -118,8 +120,9 @@ def dsa_block_scores_workspace_size(kind, B, Hq, Hkv, n, D, block) -> int:
 
 def dsa_block_scores(kind, q, k_or_kmin, kmax, block, workspace, scores, stream=None):
     """POOLED: q [B,Hq,S,D], k [B,Hkv,S,D] -> scores [B,Hkv,nb,nb].
+    POOLED_HEAD: the same inputs -> scores [B,Hq,nb,nb] (one per query head).
     PAGE_BOUND: q [B,Hq,D], kmin/kmax [B,Hkv,nP,D] -> scores [B,Hkv,nP]."""
-    if kind == DSA_SCORE_POOLED:
+    if kind in (DSA_SCORE_POOLED, DSA_SCORE_POOLED_HEAD):
         B, Hq, n, D = q.shape
         Hkv = k_or_kmin.shape[1]
     else:
@@ -170,6 +173,18 @@ def dsa_sparse_attn_prefill_backward(q, k, v, out, lse, dout, idx, count, block,
         workspace.numel() * workspace.element_size(), _ptr(dq, "dq", q.dtype),
         _ptr(dk, "dk", q.dtype), _ptr(dv, "dv", q.dtype), _stream(stream))
     _check(st, "dsa_sparse_attn_prefill_backward")
+
+
+def dsa_sparse_attn_prefill_sel(q, k, v, idx, count, block, sel_heads, scale, out, lse=None,
+                                stream=None):
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    st = load().dsa_sparse_attn_prefill_sel(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S, D,
+        _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), idx.shape[-1], block,
+        sel_heads, float(scale), _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32),
+        _stream(stream))
+    _check(st, "dsa_sparse_attn_prefill_sel")
 
 
 def dsa_page_minmax(k, page, kmin, kmax, stream=None):

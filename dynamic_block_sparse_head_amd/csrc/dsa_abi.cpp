@@ -99,10 +99,12 @@ const char* dsa_status_string(int status) {
 const char* dsa_last_error(void) { return g_err.c_str(); }
 
 size_t dsa_block_scores_workspace_size(int kind, int B, int Hq, int Hkv, int n, int D, int block) {
-  (void)Hq;
-  if (kind != DSA_SCORE_POOLED || B <= 0 || Hkv <= 0 || n <= 0 || D <= 0 || block <= 0) return 0;
+  if ((kind != DSA_SCORE_POOLED && kind != DSA_SCORE_POOLED_HEAD) || B <= 0 || Hq <= 0 || Hkv <= 0 ||
+      n <= 0 || D <= 0 || block <= 0)
+    return 0;
   const size_t nb = (size_t(n) + block - 1) / block;
-  return size_t(2) * B * Hkv * nb * D * sizeof(double);
+  const size_t units = kind == DSA_SCORE_POOLED ? size_t(Hkv) : size_t(Hq);
+  return (units + Hkv) * B * nb * D * sizeof(double);
 }
 
 int dsa_block_scores(int kind, int dtype, const void* q, const void* k_or_kmin, const void* kmax,
@@ -117,18 +119,20 @@ int dsa_block_scores(int kind, int dtype, const void* q, const void* k_or_kmin, 
   REQUIRE_PTR(k_or_kmin);
   REQUIRE_PTR(scores);
   auto s = static_cast<hipStream_t>(stream);
-  if (kind == DSA_SCORE_POOLED) {
+  if (kind == DSA_SCORE_POOLED || kind == DSA_SCORE_POOLED_HEAD) {
     TRY(check_block(block, "block"));
-    REQUIRE(kmax == nullptr, DSA_E_ARG, "kmax must be NULL for DSA_SCORE_POOLED");
+    REQUIRE(kmax == nullptr, DSA_E_ARG, "kmax must be NULL for pooled scores");
     REQUIRE(rows_fit(B, Hq, n), DSA_E_ARG, "B*Hq*n too large");
     const size_t need = dsa_block_scores_workspace_size(kind, B, Hq, Hkv, n, D, block);
     REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
             "pooled scores need a workspace of %zu bytes (got %zu)", need, workspace_bytes);
     REQUIRE_PTR(workspace);
     const int nb = (n + block - 1) / block;
-    dsa::PoolScoreArgs a{dtype, q, k_or_kmin, B, Hq, Hkv, n, D, block,
+    const int sel_heads = kind == DSA_SCORE_POOLED ? Hq / Hkv : 1;
+    dsa::PoolScoreArgs a{dtype, q, k_or_kmin, B, Hq, Hkv, n, D, block, sel_heads,
                          static_cast<double*>(workspace),
-                         static_cast<double*>(workspace) + size_t(B) * Hkv * nb * D, scores};
+                         static_cast<double*>(workspace) + size_t(B) * (Hq / sel_heads) * nb * D,
+                         scores};
     return hip_status(dsa::launch_pooled_scores(a, s), "dsa_block_scores");
   }
   if (kind == DSA_SCORE_PAGE_BOUND) {
@@ -159,11 +163,10 @@ int dsa_topk_select(const float* scores, int rows, int n_q, int n_k, int k, int 
                     "dsa_topk_select");
 }
 
-int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
-                            int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
-                            int idx_width, int block, int window, float scale, void* out,
-                            float* lse, void* stream) {
-  g_err.clear();
+static int prefill_impl(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                        int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
+                        int idx_width, int block, int window, int sel_heads, float scale,
+                        void* out, float* lse, void* stream) {
   TRY(check_dtype(dtype, true));
   TRY(check_heads(B, Hq, Hkv));
   TRY(check_dim(D));
@@ -204,9 +207,33 @@ int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void*
   a.window = window;
   a.cmp_len = 1;
   a.cmp_stride = 1;
+  a.sel_heads = sel_heads;
   a.scale = scale;
   return hip_status(dsa::launch_attention(a, static_cast<hipStream_t>(stream)),
                     "dsa_sparse_attn_prefill");
+}
+
+int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                            int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
+                            int idx_width, int block, int window, float scale, void* out,
+                            float* lse, void* stream) {
+  g_err.clear();
+  TRY(check_heads(B, Hq, Hkv));
+  return prefill_impl(dtype, q, k, v, B, Hq, Hkv, S, D, idx, count, idx_width, block, window,
+                      Hq / Hkv, scale, out, lse, stream);
+}
+
+int dsa_sparse_attn_prefill_sel(int dtype, const void* q, const void* k, const void* v, int B,
+                                int Hq, int Hkv, int S, int D, const int32_t* idx,
+                                const int32_t* count, int idx_width, int block, int sel_heads,
+                                float scale, void* out, float* lse, void* stream) {
+  g_err.clear();
+  TRY(check_heads(B, Hq, Hkv));
+  REQUIRE(sel_heads >= 1 && (Hq / Hkv) % sel_heads == 0, DSA_E_ARG,
+          "sel_heads (%d) must divide Hq/Hkv (%d)", sel_heads, Hq / Hkv);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  return prefill_impl(dtype, q, k, v, B, Hq, Hkv, S, D, idx, count, idx_width, block, 0, sel_heads,
+                      scale, out, lse, stream);
 }
 
 size_t dsa_sparse_attn_prefill_backward_workspace_size(int B, int Hq, int Hkv, int S, int D,
@@ -368,6 +395,7 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, i
   a.mode = dsa::MODE_CMP;
   a.cmp_len = len;
   a.cmp_stride = stride;
+  a.sel_heads = Hq / Hkv;
   a.scale = scale;
   int st = hip_status(dsa::launch_attention(a, s), "dsa_nsa_cmp_attn");
   if (st != DSA_OK || block_scores == nullptr) return st;

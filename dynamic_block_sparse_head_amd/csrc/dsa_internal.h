@@ -18,9 +18,10 @@ struct PoolScoreArgs {
   const void* q;     // [B,Hq,S,D]
   const void* k;     // [B,Hkv,S,D]
   int B, Hq, Hkv, S, D, block;
-  double* ws_q;      // [B*Hkv, nb, D]  group-summed pooled queries
+  int sel_heads;     // query heads per selection unit (Hq/Hkv: per KV group; 1: per query head)
+  double* ws_q;      // [B*Hq/sel_heads, nb, D]  unit-summed pooled queries
   double* ws_k;      // [B*Hkv, nb, D]  pooled keys
-  float* scores;     // [B,Hkv,nb,nb]
+  float* scores;     // [B,Hq/sel_heads,nb,nb]
 };
 hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s);
 
@@ -57,6 +58,7 @@ struct AttnArgs {
   int mode;
   int window;           // window mode: tokens
   int cmp_len, cmp_stride;  // compressed mode: summary c ends at c*stride+len-1
+  int sel_heads;        // query heads sharing one index row (Hq/Hkv unless per-head lists)
   float scale;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);

@@ -134,8 +134,11 @@ __device__ __forceinline__ float half_sum(float x) {
 // same softmax: numerator and denominator share the reference maximum.
 constexpr float kLazyRescale = 8.0f;
 
+// (two-wave instances stage a tile in more registers per lane and run one
+// wave per SIMD)
 template <int D, int KT, int QT, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(NW >= 4 ? DSA_ATTN_WAVES_PER_EU : 1)))
 void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
                                                        int per_xcd, int total) {
   constexpr int NT = NW * 64;
@@ -156,9 +159,12 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
   const int sub = w % wg_per_qb;
   const int rest = w / wg_per_qb;
   const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
-  const int bg = rest / nqb;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int G = a.Hq / a.Hkv;
+  // (sequence, selection unit): SH query heads sharing one index list and
+  // their KV head (SH = G unless the caller selects per query head)
+  const int SH = a.sel_heads, U = a.Hq / SH;
+  const int bu = rest / nqb;
+  const int b = bu / U, u = bu % U;
+  const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
   const int t0 = i * a.block;
   const int t1 = min(a.S, t0 + a.block) - 1;
 
@@ -180,8 +186,8 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
     const int r = sub * ROWS + wave * 32 * QT + qt * 32 + col;
     const int hh = r / a.block;
     row_t[qt] = t0 + r % a.block;
-    row_h[qt] = g * G + hh;
-    row_ok[qt] = hh < G && row_t[qt] < a.S;
+    row_h[qt] = u * SH + hh;
+    row_ok[qt] = hh < SH && row_t[qt] < a.S;
     const uint16_t* src = qp + ((size_t(b) * a.Hq + row_h[qt]) * a.S + row_t[qt]) * D + half * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -216,7 +222,7 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
   row_range(a, t0, dummy, blk_hi);
 
   TileSpec ts;
-  const int ntiles = make_tiles(a, bg, i, t0, t1, KT, ts);
+  const int ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
   const float c = a.scale * kLog2e;
 
   // K: one 16-byte chunk per (key, 8 dims).  V: four keys x 8 dims per
@@ -455,9 +461,12 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   const int sub = w % wg_per_qb;
   const int rest = w / wg_per_qb;
   const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
-  const int bg = rest / nqb;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int G = a.Hq / a.Hkv;
+  // (sequence, selection unit): SH query heads sharing one index list and
+  // their KV head (SH = G unless the caller selects per query head)
+  const int SH = a.sel_heads, U = a.Hq / SH;
+  const int bu = rest / nqb;
+  const int b = bu / U, u = bu % U;
+  const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
   const int t0 = i * a.block;
   const int t1 = min(a.S, t0 + a.block) - 1;
 
@@ -473,15 +482,15 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   const int r = sub * ROWS + wave * 32 + col;
   const int hh = r / a.block;
   const int row_t = t0 + r % a.block;
-  const bool row_ok = hh < G && row_t < a.S;
-  const int row_h = g * G + (row_ok ? hh : 0);
+  const bool row_ok = hh < SH && row_t < a.S;
+  const int row_h = u * SH + (row_ok ? hh : 0);
   bf16x8 qf[D / 16];
   {
-    // one descriptor over the group's query heads; rows that are not ours
+    // one descriptor over the unit's query heads; rows that are not ours
     // get an offset past its end and read zeros
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
-        static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(g) * G) * a.S * D,
-        uint32_t(G) * a.S * D * 2);
+        static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(u) * SH) * a.S * D,
+        uint32_t(SH) * a.S * D * 2);
     const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + half * 8) * 2) : 0x80000000u;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
@@ -503,7 +512,7 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   row_range(a, t0, dummy, blk_hi);
 
   TileSpec ts;
-  const int ntiles = make_tiles(a, bg, i, t0, t1, KT, ts);
+  const int ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
   const float c = a.scale * kLog2e;
   // First key of every tile, held across lanes (tile n in lane n % 64 of
   // word n / 64) and read back with v_readlane: no memory access and no wait
@@ -716,6 +725,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
   __shared__ float v_lds[KT][D];
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv, g = h / G, bg = b * a.Hkv + g;
+  const int bu = b * (a.Hq / a.sel_heads) + h / a.sel_heads;   // index rows of h's selection unit
   const int t0 = i * a.block;
   const int t1 = min(a.S, t0 + a.block) - 1;
   const int t = t0 + threadIdx.x;
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
   float m = -__builtin_inff(), l = 0.f;
 
   TileSpec ts;
-  const int ntiles = make_tiles(a, bg, i, t0, t1, KT, ts);
+  const int ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
   for (int n = 0; n < ntiles; ++n) {
     const int key0 = tile_key0(ts, n);
     __syncthreads();
@@ -783,9 +793,8 @@ template <int D, int KT, int QT, int NW>
 hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
   constexpr int ROWS = NW * 32 * QT;
   const int nqb = (a.S + a.block - 1) / a.block;
-  const int G = a.Hq / a.Hkv;
-  const int wg_per_qb = (G * a.block + ROWS - 1) / ROWS;
-  const int total = a.B * a.Hkv * nqb * wg_per_qb;
+  const int wg_per_qb = (a.sel_heads * a.block + ROWS - 1) / ROWS;
+  const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
   const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
   k_attn_bf16<D, KT, QT, NW><<<per_xcd * kNumXcd, NW * 64, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
   return hipGetLastError();
@@ -808,12 +817,22 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.D == 128 && a.mode == MODE_INDEX && a.block % 128 == 0)
     return run_bf16<128, 128, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
 #endif
+  // a selection unit with fewer rows than an eight-wave workgroup (per-head
+  // selection) runs the generic kernel with as many waves as it has rows
+  const int unit_rows = a.sel_heads * a.block;
+  if (unit_rows < 256) {
+    const int nw = unit_rows <= 64 ? 2 : 4;
+    if (a.D == 128)
+      return kt32 ? (nw == 2 ? run_bf16<128, 32, 1, 2>(a, s) : run_bf16<128, 32, 1, 4>(a, s))
+                  : (nw == 2 ? run_bf16<128, 64, 1, 2>(a, s) : run_bf16<128, 64, 1, 4>(a, s));
+    return kt32 ? (nw == 2 ? run_bf16<64, 32, 1, 2>(a, s) : run_bf16<64, 32, 1, 4>(a, s))
+                : (nw == 2 ? run_bf16<64, 64, 1, 2>(a, s) : run_bf16<64, 64, 1, 4>(a, s));
+  }
 #ifndef DSA_ATTN_LEGACY
   if (a.D == 128 && !kt32 && attn_max_tiles(a, 64) <= d128::kMaxTiles) {
     constexpr int ROWS = d128::NW * 32;
-    const int G = a.Hq / a.Hkv;
-    const int wg_per_qb = (G * a.block + ROWS - 1) / ROWS;
-    const int total = a.B * a.Hkv * nqb * wg_per_qb;
+    const int wg_per_qb = (a.sel_heads * a.block + ROWS - 1) / ROWS;
+    const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
     k_attn_bf16_d128<<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();

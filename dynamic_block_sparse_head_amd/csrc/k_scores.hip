@@ -42,24 +42,26 @@ __device__ __forceinline__ void load8(const float* p, float* f) {
   }
 }
 
-// out[bg, i, :] = sum over hpg heads of mean over the rows of block i.
-// grid (nb, B*Hkv, 2): z = 0 pools the queries (the G heads of each group
-// summed), z = 1 the keys.  Each thread owns 8 columns and a strided set of
-// rows.
+// out[bu, i, :] = sum over hpu heads of mean over the rows of block i.
+// grid (nb, B*U, 2) with U = Hq / SH selection units: z = 0 pools the
+// queries (the SH heads of each unit summed), z = 1 the keys (one KV head
+// per bu < B*Hkv).  Each thread owns 8 columns and a strided set of rows.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ q, const T* __restrict__ k,
-                                                   int Hq, int S, int D, int block, int G, int Hkv,
+                                                   int Hq, int S, int D, int block, int SH, int Hkv,
                                                    double* __restrict__ out_q,
                                                    double* __restrict__ out_k) {
   __shared__ double red[kThreads * 8];
   const bool keys = blockIdx.z != 0;
+  const int U = keys ? Hkv : Hq / SH;   // units (keys: KV heads) per sequence
+  const int bg = blockIdx.y;
+  if (keys && int(bg) >= int(gridDim.y) / (Hq / SH) * Hkv) return;   // whole workgroup
   const T* __restrict__ x = keys ? k : q;
   const int H = keys ? Hkv : Hq;
-  const int hpg = keys ? 1 : G;
+  const int hpg = keys ? 1 : SH;
   double* __restrict__ out = keys ? out_k : out_q;
   const int i = blockIdx.x;
-  const int bg = blockIdx.y;
-  const int b = bg / Hkv, g = bg % Hkv;
+  const int b = bg / U, g = bg % U;
   const int ncg = D / 8;
   const int nrg = kThreads / ncg;
   const int cg = threadIdx.x % ncg;
@@ -88,15 +90,18 @@ __global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ q, cons
   }
 }
 
-// scores[bg, i, j] = qs[bg, i, :] . kb[bg, j, :] for j <= i, -inf above the
-// diagonal.  32x32 output tile per workgroup; thread (ti, tj) owns rows
-// ti, ti+16 and columns tj, tj+16, i.e. four independent float64 dot
-// products fed from LDS (two query and two key values per step).
+// scores[bu, i, j] = qs[bu, i, :] . kb[kv(bu), j, :] for j <= i, -inf above
+// the diagonal, kv(bu) the KV head of selection unit bu (U units and Hkv KV
+// heads per sequence).  32x32 output tile per workgroup; thread (ti, tj)
+// owns rows ti, ti+16 and columns tj, tj+16, i.e. four independent float64
+// dot products fed from LDS (two query and two key values per step).
 __global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restrict__ qs,
                                                          const double* __restrict__ kb, int nb,
-                                                         int D, float* __restrict__ scores) {
+                                                         int D, int U, int Hkv,
+                                                         float* __restrict__ scores) {
   extern __shared__ double lds[];  // [32][D+2] queries, then [32][D+2] keys
   const int bg = blockIdx.z;
+  const int kvh = (bg / U) * Hkv + (bg % U) / (U / Hkv);   // its KV head (row of kb)
   const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
   const int ti = threadIdx.x / 16, tj = threadIdx.x % 16;
   float* srow = scores + size_t(bg) * nb * nb;
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restric
     const int r = e / hd, d = (e % hd) * 2;
     double2 a = {0.0, 0.0}, c = {0.0, 0.0};
     if (i0 + r < nb) a = *reinterpret_cast<const double2*>(qs + (size_t(bg) * nb + i0 + r) * D + d);
-    if (j0 + r < nb) c = *reinterpret_cast<const double2*>(kb + (size_t(bg) * nb + j0 + r) * D + d);
+    if (j0 + r < nb) c = *reinterpret_cast<const double2*>(kb + (size_t(kvh) * nb + j0 + r) * D + d);
     *reinterpret_cast<double2*>(lq + r * ld + d) = a;
     *reinterpret_cast<double2*>(lk + r * ld + d) = c;
   }
@@ -350,19 +355,20 @@ __global__ __launch_bounds__(kThreads) void k_page_minmax(const T* __restrict__ 
 
 hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s) {
   const int nb = (a.S + a.block - 1) / a.block;
-  const int G = a.Hq / a.Hkv;
-  dim3 grid(nb, a.B * a.Hkv, 2);
+  const int U = a.Hq / a.sel_heads;
+  dim3 grid(nb, a.B * U, 2);
   if (a.dtype == 1)
     k_pool<uint16_t><<<grid, kThreads, 0, s>>>(static_cast<const uint16_t*>(a.q),
                                                static_cast<const uint16_t*>(a.k), a.Hq, a.S, a.D,
-                                               a.block, G, a.Hkv, a.ws_q, a.ws_k);
+                                               a.block, a.sel_heads, a.Hkv, a.ws_q, a.ws_k);
   else
     k_pool<float><<<grid, kThreads, 0, s>>>(static_cast<const float*>(a.q),
                                             static_cast<const float*>(a.k), a.Hq, a.S, a.D,
-                                            a.block, G, a.Hkv, a.ws_q, a.ws_k);
+                                            a.block, a.sel_heads, a.Hkv, a.ws_q, a.ws_k);
   const int nt = (nb + 31) / 32;
   const size_t lds = size_t(2) * 32 * (a.D + 2) * sizeof(double);
-  k_pooled_dot<<<dim3(nt, nt, a.B * a.Hkv), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, a.D, a.scores);
+  k_pooled_dot<<<dim3(nt, nt, a.B * U), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, a.D, U, a.Hkv,
+                                                            a.scores);
   return hipGetLastError();
 }
 

@@ -19,30 +19,41 @@ def _empty(shape, dtype, device):
 
 
 class PrefillPlan:
-    """Pooled scores -> top-k + window -> block-sparse attention ([DMA] §五)."""
+    """Pooled scores -> top-k + window -> block-sparse attention ([DMA] §五).
 
-    def __init__(self, B, Hq, Hkv, S, D, block, topk, n_local, dtype, device, scale=None):
+    per_head=False: one selection per KV group (its query heads' scores
+    summed); per_head=True: every query head ranks and keeps its own blocks."""
+
+    def __init__(self, B, Hq, Hkv, S, D, block, topk, n_local, dtype, device, scale=None,
+                 per_head=False):
         self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
         self.block, self.topk, self.n_local = block, topk, n_local
         self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
         self.nb = -(-S // block)
-        ws = L.dsa_block_scores_workspace_size(L.DSA_SCORE_POOLED, B, Hq, Hkv, S, D, block)
+        self.per_head = per_head
+        self.kind = L.DSA_SCORE_POOLED_HEAD if per_head else L.DSA_SCORE_POOLED
+        U = Hq if per_head else Hkv                     # selection units per sequence
+        ws = L.dsa_block_scores_workspace_size(self.kind, B, Hq, Hkv, S, D, block)
         self.ws = _empty((ws,), torch.uint8, device)
-        self.scores = _empty((B, Hkv, self.nb, self.nb), torch.float32, device)
-        self.idx = _empty((B, Hkv, self.nb, topk + n_local), torch.int32, device)
-        self.count = _empty((B, Hkv, self.nb), torch.int32, device)
+        self.scores = _empty((B, U, self.nb, self.nb), torch.float32, device)
+        self.idx = _empty((B, U, self.nb, topk + n_local), torch.int32, device)
+        self.count = _empty((B, U, self.nb), torch.int32, device)
         self.out = _empty((B, Hq, S, D), dtype, device)
         self.lse = _empty((B, Hq, S), torch.float32, device)
 
     def score(self, q, k):
-        L.dsa_block_scores(L.DSA_SCORE_POOLED, q, k, None, self.block, self.ws, self.scores)
+        L.dsa_block_scores(self.kind, q, k, None, self.block, self.ws, self.scores)
 
     def select(self):
         L.dsa_topk_select(self.scores, self.topk, self.n_local, True, self.idx, self.count)
 
     def attend(self, q, k, v):
-        L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.block, 0, self.scale,
-                                  self.out, self.lse)
+        if self.per_head:
+            L.dsa_sparse_attn_prefill_sel(q, k, v, self.idx, self.count, self.block, 1, self.scale,
+                                          self.out, self.lse)
+        else:
+            L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.block, 0, self.scale,
+                                      self.out, self.lse)
 
     def run(self, q, k, v):
         self.score(q, k)
@@ -52,7 +63,10 @@ class PrefillPlan:
 
     def backward(self, q, k, v, dout):
         """dq, dk, dv of the last run's attention for the upstream gradient
-        dout ([DMA] §四-§五); the run's index lists are held fixed."""
+        dout ([DMA] §四-§五); the run's index lists are held fixed.  Takes
+        per-KV-group lists only."""
+        if self.per_head:
+            raise NotImplementedError("the backward takes per-KV-group index lists")
         if not hasattr(self, "dq"):
             B, Hq, Hkv, S, D = self.B, self.Hq, self.Hkv, self.S, self.D
             ws = L.dsa_sparse_attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D, self.block)

@@ -56,8 +56,9 @@ enum dsa_status {
 enum dsa_dtype { DSA_F32 = 0, DSA_BF16 = 1 };
 
 enum dsa_score_kind {
-  DSA_SCORE_POOLED = 0,     /* prefill: mean-pooled query block . mean-pooled key block */
-  DSA_SCORE_PAGE_BOUND = 1  /* decode: per-page min/max key bound */
+  DSA_SCORE_POOLED = 0,      /* prefill: mean-pooled query block . mean-pooled key block */
+  DSA_SCORE_PAGE_BOUND = 1,  /* decode: per-page min/max key bound */
+  DSA_SCORE_POOLED_HEAD = 2  /* prefill, one score per query head (no group sum) */
 };
 
 int dsa_version(void);
@@ -76,6 +77,12 @@ const char* dsa_last_error(void);
  *   heads h of group g of mean(Q[b,h,block i]) . mean(K[b,g,block j]) for
  *   j <= i, -inf for j > i.  Means, dots and the head sum are accumulated
  *   in float64 and rounded once to float32.  Needs a workspace of
+ *   dsa_block_scores_workspace_size() bytes.
+ *
+ * kind = DSA_SCORE_POOLED_HEAD: as DSA_SCORE_POOLED with every query head
+ *   its own selection unit ([DMA] §四: every head gets its own mask):
+ *   scores [B,Hq,nb,nb], scores[b,h,i,j] = mean(Q[b,h,block i]) .
+ *   mean(K[b,h/(Hq/Hkv),block j]).  Needs a (larger) workspace of
  *   dsa_block_scores_workspace_size() bytes.
  *
  * kind = DSA_SCORE_PAGE_BOUND:
@@ -129,6 +136,22 @@ int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void*
                             int B, int Hq, int Hkv, int S, int D,
                             const int32_t* idx, const int32_t* count, int idx_width, int block,
                             int window, float scale, void* out, float* lse, void* stream);
+
+/*
+ * dsa_sparse_attn_prefill in index mode with a chosen selection unit:
+ * sel_heads consecutive query heads share one index list ([DMA] §四 gives
+ * every head its own mask; sel_heads = Hq/Hkv is the per-KV-group sharing of
+ * dsa_sparse_attn_prefill, sel_heads = 1 per-query-head lists).
+ * idx [B,Hq/sel_heads,ceil(S/block),idx_width], count [B,Hq/sel_heads,
+ * ceil(S/block)]; query head h uses the lists of unit h / sel_heads and the
+ * K/V of its KV head.  Everything else as dsa_sparse_attn_prefill.
+ * Errors: DSA_E_ARG unless sel_heads divides Hq/Hkv.
+ */
+int dsa_sparse_attn_prefill_sel(int dtype, const void* q, const void* k, const void* v,
+                                int B, int Hq, int Hkv, int S, int D,
+                                const int32_t* idx, const int32_t* count, int idx_width,
+                                int block, int sel_heads, float scale, void* out, float* lse,
+                                void* stream);
 
 /*
  * Gradients of dsa_sparse_attn_prefill in index mode ([DMA] §四-§五: the
