@@ -8,11 +8,12 @@ top-16 blocks + 512-token window), inputs resident in HBM.  The line also
 carries the attention kernel's roofline (effective FLOPs on selected blocks
 against the bf16 MFMA peak), the decode path's HBM rate on the 128K-page
 workload, the long-prefill and three-branch workloads, the backward of the
-headline attention, and the CPU oracle timed on a bounded sample of the
-headline workload.
+headline attention, the per-query-head selection variant, and the CPU oracle
+timed on a bounded sample of the headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|long|nsa|backward] [--copy-calibration]
+                    [--only prefill|decode|long|nsa|backward|per_head]
+                    [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -206,6 +207,31 @@ def bench_decode(torch, iters=20, n_query_sets=4):
             "page_metadata_build_ms": round(t_meta, 3)}
 
 
+def bench_per_head(torch, iters=10):
+    """The 16K prefill path with per-query-head selection (every query head
+    ranks blocks by its own pooled score and keeps its own list): scores,
+    selection and attention; effective FLOPs count each head's own blocks."""
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import PrefillPlan
+
+    c = configs.PREFILL_16K
+    x = inputs.prefill_inputs(c, seed=0, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda",
+                       per_head=True)
+    plan.run(q, k, v)
+    ms_step = _timed(lambda: plan.run(q, k, v), iters, torch)
+    ms_attn = _timed(lambda: plan.attend(q, k, v), iters, torch)
+    sel = int(plan.count.to(torch.int64).sum().item())   # (query head, q-block, k-block) triples
+    flops = 4.0 * c.D * c.block * c.block * sel
+    del x, q, k, v, plan
+    return {"workload": f"{c.name}: per-query-head selection (32 lists per query block)",
+            "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.S / (ms_step * 1e-3), 1),
+            "attn_ms": round(ms_attn, 4),
+            "attn_effective_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
+            "attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_backward(torch, iters=10):
     """Gradients of the 16K prefill's attention (dq, dk, dv) for an N(0,1)
     upstream gradient, the forward's selection held fixed.  Effective FLOPs
@@ -317,7 +343,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward"],
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward", "per_head"],
                     default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -378,6 +404,8 @@ def main():
         extra["nsa"] = bench_nsa(torch)
     if args.only in (None, "backward"):
         extra["backward"] = bench_backward(torch)
+    if args.only in (None, "per_head"):
+        extra["per_head_selection"] = bench_per_head(torch)
     line.update(extra)
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         line["cpu_baseline"] = cpu_baseline()
