@@ -17,7 +17,8 @@ import torch
 
 from .configs import DecodeConfig, NSAConfig, PrefillConfig
 
-_TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gates": 3, "needles": 4, "clusters": 5, "dout": 6}
+_TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "gates": 3, "needles": 4, "clusters": 5, "dout": 6,
+               "dma": 7}
 
 
 def _dtype(name: str) -> torch.dtype:
@@ -134,6 +135,15 @@ def grad_output(cfg: PrefillConfig, seed: int = 0, device="cpu"):
     dev = torch.device(device)
     d = _normal((cfg.B, cfg.Hq, cfg.S, cfg.D), 1.0, _gen(dev, seed, cfg.name, "dout"), dev)
     return d.to(_dtype(cfg.dtype)).contiguous()
+
+
+def dma_params(cfg: PrefillConfig, seed: int = 0, device="cpu"):
+    """Value-driven mask parameters per KV head: a projection Delta [Hkv,D]
+    ~ N(0,1) and a gain A [Hkv] ~ U(0.1, 0.5), both float32."""
+    rng = _host_rng(seed, cfg.name, "dma")
+    delta = rng.standard_normal((cfg.Hkv, cfg.D)).astype(np.float32)
+    A = rng.uniform(0.1, 0.5, size=cfg.Hkv).astype(np.float32)
+    return torch.from_numpy(delta).to(device), torch.from_numpy(A).to(device)
 
 
 def decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):

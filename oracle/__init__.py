@@ -35,9 +35,15 @@ something other than itself):
                                                        by those two (documented as partly pinned)
   nsa.window_attention                               — W >= S dense limit, W = 1 identity
   nsa.combine                                        — closed form when branches coincide
+  dma.softplus, dma.dynamic_weights                  — softplus identities and limits, v = 0 and
+                                                       A = 0 closed forms
+  dma.block_weights, dma.block_scores                — hand example, broadcast structure
+  dma.biased_sparse_attention                        — dense SDPA with an additive float mask,
+                                                       shift invariance under a constant bias
+  dma.dma_prefill                                    — planted heavy block selected everywhere
   backward.sparse_attention_backward                 — central finite differences of the
                                                        forward oracle, autograd of a dense masked
                                                        formulation, exact zeros off the mask,
                                                        softmax identities
 """
-from . import backward, decode, nsa, prefill  # noqa: F401
+from . import backward, decode, dma, nsa, prefill  # noqa: F401
