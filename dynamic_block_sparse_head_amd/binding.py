@@ -37,8 +37,9 @@ SIGNATURES = {
     "dsa_sparse_attn_prefill_backward": (_c_int, [_c_int] + [_vp] * 4 + [_vp, _vp]
                                          + [_c_int] * 5 + [_vp, _vp] + [_c_int] * 2
                                          + [_c_float, _vp, _c_size, _vp, _vp, _vp, _vp]),
-    "dsa_sparse_attn_prefill_sel": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
-                                    + [_c_int] * 3 + [_c_float, _vp, _vp, _vp]),
+    "dsa_sparse_attn_prefill_ex": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                                   + [_c_int] * 3 + [_vp, _c_float, _vp, _vp, _vp]),
+    "dsa_dma_weights": (_c_int, [_c_int, _vp] + [_c_int] * 4 + [_vp, _vp, _c_int, _vp, _vp, _vp]),
     "dsa_page_minmax": (_c_int, [_c_int, _vp] + [_c_int] * 5 + [_vp, _vp, _vp]),
     "dsa_sparse_attn_decode_workspace_size": (_c_size, [_c_int] * 6),
     "dsa_sparse_attn_decode": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
@@ -175,16 +176,26 @@ def dsa_sparse_attn_prefill_backward(q, k, v, out, lse, dout, idx, count, block,
     _check(st, "dsa_sparse_attn_prefill_backward")
 
 
-def dsa_sparse_attn_prefill_sel(q, k, v, idx, count, block, sel_heads, scale, out, lse=None,
-                                stream=None):
+def dsa_sparse_attn_prefill_ex(q, k, v, idx, count, block, sel_heads, key_bias, scale, out,
+                               lse=None, stream=None):
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    st = load().dsa_sparse_attn_prefill_sel(
+    st = load().dsa_sparse_attn_prefill_ex(
         _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S, D,
         _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), idx.shape[-1], block,
-        sel_heads, float(scale), _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32),
-        _stream(stream))
-    _check(st, "dsa_sparse_attn_prefill_sel")
+        sel_heads, _ptr(key_bias, "key_bias", torch.float32), float(scale),
+        _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream))
+    _check(st, "dsa_sparse_attn_prefill_ex")
+
+
+def dsa_dma_weights(v, proj, gain, block, weights, block_scores=None, stream=None):
+    """v [B,Hkv,S,D] -> weights [B,Hkv,S] (and block_scores [B,Hkv,nb,nb])."""
+    B, Hkv, S, D = v.shape
+    st = load().dsa_dma_weights(_dtype_code(v), _ptr(v, "v"), B, Hkv, S, D,
+                                _ptr(proj, "proj", torch.float32), _ptr(gain, "gain", torch.float32),
+                                block, _ptr(weights, "weights", torch.float32),
+                                _ptr(block_scores, "block_scores", torch.float32), _stream(stream))
+    _check(st, "dsa_dma_weights")
 
 
 def dsa_page_minmax(k, page, kmin, kmax, stream=None):

@@ -165,8 +165,9 @@ int dsa_topk_select(const float* scores, int rows, int n_q, int n_k, int k, int 
 
 static int prefill_impl(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
                         int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
-                        int idx_width, int block, int window, int sel_heads, float scale,
-                        void* out, float* lse, void* stream) {
+                        int idx_width, int block, int window, int sel_heads,
+                        const float* key_bias, float scale, void* out, float* lse,
+                        void* stream) {
   TRY(check_dtype(dtype, true));
   TRY(check_heads(B, Hq, Hkv));
   TRY(check_dim(D));
@@ -208,7 +209,11 @@ static int prefill_impl(int dtype, const void* q, const void* k, const void* v, 
   a.cmp_len = 1;
   a.cmp_stride = 1;
   a.sel_heads = sel_heads;
+  a.key_bias = key_bias;
   a.scale = scale;
+  REQUIRE(dsa::attention_supported(a), DSA_E_UNSUPPORTED,
+          "key_bias needs D = 128, blocks of 64k tokens and at least 256 rows per selection unit "
+          "(bf16), or DSA_F32");
   return hip_status(dsa::launch_attention(a, static_cast<hipStream_t>(stream)),
                     "dsa_sparse_attn_prefill");
 }
@@ -220,20 +225,44 @@ int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void*
   g_err.clear();
   TRY(check_heads(B, Hq, Hkv));
   return prefill_impl(dtype, q, k, v, B, Hq, Hkv, S, D, idx, count, idx_width, block, window,
-                      Hq / Hkv, scale, out, lse, stream);
+                      Hq / Hkv, nullptr, scale, out, lse, stream);
 }
 
-int dsa_sparse_attn_prefill_sel(int dtype, const void* q, const void* k, const void* v, int B,
-                                int Hq, int Hkv, int S, int D, const int32_t* idx,
-                                const int32_t* count, int idx_width, int block, int sel_heads,
-                                float scale, void* out, float* lse, void* stream) {
+int dsa_sparse_attn_prefill_ex(int dtype, const void* q, const void* k, const void* v, int B,
+                               int Hq, int Hkv, int S, int D, const int32_t* idx,
+                               const int32_t* count, int idx_width, int block, int sel_heads,
+                               const float* key_bias, float scale, void* out, float* lse,
+                               void* stream) {
   g_err.clear();
   TRY(check_heads(B, Hq, Hkv));
   REQUIRE(sel_heads >= 1 && (Hq / Hkv) % sel_heads == 0, DSA_E_ARG,
           "sel_heads (%d) must divide Hq/Hkv (%d)", sel_heads, Hq / Hkv);
   REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  if (key_bias != nullptr) REQUIRE_PTR(key_bias);
   return prefill_impl(dtype, q, k, v, B, Hq, Hkv, S, D, idx, count, idx_width, block, 0, sel_heads,
-                      scale, out, lse, stream);
+                      key_bias, scale, out, lse, stream);
+}
+
+int dsa_dma_weights(int dtype, const void* v, int B, int Hkv, int S, int D, const float* proj,
+                    const float* gain, int block, float* weights, float* block_scores,
+                    void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, true));
+  TRY(check_heads(B, Hkv, Hkv));
+  TRY(check_dim(D));
+  TRY(check_block(block, "block"));
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE(rows_fit(B, Hkv, S), DSA_E_ARG, "B*Hkv*S too large");
+  const long long nb = (S + block - 1) / block;
+  REQUIRE(nb <= 65535, DSA_E_UNSUPPORTED, "at most 65535 blocks");
+  REQUIRE((long long)B * Hkv * nb * nb < (1ll << 31), DSA_E_ARG, "B*Hkv*nb*nb too large");
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(proj);
+  REQUIRE(gain != nullptr, DSA_E_ARG, "gain must not be NULL");
+  REQUIRE(weights != nullptr, DSA_E_ARG, "weights must not be NULL");
+  return hip_status(dsa::launch_dma_weights(dtype, v, B, Hkv, S, D, proj, gain, block, weights,
+                                            block_scores, static_cast<hipStream_t>(stream)),
+                    "dsa_dma_weights");
 }
 
 size_t dsa_sparse_attn_prefill_backward_workspace_size(int B, int Hq, int Hkv, int S, int D,
@@ -396,6 +425,7 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, i
   a.cmp_len = len;
   a.cmp_stride = stride;
   a.sel_heads = Hq / Hkv;
+  a.key_bias = nullptr;
   a.scale = scale;
   int st = hip_status(dsa::launch_attention(a, s), "dsa_nsa_cmp_attn");
   if (st != DSA_OK || block_scores == nullptr) return st;

@@ -59,9 +59,16 @@ struct AttnArgs {
   int window;           // window mode: tokens
   int cmp_len, cmp_stride;  // compressed mode: summary c ends at c*stride+len-1
   int sel_heads;        // query heads sharing one index row (Hq/Hkv unless per-head lists)
+  const float* key_bias;  // [B,Hkv,Skv] additive logit term per key, or null
   float scale;
 };
+// Whether some kernel serves this configuration (host-side check).
+bool attention_supported(const AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_dma_weights(int dtype, const void* v, int B, int Hkv, int S, int D,
+                              const float* proj, const float* gain, int block, float* weights,
+                              float* block_scores, hipStream_t s);
 
 struct AttnBwdArgs {
   const void* q;        // [B,Hq,S,D] bf16

@@ -449,12 +449,16 @@ constexpr int kMaxTiles = 128;         // key tiles per query block (lane table)
 
 #define DSA_LDS_BF16X4(p) ((__attribute__((address_space(3))) bf16x4*)(p))
 
+// BIAS: every key carries an additive logit term (key_bias, per KV head and
+// position), staged per tile next to K.
+template <bool BIAS>
 __global__ __launch_bounds__(d128::NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
 void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
   using namespace d128;
   constexpr int ROWS = NW * 32;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VBYTES];
+  __shared__ __attribute__((aligned(16))) float kbias[2][BIAS ? KT : 4];   // key_bias / scale
 
   const int w = xcd_work_id(per_xcd);
   if (w >= total) return;
@@ -539,10 +543,18 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
     }
   }
   u32x4 stk[2], stv[2];
+  u32x4 stb = {0u, 0u, 0u, 0u};   // BIAS: four key terms (wave 0, lanes 0..15)
+  // (BIAS only; without it the descriptor covers nothing and is never used)
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(BIAS ? a.key_bias + size_t(bg) * a.Skv : a.q, BIAS ? uint32_t(a.Skv) * 4 : 0u);
+  const float inv_scale = 1.f / a.scale;
   auto load_k = [&](int n) __attribute__((always_inline)) {
     const uint32_t base = uint32_t(key0_of(n)) * uint32_t(D * 2);
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) stk[j2] = __builtin_amdgcn_raw_buffer_load_b128(krs, kvo[j2], base, 0);
+    if constexpr (BIAS)
+      if (wave == 0 && lane < KT / 4)
+        stb = __builtin_amdgcn_raw_buffer_load_b128(brs, uint32_t(lane * 16), uint32_t(key0_of(n)) * 4u, 0);
   };
   auto load_v = [&](int n) __attribute__((always_inline)) {
     const uint32_t base = uint32_t(key0_of(n)) * uint32_t(D * 2);
@@ -553,6 +565,13 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2)
       *reinterpret_cast<u32x4*>(&kbuf[buf][(2 * wave + j2) * KCH + lane * 16]) = stk[j2];
+    if constexpr (BIAS)
+      if (wave == 0 && lane < KT / 4) {
+        floatx4 bv = __builtin_bit_cast(floatx4, stb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] *= inv_scale;
+        *reinterpret_cast<floatx4*>(&kbias[buf][lane * 4]) = bv;
+      }
   };
   auto store_v = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
@@ -629,6 +648,16 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   };
   auto softmax = [&](int n) __attribute__((always_inline)) {
     const int key0 = key0_of(n);
+    if constexpr (BIAS) {   // logit += key_bias: in units of s, key_bias / scale
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const floatx4 b4 = *reinterpret_cast<const floatx4*>(&kbias[n & 1][kt * 32 + e4 * 8 + half * 4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kt][e4 * 4 + e] += b4[e];
+        }
+    }
     if (key0 < blk_lo || key0 + KT - 1 > blk_hi) {   // wave-uniform
       asm volatile("");   // a real branch: if-converting it would copy s
       const int lo = row_lo - key0, hi = row_hi - key0;
@@ -760,7 +789,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
       float dot = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) dot = fmaf(qv[d], k_lds[kk][d], dot);
-      const float sc = dot * a.scale;
+      const float sc = dot * a.scale + (a.key_bias ? a.key_bias[size_t(bg) * a.Skv + key0 + kk] : 0.f);
       if (sc > m) {  // new running maximum: rescale what was accumulated
         const float alpha = expf(m - sc);
         l *= alpha;
@@ -802,7 +831,25 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+bool uses_d128(const AttnArgs& a) {
+#ifdef DSA_ATTN_LEGACY
+  return false;
+#else
+  const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
+  return a.dtype == 1 && a.D == 128 && !kt32 && a.sel_heads * a.block >= 256 &&
+         attn_max_tiles(a, 64) <= d128::kMaxTiles;
+#endif
+}
+}  // namespace
+
+bool attention_supported(const AttnArgs& a) {
+  // the additive key term exists in the float32 kernel and the D = 128 one
+  return a.key_bias == nullptr || a.dtype == 0 || uses_d128(a);
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (!attention_supported(a)) return hipErrorInvalidValue;
   const int nqb = (a.S + a.block - 1) / a.block;
   if (a.dtype == 0) {
     dim3 grid(nqb, a.Hq, a.B);
@@ -829,12 +876,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                 : (nw == 2 ? run_bf16<64, 64, 1, 2>(a, s) : run_bf16<64, 64, 1, 4>(a, s));
   }
 #ifndef DSA_ATTN_LEGACY
-  if (a.D == 128 && !kt32 && attn_max_tiles(a, 64) <= d128::kMaxTiles) {
+  if (uses_d128(a)) {
     constexpr int ROWS = d128::NW * 32;
     const int wg_per_qb = (a.sel_heads * a.block + ROWS - 1) / ROWS;
     const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
-    k_attn_bf16_d128<<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    if (a.key_bias)
+      k_attn_bf16_d128<true><<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    else
+      k_attn_bf16_d128<false><<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();
   }
 #endif

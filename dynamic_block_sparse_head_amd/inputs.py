@@ -139,9 +139,10 @@ def grad_output(cfg: PrefillConfig, seed: int = 0, device="cpu"):
 
 def dma_params(cfg: PrefillConfig, seed: int = 0, device="cpu"):
     """Value-driven mask parameters per KV head: a projection Delta [Hkv,D]
-    ~ N(0,1) and a gain A [Hkv] ~ U(0.1, 0.5), both float32."""
+    ~ N(0, 1/(D v_std^2)), so that v . Delta ~ N(0, 1) whatever the value
+    scale, and a gain A [Hkv] ~ U(0.1, 0.5), both float32."""
     rng = _host_rng(seed, cfg.name, "dma")
-    delta = rng.standard_normal((cfg.Hkv, cfg.D)).astype(np.float32)
+    delta = (rng.standard_normal((cfg.Hkv, cfg.D)) / (np.sqrt(cfg.D) * cfg.v_std)).astype(np.float32)
     A = rng.uniform(0.1, 0.5, size=cfg.Hkv).astype(np.float32)
     return torch.from_numpy(delta).to(device), torch.from_numpy(A).to(device)
 

@@ -49,8 +49,8 @@ class PrefillPlan:
 
     def attend(self, q, k, v):
         if self.per_head:
-            L.dsa_sparse_attn_prefill_sel(q, k, v, self.idx, self.count, self.block, 1, self.scale,
-                                          self.out, self.lse)
+            L.dsa_sparse_attn_prefill_ex(q, k, v, self.idx, self.count, self.block, 1, None,
+                                         self.scale, self.out, self.lse)
         else:
             L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.block, 0, self.scale,
                                       self.out, self.lse)
@@ -78,6 +78,40 @@ class PrefillPlan:
                                            self.block, self.scale, self.bwd_ws, self.dq, self.dk,
                                            self.dv)
         return self.dq, self.dk, self.dv
+
+
+class DMAPlan:
+    """Value-driven dynamic mask ([DMA] §四-§五): weights from the values ->
+    heaviest key blocks + window -> attention over them with each kept key's
+    weight added to its logit."""
+
+    def __init__(self, B, Hq, Hkv, S, D, block, topk, n_local, dtype, device, scale=None):
+        self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
+        self.block, self.topk, self.n_local = block, topk, n_local
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
+        self.nb = -(-S // block)
+        self.weights = _empty((B, Hkv, S), torch.float32, device)
+        self.scores = _empty((B, Hkv, self.nb, self.nb), torch.float32, device)
+        self.idx = _empty((B, Hkv, self.nb, topk + n_local), torch.int32, device)
+        self.count = _empty((B, Hkv, self.nb), torch.int32, device)
+        self.out = _empty((B, Hq, S, D), dtype, device)
+        self.lse = _empty((B, Hq, S), torch.float32, device)
+
+    def score(self, v, proj, gain):
+        L.dsa_dma_weights(v, proj, gain, self.block, self.weights, self.scores)
+
+    def select(self):
+        L.dsa_topk_select(self.scores, self.topk, self.n_local, True, self.idx, self.count)
+
+    def attend(self, q, k, v):
+        L.dsa_sparse_attn_prefill_ex(q, k, v, self.idx, self.count, self.block, self.Hq // self.Hkv,
+                                     self.weights, self.scale, self.out, self.lse)
+
+    def run(self, q, k, v, proj, gain):
+        self.score(v, proj, gain)
+        self.select()
+        self.attend(q, k, v)
+        return self.out
 
 
 class DecodePlan:

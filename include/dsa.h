@@ -138,20 +138,41 @@ int dsa_sparse_attn_prefill(int dtype, const void* q, const void* k, const void*
                             int window, float scale, void* out, float* lse, void* stream);
 
 /*
- * dsa_sparse_attn_prefill in index mode with a chosen selection unit:
- * sel_heads consecutive query heads share one index list ([DMA] §四 gives
- * every head its own mask; sel_heads = Hq/Hkv is the per-KV-group sharing of
- * dsa_sparse_attn_prefill, sel_heads = 1 per-query-head lists).
- * idx [B,Hq/sel_heads,ceil(S/block),idx_width], count [B,Hq/sel_heads,
- * ceil(S/block)]; query head h uses the lists of unit h / sel_heads and the
- * K/V of its KV head.  Everything else as dsa_sparse_attn_prefill.
+ * dsa_sparse_attn_prefill in index mode with two extensions.
+ *  - Selection unit: sel_heads consecutive query heads share one index list
+ *    ([DMA] §四 gives every head its own mask; sel_heads = Hq/Hkv is the
+ *    per-KV-group sharing of dsa_sparse_attn_prefill, sel_heads = 1 gives
+ *    per-query-head lists).  idx [B,Hq/sel_heads,ceil(S/block),idx_width],
+ *    count [B,Hq/sel_heads,ceil(S/block)]; query head h uses the lists of
+ *    unit h / sel_heads and the K/V of its KV head.
+ *  - key_bias [B,Hkv,S] float32 or NULL: an additive term of every key's
+ *    logit, scale q.k + key_bias[b,g,s] ([DMA] §五: a kept position's mask
+ *    value is its dynamic weight; dsa_dma_weights computes them).  Supported
+ *    for DSA_F32, and for bf16 with D = 128, blocks a multiple of 64 and
+ *    sel_heads * block >= 256; otherwise DSA_E_UNSUPPORTED.
+ * Everything else as dsa_sparse_attn_prefill (lse includes the bias).
  * Errors: DSA_E_ARG unless sel_heads divides Hq/Hkv.
  */
-int dsa_sparse_attn_prefill_sel(int dtype, const void* q, const void* k, const void* v,
-                                int B, int Hq, int Hkv, int S, int D,
-                                const int32_t* idx, const int32_t* count, int idx_width,
-                                int block, int sel_heads, float scale, void* out, float* lse,
-                                void* stream);
+int dsa_sparse_attn_prefill_ex(int dtype, const void* q, const void* k, const void* v,
+                               int B, int Hq, int Hkv, int S, int D,
+                               const int32_t* idx, const int32_t* count, int idx_width,
+                               int block, int sel_heads, const float* key_bias, float scale,
+                               void* out, float* lse, void* stream);
+
+/*
+ * Value-driven dynamic weights ([DMA] §四-§五: a weight per history position
+ * from the value content, delta = exp(tau(v Delta) x A), tau non-negative).
+ * v [B,Hkv,S,D] (dtype), proj [Hkv,D] float32 (Delta, one projection per KV
+ * head), gain [Hkv] float32 (A).  Writes weights [B,Hkv,S] float32:
+ *   weights[b,g,s] = exp(gain[g] * softplus(v[b,g,s,:] . proj[g,:])),
+ * softplus(x) = log(1 + e^x), float32 arithmetic.  If block_scores is not
+ * NULL, also writes block_scores [B,Hkv,nb,nb] (nb = ceil(S/block)): for
+ * j <= i the largest weight of key block j, -inf above the diagonal — the
+ * input dsa_topk_select expects for causal block selection.
+ */
+int dsa_dma_weights(int dtype, const void* v, int B, int Hkv, int S, int D, const float* proj,
+                    const float* gain, int block, float* weights, float* block_scores,
+                    void* stream);
 
 /*
  * Gradients of dsa_sparse_attn_prefill in index mode ([DMA] §四-§五: the

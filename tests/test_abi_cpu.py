@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -116,8 +116,9 @@ def test_selection_unit_validation():
     g = lib.dsa_block_scores_workspace_size(0, 1, 32, 8, 16384, 128, 64)
     h = lib.dsa_block_scores_workspace_size(2, 1, 32, 8, 16384, 128, 64)
     assert h == (32 + 8) * 256 * 128 * 8 and g == 2 * 8 * 256 * 128 * 8
-    f = lib.dsa_sparse_attn_prefill_sel
-    args = [1, FAKE, FAKE, FAKE, 1, 32, 8, 2048, 128, FAKE, FAKE, 24, 64, 1, 0.1, FAKE, None, None]
+    f = lib.dsa_sparse_attn_prefill_ex
+    args = [1, FAKE, FAKE, FAKE, 1, 32, 8, 2048, 128, FAKE, FAKE, 24, 64, 1, None, 0.1, FAKE, None,
+            None]
     a = list(args); a[13] = 3
     assert f(*a) == L.DSA_E_ARG                                    # 3 does not divide G = 4
     assert "sel_heads" in _err()
@@ -127,6 +128,22 @@ def test_selection_unit_validation():
     assert f(*a) == L.DSA_E_ARG                                    # index lists required
     a = list(args); a[12] = 48
     assert f(*a) == L.DSA_E_UNSUPPORTED                            # block 48
+    a = list(args); a[14] = FAKE
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # key bias with per-head units
+
+
+def test_dma_weights_validation():
+    lib = L.load()
+    f = lib.dsa_dma_weights
+    args = [1, FAKE, 1, 8, 2048, 128, FAKE, FAKE, 64, FAKE, FAKE, None]
+    a = list(args); a[5] = 96
+    assert f(*a) == L.DSA_E_UNSUPPORTED
+    a = list(args); a[7] = None
+    assert f(*a) == L.DSA_E_ARG and "gain" in _err()
+    a = list(args); a[6] = MISALIGNED
+    assert f(*a) == L.DSA_E_ARG
+    a = list(args); a[8] = 33
+    assert f(*a) == L.DSA_E_UNSUPPORTED
 
 
 def test_backward_validation():

@@ -78,8 +78,8 @@ def test_lists_shared_by_sel_heads(sel):
     idx, cnt = Op.select_blocks(s, c.topk, c.n_local, True)
     out = torch.empty_like(x["q"])
     lse = torch.empty((c.B, c.Hq, c.S), dtype=torch.float32, device=DEV)
-    L.dsa_sparse_attn_prefill_sel(x["q"], x["k"], x["v"], torch.from_numpy(idx).to(DEV),
-                                  torch.from_numpy(cnt).to(DEV), c.block, sel, c.scale, out, lse)
+    L.dsa_sparse_attn_prefill_ex(x["q"], x["k"], x["v"], torch.from_numpy(idx).to(DEV),
+                                 torch.from_numpy(cnt).to(DEV), c.block, sel, None, c.scale, out, lse)
     torch.cuda.synchronize()
     ref, rl = Op.sparse_attention(q, k, v, idx, cnt, c.block, c.scale, sel_heads=sel)
     check_bf16(to_np(out), ref, f"sel {sel}")
@@ -92,7 +92,7 @@ def test_sel_heads_equal_to_group_matches_the_group_call():
     plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, x["q"].dtype, DEV)
     plan.run(x["q"], x["k"], x["v"])
     out = torch.empty_like(plan.out)
-    L.dsa_sparse_attn_prefill_sel(x["q"], x["k"], x["v"], plan.idx, plan.count, c.block, c.G,
-                                  c.scale, out)
+    L.dsa_sparse_attn_prefill_ex(x["q"], x["k"], x["v"], plan.idx, plan.count, c.block, c.G, None,
+                                 c.scale, out)
     torch.cuda.synchronize()
     assert torch.equal(out, plan.out)
