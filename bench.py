@@ -8,11 +8,12 @@ top-16 blocks + 512-token window), inputs resident in HBM.  The line also
 carries the attention kernel's roofline (effective FLOPs on selected blocks
 against the bf16 MFMA peak), the decode path's HBM rate on the 128K-page
 workload, the long-prefill and three-branch workloads, the backward of the
-headline attention, the per-query-head selection variant, and the CPU oracle
-timed on a bounded sample of the headline workload.
+headline attention, the per-query-head selection and value-driven mask
+variants, and the CPU oracle timed on a bounded sample of the headline
+workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|long|nsa|backward|per_head]
+                    [--only prefill|decode|long|nsa|backward|per_head|dma]
                     [--copy-calibration]
 """
 from __future__ import annotations
@@ -232,6 +233,33 @@ def bench_per_head(torch, iters=10):
             "attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def bench_dma(torch, iters=10):
+    """The 16K workload shape with the value-driven dynamic mask: weights from
+    the values, heaviest 16 blocks + 512-token window, attention with each
+    kept key's weight added to its logit."""
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import DMAPlan
+
+    c = configs.PREFILL_16K
+    x = inputs.prefill_inputs(c, seed=0, device="cuda")
+    proj, gain = inputs.dma_params(c, seed=0, device="cuda")
+    q, k, v = x["q"], x["k"], x["v"]
+    plan = DMAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
+    plan.run(q, k, v, proj, gain)
+    ms_step = _timed(lambda: plan.run(q, k, v, proj, gain), iters, torch)
+    ms_w = _timed(lambda: plan.score(v, proj, gain), iters, torch)
+    ms_attn = _timed(lambda: plan.attend(q, k, v), iters, torch)
+    sel = int(plan.count.to(torch.int64).sum().item())
+    flops = 4.0 * c.D * c.block * c.block * c.G * sel
+    del x, q, k, v, plan
+    return {"workload": f"{c.name} shape, value-driven mask: weights exp(A softplus(v.Delta)), "
+                        "top-16 blocks by largest weight + window 512, weights added to logits",
+            "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.S / (ms_step * 1e-3), 1),
+            "weights_ms": round(ms_w, 4), "attn_ms": round(ms_attn, 4),
+            "attn_effective_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
+            "attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_backward(torch, iters=10):
     """Gradients of the 16K prefill's attention (dq, dk, dv) for an N(0,1)
     upstream gradient, the forward's selection held fixed.  Effective FLOPs
@@ -343,8 +371,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward", "per_head"],
-                    default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward", "per_head",
+                                       "dma"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -406,6 +434,8 @@ def main():
         extra["backward"] = bench_backward(torch)
     if args.only in (None, "per_head"):
         extra["per_head_selection"] = bench_per_head(torch)
+    if args.only in (None, "dma"):
+        extra["dma_mask"] = bench_dma(torch)
     line.update(extra)
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         line["cpu_baseline"] = cpu_baseline()
