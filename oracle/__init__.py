@@ -41,9 +41,15 @@ something other than itself):
   dma.biased_sparse_attention                        — dense SDPA with an additive float mask,
                                                        shift invariance under a constant bias
   dma.dma_prefill                                    — planted heavy block selected everywhere
+  paged.append, paged.gather                         — appended summaries = min/max of the
+                                                       valid tokens; gathered tokens = appended
+  paged.page_scores, paged.decode                    — identity table with full pages = the
+                                                       contiguous decode oracle; all pages = dense
+                                                       SDPA over the valid prefix; -inf past the
+                                                       length; invariance under pool permutation
   backward.sparse_attention_backward                 — central finite differences of the
                                                        forward oracle, autograd of a dense masked
                                                        formulation, exact zeros off the mask,
                                                        softmax identities
 """
-from . import backward, decode, dma, nsa, prefill  # noqa: F401
+from . import backward, decode, dma, nsa, paged, prefill  # noqa: F401
