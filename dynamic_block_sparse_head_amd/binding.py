@@ -40,6 +40,11 @@ SIGNATURES = {
     "dsa_sparse_attn_prefill_ex": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
                                    + [_c_int] * 3 + [_vp, _c_float, _vp, _vp, _vp]),
     "dsa_dma_weights": (_c_int, [_c_int, _vp] + [_c_int] * 4 + [_vp, _vp, _c_int, _vp, _vp, _vp]),
+    "dsa_paged_append": (_c_int, [_c_int, _vp, _vp] + [_c_int] * 5 + [_vp, _vp, _c_int] + [_vp] * 5),
+    "dsa_paged_page_scores": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 6
+                              + [_vp, _vp, _c_int, _vp, _vp]),
+    "dsa_paged_decode": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 6
+                         + [_vp, _vp, _c_int, _vp, _vp, _c_int, _c_float, _vp, _c_size, _vp, _vp]),
     "dsa_page_minmax": (_c_int, [_c_int, _vp] + [_c_int] * 5 + [_vp, _vp, _vp]),
     "dsa_sparse_attn_decode_workspace_size": (_c_size, [_c_int] * 6),
     "dsa_sparse_attn_decode": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
@@ -196,6 +201,45 @@ def dsa_dma_weights(v, proj, gain, block, weights, block_scores=None, stream=Non
                                 block, _ptr(weights, "weights", torch.float32),
                                 _ptr(block_scores, "block_scores", torch.float32), _stream(stream))
     _check(st, "dsa_dma_weights")
+
+
+def dsa_paged_append(k_new, v_new, page_table, seq_len, k_pool, v_pool, kmin, kmax, stream=None):
+    """k_new, v_new [B,Hkv,D]; pools [n_pool,Hkv,page,D]; kmin/kmax [n_pool,Hkv,D];
+    page_table [B,max_pages] int32; seq_len [B] int32 (incremented)."""
+    B, Hkv, D = k_new.shape
+    n_pool, _, page, _ = k_pool.shape
+    st = load().dsa_paged_append(
+        _dtype_code(k_new), _ptr(k_new, "k_new"), _ptr(v_new, "v_new", k_new.dtype), B, Hkv, D, page,
+        page_table.shape[1], _ptr(page_table, "page_table", torch.int32),
+        _ptr(seq_len, "seq_len", torch.int32), n_pool, _ptr(k_pool, "k_pool", k_new.dtype),
+        _ptr(v_pool, "v_pool", k_new.dtype), _ptr(kmin, "kmin", k_new.dtype),
+        _ptr(kmax, "kmax", k_new.dtype), _stream(stream))
+    _check(st, "dsa_paged_append")
+
+
+def dsa_paged_page_scores(q, kmin, kmax, page, page_table, seq_len, scores, stream=None):
+    """q [B,Hq,D]; kmin/kmax [n_pool,Hkv,D] -> scores [B,Hkv,max_pages]."""
+    B, Hq, D = q.shape
+    n_pool, Hkv, _ = kmin.shape
+    st = load().dsa_paged_page_scores(
+        _dtype_code(q), _ptr(q, "q"), _ptr(kmin, "kmin", q.dtype), _ptr(kmax, "kmax", q.dtype), B, Hq,
+        Hkv, D, page, page_table.shape[1], _ptr(page_table, "page_table", torch.int32),
+        _ptr(seq_len, "seq_len", torch.int32), n_pool, _ptr(scores, "scores", torch.float32),
+        _stream(stream))
+    _check(st, "dsa_paged_page_scores")
+
+
+def dsa_paged_decode(q, k_pool, v_pool, page_table, seq_len, idx, count, scale, workspace, out,
+                     stream=None):
+    B, Hq, D = q.shape
+    n_pool, Hkv, page, _ = k_pool.shape
+    st = load().dsa_paged_decode(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
+        B, Hq, Hkv, D, page, page_table.shape[1], _ptr(page_table, "page_table", torch.int32),
+        _ptr(seq_len, "seq_len", torch.int32), n_pool, _ptr(idx, "idx", torch.int32),
+        _ptr(count, "count", torch.int32), idx.shape[-1], float(scale), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(out, "out", q.dtype), _stream(stream))
+    _check(st, "dsa_paged_decode")
 
 
 def dsa_page_minmax(k, page, kmin, kmax, stream=None):

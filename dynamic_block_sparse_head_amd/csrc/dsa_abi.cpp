@@ -367,6 +367,89 @@ int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const 
                     "dsa_sparse_attn_decode");
 }
 
+// shared checks of the paged-cache calls
+static int check_paged(int dtype, int B, int Hq, int Hkv, int D, int page, int max_pages,
+                       const int32_t* page_table, const int32_t* seq_len, int n_pool) {
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  REQUIRE(page == 32 || page == 64 || page == 128 || page == 256 || page == 512, DSA_E_UNSUPPORTED,
+          "page %d not supported (32, 64, 128, 256 or 512)", page);
+  REQUIRE(max_pages >= 1, DSA_E_ARG, "max_pages must be >= 1 (got %d)", max_pages);
+  REQUIRE(n_pool >= 1, DSA_E_ARG, "n_pool must be >= 1 (got %d)", n_pool);
+  REQUIRE((long long)n_pool * Hkv * page * D < (1ll << 40), DSA_E_ARG, "pool too large");
+  REQUIRE((long long)B * max_pages < (1ll << 31), DSA_E_ARG, "B*max_pages too large");
+  REQUIRE(page_table != nullptr && seq_len != nullptr, DSA_E_ARG,
+          "page_table and seq_len must not be NULL");
+  return DSA_OK;
+}
+
+int dsa_paged_append(int dtype, const void* k_new, const void* v_new, int B, int Hkv, int D,
+                     int page, int max_pages, const int32_t* page_table, int32_t* seq_len,
+                     int n_pool, void* k_pool, void* v_pool, void* kmin, void* kmax,
+                     void* stream) {
+  g_err.clear();
+  TRY(check_paged(dtype, B, Hkv, Hkv, D, page, max_pages, page_table, seq_len, n_pool));
+  REQUIRE_PTR(k_new);
+  REQUIRE_PTR(v_new);
+  REQUIRE_PTR(k_pool);
+  REQUIRE_PTR(v_pool);
+  REQUIRE_PTR(kmin);
+  REQUIRE_PTR(kmax);
+  return hip_status(dsa::launch_paged_append(k_new, v_new, B, Hkv, D, page, max_pages, page_table,
+                                             seq_len, n_pool, k_pool, v_pool, kmin, kmax,
+                                             static_cast<hipStream_t>(stream)),
+                    "dsa_paged_append");
+}
+
+int dsa_paged_page_scores(int dtype, const void* q, const void* kmin, const void* kmax, int B,
+                          int Hq, int Hkv, int D, int page, int max_pages,
+                          const int32_t* page_table, const int32_t* seq_len, int n_pool,
+                          float* scores, void* stream) {
+  g_err.clear();
+  TRY(check_paged(dtype, B, Hq, Hkv, D, page, max_pages, page_table, seq_len, n_pool));
+  const int G = Hq / Hkv;
+  REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, DSA_E_UNSUPPORTED,
+          "paged scores support 1, 2, 4 or 8 query heads per KV head (got %d)", G);
+  REQUIRE(max_pages <= 65535 * 256, DSA_E_UNSUPPORTED, "max_pages too large");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(kmin);
+  REQUIRE_PTR(kmax);
+  REQUIRE(scores != nullptr, DSA_E_ARG, "scores must not be NULL");
+  dsa::PageScoreArgs a{dtype, q, kmin, kmax, B, Hq, Hkv, max_pages, D, scores,
+                       page_table, seq_len, page, n_pool};
+  return hip_status(dsa::launch_page_scores(a, static_cast<hipStream_t>(stream)),
+                    "dsa_paged_page_scores");
+}
+
+int dsa_paged_decode(int dtype, const void* q, const void* k_pool, const void* v_pool, int B,
+                     int Hq, int Hkv, int D, int page, int max_pages, const int32_t* page_table,
+                     const int32_t* seq_len, int n_pool, const int32_t* idx, const int32_t* count,
+                     int idx_width, float scale, void* workspace, size_t workspace_bytes,
+                     void* out, void* stream) {
+  g_err.clear();
+  TRY(check_paged(dtype, B, Hq, Hkv, D, page, max_pages, page_table, seq_len, n_pool));
+  const int G = Hq / Hkv;
+  REQUIRE(G == 1 || G == 2 || G == 4 || G == 8, DSA_E_UNSUPPORTED,
+          "decode supports 1, 2, 4 or 8 query heads per KV head (got %d)", G);
+  REQUIRE(idx_width >= 1, DSA_E_ARG, "idx_width must be >= 1 (got %d)", idx_width);
+  REQUIRE(B * Hkv <= 65535, DSA_E_UNSUPPORTED, "B*Hkv must be at most 65535");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k_pool);
+  REQUIRE_PTR(v_pool);
+  REQUIRE_PTR(out);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  const size_t need = dsa::decode_workspace_bytes(B, Hq, Hkv, idx_width, page, D);
+  REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
+          "decode needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+  REQUIRE_PTR(workspace);
+  dsa::DecodeArgs a{q,     k_pool, v_pool, idx, count, B, Hq, Hkv, 0, D, idx_width, page,
+                    scale, static_cast<float*>(workspace), out, page_table, seq_len, max_pages,
+                    n_pool};
+  return hip_status(dsa::launch_decode(a, static_cast<hipStream_t>(stream)), "dsa_paged_decode");
+}
+
 int dsa_nsa_compress(int dtype, const void* k, const void* v, int B, int Hkv, int S, int D, int len,
                      int stride, void* ck, void* cv, void* stream) {
   g_err.clear();

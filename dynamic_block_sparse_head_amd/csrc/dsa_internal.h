@@ -28,10 +28,15 @@ hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s);
 struct PageScoreArgs {
   int dtype;
   const void* q;     // [B,Hq,D]
-  const void* kmin;  // [B,Hkv,nP,D]
+  const void* kmin;  // [B,Hkv,nP,D]; paged: [n_pool,Hkv,D]
   const void* kmax;
   int B, Hq, Hkv, nP, D;
-  float* scores;     // [B,Hkv,nP]
+  float* scores;     // [B,Hkv,nP]  (paged: nP = max_pages)
+  // paged (page_table != null): page p of sequence b is pool page
+  // page_table[b][p]; pages at or past ceil(seq_len[b]/page) score -inf
+  const int32_t* page_table;
+  const int32_t* seq_len;
+  int page, n_pool;
 };
 hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s);
 
@@ -97,9 +102,17 @@ struct DecodeArgs {
   float scale;
   float* partial;       // workspace
   void* out;            // [B,Hq,D] bf16
+  // paged cache (page_table != null): k, v are pools [n_pool, Hkv, page, D]
+  const int32_t* page_table;  // [B, max_pages] pool page of each logical page
+  const int32_t* seq_len;     // [B] tokens per sequence (L unused)
+  int max_pages, n_pool;
 };
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int idx_width, int page, int D);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_paged_append(const void* k_new, const void* v_new, int B, int Hkv, int D,
+                               int page, int max_pages, const int32_t* page_table,
+                               int32_t* seq_len, int n_pool, void* k_pool, void* v_pool,
+                               void* kmin, void* kmax, hipStream_t s);
 
 hipError_t launch_nsa_compress(const void* k, const void* v, int B, int Hkv, int S, int D,
                                int len, int stride, void* ck, void* cv, hipStream_t s);

@@ -41,14 +41,18 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
-// grid (nsplit, B*Hkv).  The chunk's tokens are walked in slabs of
+// grid (nsplit, B*Hkv).  PAGED: the cache is a pool [P, Hkv, PAGE, D]
+// shared by the batch, logical page p of sequence b lives in pool page
+// page_table[b][p], and only tokens below seq_len[b] exist (rows past it,
+// pages past it and pool ids out of range score -inf with zero values).
+// The chunk's tokens are walked in slabs of
 // kBatch * NG consecutive tokens; group tg of D/8 lanes takes rows
 // tg, tg + NG, ... of each slab, with an online softmax.  Page numbers are
 // uniform per row of a slab (pages are whole multiples of NG tokens), so
 // every load is a buffer load with a per-thread constant offset plus a
 // scalar row offset; the next slab's K and V are in flight while the
 // current one is used.  The NG group partials are merged in LDS in order.
-template <int D, int G, int PAGE>
+template <int D, int G, int PAGE, bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsplit, int ppsplit) {
   constexpr int CPR = D / 8;              // lanes per token row (8 dims each)
   constexpr int NG = kThreads / CPR;      // token groups
@@ -61,7 +65,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
   const int split = blockIdx.x, bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int cnt = min(a.count[bg], a.idx_width);
-  const int n_pages = a.L / PAGE;
+  const int len = PAGED ? a.seq_len[b] : a.L;        // tokens in this sequence's cache
+  const int n_pages = (len + PAGE - 1) / PAGE;
   const int p0 = split * ppsplit;
   const int np = max(0, min(cnt, p0 + ppsplit) - p0);
   const int ntok = np * PAGE;
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
   const int32_t* pages = a.idx + size_t(bg) * a.idx_width + p0;
 
   // K and V of this (sequence, KV head); a missing token reads zeros
-  const uint32_t kv_bytes = uint32_t(a.L) * D * 2;
+  const uint32_t kv_bytes = PAGED ? 0u : uint32_t(a.L) * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.L * D, kv_bytes);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -96,6 +101,21 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
     if (pg < 0 || pg >= n_pages) return 0xffffffffu;
     return uint32_t(pg * PAGE + t % PAGE) * uint32_t(D * 2);
   };
+  // PAGED: first element of row block u of slab sl in the pool (null: absent)
+  // and the logical position of its first row
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
+  auto pool_row = [&](int sl, int u, int& tok0) -> size_t {
+    const int t = sl * SLAB + u * NG;
+    tok0 = 0x7fffffff;
+    if (t >= ntok) return ~size_t(0);
+    const int pg = pages[t / PAGE];
+    if (pg < 0 || pg >= n_pages) return ~size_t(0);
+    const int phys = a.page_table[size_t(b) * a.max_pages + pg];
+    if (phys < 0 || phys >= a.n_pool) return ~size_t(0);
+    tok0 = pg * PAGE + t % PAGE;
+    return ((size_t(phys) * a.Hkv + g) * PAGE + t % PAGE) * D;
+  };
 
   float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -108,14 +128,25 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
 
   struct Batch {
     u32x4 k[kBatch], v[kBatch];
-    uint32_t base[kBatch];
+    uint32_t base[kBatch];   // contiguous: row offset; PAGED: 1 if this lane's row exists
   };
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
   auto fetch = [&](int sl, Batch& bt) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      bt.base[u] = row_base(sl, u);
-      bt.k[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, bt.base[u], 0);
-      bt.v[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, bt.base[u], 0);
+      if constexpr (PAGED) {
+        int tok0;
+        const size_t e = pool_row(sl, u, tok0);
+        const bool ok = e != ~size_t(0) && tok0 + tg < len;   // the row exists and is written
+        const size_t off = ok ? e + tg * D + dc * 8 : 0;
+        bt.base[u] = ok ? 1u : 0xffffffffu;
+        bt.k[u] = *reinterpret_cast<const u32x4*>(kpool + off);
+        bt.v[u] = *reinterpret_cast<const u32x4*>(vpool + off);
+      } else {
+        bt.base[u] = row_base(sl, u);
+        bt.k[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, bt.base[u], 0);
+        bt.v[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, bt.base[u], 0);
+      }
     }
   };
   auto consume = [&](const Batch& bt) {
@@ -150,7 +181,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       float vf[8];
-      unpack8(bt.v[u], vf);
+      // a missing row contributes nothing: its (pool) values may be anything
+      unpack8(PAGED && bt.base[u] == 0xffffffffu ? zero4 : bt.v[u], vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float p = fast_exp2(sc[u][h] - (m[h] == -__builtin_inff() ? 0.f : m[h]));
@@ -246,7 +278,10 @@ template <int D, int G, int PAGE>
 hipError_t run(const DecodeArgs& a, hipStream_t s) {
   const int pps = pages_per_split(PAGE);
   const int nsplit = (a.idx_width + pps - 1) / pps;
-  k_decode_split<D, G, PAGE><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
+  if (a.page_table)
+    k_decode_split<D, G, PAGE, true><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
+  else
+    k_decode_split<D, G, PAGE, false><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
   k_decode_merge<D><<<a.B * a.Hq, D, 0, s>>>(a.partial, nsplit, static_cast<uint16_t*>(a.out));
   return hipGetLastError();
 }
@@ -272,7 +307,54 @@ hipError_t run_d(const DecodeArgs& a, hipStream_t s) {
   }
 }
 
+// Append one token per sequence to a paged cache: grid B.  Token
+// t = seq_len[b] goes to row t % page of pool page page_table[b][t / page];
+// its key is folded into that page's element-wise min/max (the page's first
+// token sets them); then seq_len[b] = t + 1.  A sequence whose page slot or
+// pool id is out of range is left unchanged.
+__global__ __launch_bounds__(kThreads) void k_paged_append(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int Hkv, int D,
+    int page, int max_pages, const int32_t* __restrict__ page_table, int32_t* seq_len, int n_pool,
+    uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool, uint16_t* __restrict__ kmin,
+    uint16_t* __restrict__ kmax) {
+  const int b = blockIdx.x;
+  const int t = seq_len[b];
+  const int p = t / page, r = t % page;
+  const bool ok = t >= 0 && p < max_pages;
+  const int phys = ok ? page_table[size_t(b) * max_pages + p] : -1;
+  if (phys < 0 || phys >= n_pool) return;   // whole workgroup
+  for (int e = threadIdx.x; e < Hkv * D; e += kThreads) {
+    const int g = e / D, d = e % D;
+    const uint16_t kb = k_new[(size_t(b) * Hkv + g) * D + d];
+    const size_t row = ((size_t(phys) * Hkv + g) * page + r) * D + d;
+    k_pool[row] = kb;
+    v_pool[row] = v_new[(size_t(b) * Hkv + g) * D + d];
+    const size_t m = (size_t(phys) * Hkv + g) * D + d;
+    if (r == 0) {
+      kmin[m] = kb;
+      kmax[m] = kb;
+    } else {
+      const float x = bf16_to_f32(kb);
+      if (x < bf16_to_f32(kmin[m])) kmin[m] = kb;
+      if (x > bf16_to_f32(kmax[m])) kmax[m] = kb;
+    }
+  }
+  __syncthreads();   // every thread has read seq_len[b]
+  if (threadIdx.x == 0) seq_len[b] = t + 1;
+}
+
 }  // namespace
+
+hipError_t launch_paged_append(const void* k_new, const void* v_new, int B, int Hkv, int D,
+                               int page, int max_pages, const int32_t* page_table,
+                               int32_t* seq_len, int n_pool, void* k_pool, void* v_pool,
+                               void* kmin, void* kmax, hipStream_t s) {
+  k_paged_append<<<B, kThreads, 0, s>>>(
+      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), Hkv, D, page,
+      max_pages, page_table, seq_len, n_pool, static_cast<uint16_t*>(k_pool),
+      static_cast<uint16_t*>(v_pool), static_cast<uint16_t*>(kmin), static_cast<uint16_t*>(kmax));
+  return hipGetLastError();
+}
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int idx_width, int page, int D) {
   (void)Hkv;

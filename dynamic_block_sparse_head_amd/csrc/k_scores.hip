@@ -240,14 +240,20 @@ __global__ __launch_bounds__(kThreads) void k_page_scores(const T* __restrict__ 
 // bound loads in flight while the current one is reduced; no LDS, no barrier.
 constexpr int kIters = 4;
 
-template <int G>
+//
+// PAGED: the summaries live in a pool [n_pool, Hkv, D]; logical page p of
+// sequence b reads pool page page_table[b][p], and pages at or past
+// ceil(seq_len[b] / page) (or naming no pool page) score -inf.
+template <int G, bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ kmin,
                                                                const uint16_t* __restrict__ kmax,
                                                                int Hq, int Hkv, int nP, int D,
-                                                               float* __restrict__ scores) {
+                                                               float* __restrict__ scores,
+                                                               PageScoreArgs pa) {
   const int bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
+  const int npg = PAGED ? min(nP, (pa.seq_len[b] + pa.page - 1) / pa.page) : nP;
   const int lpp = D / 8;
   const int ppw = kThreads / lpp;
   const int sub = threadIdx.x % lpp;
@@ -265,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* _
     }
   }
   u32x4 rlo[2][kPagesPerThread], rhi[2][kPagesPerThread];
+  bool live[2][kPagesPerThread];   // the page exists (always, unless PAGED)
   auto page_of = [&](int it, int t) {
     return ((blockIdx.x * kIters + it) * kPagesPerThread + t) * ppw + int(threadIdx.x) / lpp;
   };
@@ -272,8 +279,17 @@ __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* _
 #pragma unroll
     for (int t = 0; t < kPagesPerThread; ++t) {
       const int p = page_of(it, t);
-      if (p < nP) {
-        const size_t off = (size_t(bg) * nP + p) * D + sub * 8;
+      live[buf][t] = false;
+      if (p < npg) {
+        size_t off;
+        if constexpr (PAGED) {
+          const int phys = pa.page_table[size_t(b) * nP + p];
+          if (phys < 0 || phys >= pa.n_pool) continue;
+          off = (size_t(phys) * Hkv + g) * D + sub * 8;
+        } else {
+          off = (size_t(bg) * nP + p) * D + sub * 8;
+        }
+        live[buf][t] = true;
         rlo[buf][t] = *reinterpret_cast<const u32x4*>(kmin + off);
         rhi[buf][t] = *reinterpret_cast<const u32x4*>(kmax + off);
       }
@@ -287,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* _
     for (int t = 0; t < kPagesPerThread; ++t) {
       const int p = page_of(it, t);
       double acc = 0.0;
-      if (p < nP) {
+      if (live[it & 1][t]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lo = (e & 1) ? bf16hi(rlo[it & 1][t][e / 2]) : bf16lo(rlo[it & 1][t][e / 2]);
@@ -297,7 +313,8 @@ __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* _
         }
       }
       for (int o = lpp / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
-      if (p < nP && sub == 0) scores[size_t(bg) * nP + p] = float(acc);
+      if (p < nP && sub == 0)
+        scores[size_t(bg) * nP + p] = live[it & 1][t] ? float(acc) : -__builtin_inff();
     }
   }
 }
@@ -380,12 +397,18 @@ hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s) {
     const auto* q = static_cast<const uint16_t*>(a.q);
     const auto* lo = static_cast<const uint16_t*>(a.kmin);
     const auto* hi = static_cast<const uint16_t*>(a.kmax);
+#define DSA_PS(GG)                                                                          \
+  (a.page_table ? k_page_scores_bf16<GG, true><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, \
+                                                                         a.nP, a.D, a.scores, a) \
+                : k_page_scores_bf16<GG, false><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, \
+                                                                          a.nP, a.D, a.scores, a))
     switch (G) {
-      case 1: k_page_scores_bf16<1><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
-      case 2: k_page_scores_bf16<2><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
-      case 4: k_page_scores_bf16<4><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
-      default: k_page_scores_bf16<8><<<grid, kThreads, 0, s>>>(q, lo, hi, a.Hq, a.Hkv, a.nP, a.D, a.scores); break;
+      case 1: DSA_PS(1); break;
+      case 2: DSA_PS(2); break;
+      case 4: DSA_PS(4); break;
+      default: DSA_PS(8); break;
     }
+#undef DSA_PS
     return hipGetLastError();
   }
   const int ppb = kThreads / (a.D / 8) * kPagesPerThread;

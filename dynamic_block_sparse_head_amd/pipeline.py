@@ -151,6 +151,42 @@ class DecodePlan:
         return self.out
 
 
+class PagedDecodePlan:
+    """Decode over a paged KV pool shared by a batch of sequences of
+    different lengths: page bounds through the page table -> top pages ->
+    attention over their written tokens ([SF] §二-§四)."""
+
+    def __init__(self, B, Hq, Hkv, D, page, max_pages, topk, device, scale=None):
+        self.B, self.Hq, self.Hkv, self.D, self.page = B, Hq, Hkv, D, page
+        self.max_pages, self.topk = max_pages, topk
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
+        self.scores = _empty((B, Hkv, 1, max_pages), torch.float32, device)
+        self.idx = _empty((B, Hkv, 1, topk), torch.int32, device)
+        self.count = _empty((B, Hkv, 1), torch.int32, device)
+        ws = L.dsa_sparse_attn_decode_workspace_size(B, Hq, Hkv, topk, page, D)
+        self.ws = _empty((ws,), torch.uint8, device)
+        self.out = _empty((B, Hq, D), torch.bfloat16, device)
+
+    def append(self, k_new, v_new, page_table, seq_len, k_pool, v_pool, kmin, kmax):
+        L.dsa_paged_append(k_new, v_new, page_table, seq_len, k_pool, v_pool, kmin, kmax)
+
+    def score(self, q, kmin, kmax, page_table, seq_len):
+        L.dsa_paged_page_scores(q, kmin, kmax, self.page, page_table, seq_len, self.scores)
+
+    def select(self):
+        L.dsa_topk_select(self.scores, self.topk, 0, False, self.idx, self.count)
+
+    def attend(self, q, k_pool, v_pool, page_table, seq_len):
+        L.dsa_paged_decode(q, k_pool, v_pool, page_table, seq_len, self.idx, self.count, self.scale,
+                           self.ws, self.out)
+
+    def run(self, q, k_pool, v_pool, kmin, kmax, page_table, seq_len):
+        self.score(q, kmin, kmax, page_table, seq_len)
+        self.select()
+        self.attend(q, k_pool, v_pool, page_table, seq_len)
+        return self.out
+
+
 class NSAPlan:
     """Compressed branch (+ block scores) -> top-k blocks -> selected branch;
     sliding branch; gated combine ([NSA] §03)."""

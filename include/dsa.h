@@ -233,6 +233,50 @@ int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const 
                            void* out, void* stream);
 
 /*
+ * Paged KV cache for serving ([SF] §二-§四: the whole cache is kept and a
+ * decode step reads only the pages it selects; here the cache of a whole
+ * batch lives in one pool of pages).
+ *
+ * Layout: k_pool, v_pool [n_pool, Hkv, page, D] bf16; kmin, kmax
+ * [n_pool, Hkv, D] bf16 (per pool page, the element-wise min / max of the
+ * keys written to it so far); page_table [B, max_pages] int32: logical page
+ * p of sequence b (tokens p*page .. p*page+page-1) is pool page
+ * page_table[b*max_pages + p]; seq_len [B] int32: tokens of sequence b.
+ * Pool pages are owned by the caller; two sequences must not share one.
+ *
+ * dsa_paged_append: writes token seq_len[b] of every sequence (k_new, v_new
+ * [B,Hkv,D]) into its page, folds its key into the page's kmin/kmax (the
+ * page's first token sets them) and increments seq_len[b].  A sequence whose
+ * page slot (>= max_pages) or pool id (outside [0, n_pool)) is out of range
+ * is left unchanged.
+ *
+ * dsa_paged_page_scores: scores [B,Hkv,max_pages] float32, the page bound of
+ * dsa_block_scores(DSA_SCORE_PAGE_BOUND) for logical pages below
+ * ceil(seq_len[b]/page) (read through the page table, float64 sums), -inf
+ * for the rest.  Feed it to dsa_topk_select (causal = 0, n_local = 0).
+ *
+ * dsa_paged_decode: as dsa_sparse_attn_decode over the pool: idx
+ * [B,Hkv,idx_width] logical pages, count [B,Hkv]; only tokens below
+ * seq_len[b] are attended, selected pages past the length hold nothing.
+ * Workspace: dsa_sparse_attn_decode_workspace_size(B, Hq, Hkv, idx_width,
+ * page, D) bytes.  bf16 only; page in {32,64,128,256,512}, Hq/Hkv in
+ * {1,2,4,8}.
+ */
+int dsa_paged_append(int dtype, const void* k_new, const void* v_new, int B, int Hkv, int D,
+                     int page, int max_pages, const int32_t* page_table, int32_t* seq_len,
+                     int n_pool, void* k_pool, void* v_pool, void* kmin, void* kmax,
+                     void* stream);
+int dsa_paged_page_scores(int dtype, const void* q, const void* kmin, const void* kmax, int B,
+                          int Hq, int Hkv, int D, int page, int max_pages,
+                          const int32_t* page_table, const int32_t* seq_len, int n_pool,
+                          float* scores, void* stream);
+int dsa_paged_decode(int dtype, const void* q, const void* k_pool, const void* v_pool, int B,
+                     int Hq, int Hkv, int D, int page, int max_pages, const int32_t* page_table,
+                     const int32_t* seq_len, int n_pool, const int32_t* idx, const int32_t* count,
+                     int idx_width, float scale, void* workspace, size_t workspace_bytes,
+                     void* out, void* stream);
+
+/*
  * Compressed keys / values for the coarse branch ([NSA] §03 "compressed
  * attention": a quick scan of summaries of the history).
  * ck, cv [B,Hkv,n_cmp,D] with n_cmp = (S-len)/stride + 1:

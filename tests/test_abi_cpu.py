@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -144,6 +144,32 @@ def test_dma_weights_validation():
     assert f(*a) == L.DSA_E_ARG
     a = list(args); a[8] = 33
     assert f(*a) == L.DSA_E_UNSUPPORTED
+
+
+def test_paged_validation():
+    lib = L.load()
+    app = lib.dsa_paged_append
+    args = [1, FAKE, FAKE, 4, 8, 128, 64, 100, FAKE, FAKE, 500, FAKE, FAKE, FAKE, FAKE, None]
+    a = list(args); a[0] = 0
+    assert app(*a) == L.DSA_E_UNSUPPORTED                          # float32
+    a = list(args); a[6] = 48
+    assert app(*a) == L.DSA_E_UNSUPPORTED                          # page 48
+    a = list(args); a[9] = None
+    assert app(*a) == L.DSA_E_ARG and "seq_len" in _err()
+    a = list(args); a[10] = 0
+    assert app(*a) == L.DSA_E_ARG                                  # empty pool
+    dec = lib.dsa_paged_decode
+    ws = lib.dsa_sparse_attn_decode_workspace_size(4, 32, 8, 10, 64, 128)
+    args = [1, FAKE, FAKE, FAKE, 4, 32, 8, 128, 64, 100, FAKE, FAKE, 500, FAKE, FAKE, 10, 0.1, FAKE,
+            ws, FAKE, None]
+    a = list(args); a[18] = ws - 4
+    assert dec(*a) == L.DSA_E_WORKSPACE
+    a = list(args); a[5] = 48
+    assert dec(*a) == L.DSA_E_UNSUPPORTED                          # G = 6
+    a = list(args); a[13] = None
+    assert dec(*a) == L.DSA_E_ARG
+    sc = lib.dsa_paged_page_scores
+    assert sc(1, FAKE, FAKE, FAKE, 4, 32, 8, 128, 64, 100, None, FAKE, 500, FAKE, None) == L.DSA_E_ARG
 
 
 def test_backward_validation():
