@@ -9,11 +9,11 @@ carries the attention kernel's roofline (effective FLOPs on selected blocks
 against the bf16 MFMA peak), the decode path's HBM rate on the 128K-page
 workload, the long-prefill and three-branch workloads, the backward of the
 headline attention, the per-query-head selection and value-driven mask
-variants, and the CPU oracle timed on a bounded sample of the headline
-workload.
+variants, decode over a paged pool with variable lengths, and the CPU oracle
+timed on a bounded sample of the headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|long|nsa|backward|per_head|dma]
+                    [--only prefill|decode|long|nsa|backward|per_head|dma|paged]
                     [--copy-calibration]
 """
 from __future__ import annotations
@@ -208,6 +208,86 @@ def bench_decode(torch, iters=20, n_query_sets=4):
             "page_metadata_build_ms": round(t_meta, 3)}
 
 
+def bench_paged(torch, iters=20, n_query_sets=4):
+    """Serving decode over a paged pool: 16 sequences whose lengths are drawn
+    uniformly in [64K, 128K] tokens share one pool of 64-token pages placed in
+    random order; per step: page bounds through the page table, top 102 pages
+    per (sequence, KV head), attention over their written tokens.  The LLC is
+    swept by a 1 GiB read between steps, as for the contiguous decode."""
+    import numpy as np
+    from dynamic_block_sparse_head_amd import binding as L
+    from dynamic_block_sparse_head_amd import configs
+    from dynamic_block_sparse_head_amd.pipeline import PagedDecodePlan
+
+    c = configs.DECODE_128K
+    rng = np.random.default_rng(2025)
+    lens = rng.integers(c.L // 2, c.L + 1, size=c.B)
+    npg = -(-lens // c.page)
+    max_pages = int(npg.max())
+    n_pool = int(npg.sum()) + 8
+    perm = rng.permutation(n_pool)
+    table = np.zeros((c.B, max_pages), dtype=np.int32)
+    off = 0
+    for b in range(c.B):
+        table[b, :npg[b]] = perm[off:off + npg[b]]
+        off += npg[b]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    shape = (n_pool, c.Hkv, c.page, c.D)
+    k_pool = torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
+    v_pool = torch.randn(shape, generator=g, device="cuda", dtype=torch.bfloat16)
+    # page summaries of the whole pool: one sequence of n_pool * Hkv pages
+    kmin = torch.empty((n_pool, c.Hkv, c.D), dtype=torch.bfloat16, device="cuda")
+    kmax = torch.empty_like(kmin)
+    L.dsa_page_minmax(k_pool.view(1, 1, -1, c.D), c.page, kmin.view(1, 1, -1, c.D),
+                      kmax.view(1, 1, -1, c.D))
+    table_d = torch.from_numpy(table).to("cuda")
+    seq = torch.from_numpy(lens.astype(np.int32)).to("cuda")
+    plan = PagedDecodePlan(c.B, c.Hq, c.Hkv, c.D, c.page, max_pages, c.topk, "cuda")
+    qs = [torch.randn((c.B, c.Hq, c.D), generator=g, device="cuda", dtype=torch.bfloat16)
+          for _ in range(n_query_sets)]
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+    sel_bytes = []
+    for q in qs:                       # bytes of the written tokens of the selected pages
+        plan.run(q, k_pool, v_pool, kmin, kmax, table_d, seq)
+        idx, cnt = plan.idx.cpu().numpy()[:, :, 0], plan.count.cpu().numpy()[:, :, 0]
+        tot = 0
+        for b in range(c.B):
+            for h in range(c.Hkv):
+                for p in idx[b, h, :cnt[b, h]]:
+                    if 0 <= p < npg[b]:
+                        tot += min(c.page, int(lens[b]) - int(p) * c.page)
+        sel_bytes.append(tot * c.D * 2 * 2)
+    t_step = t_attn = 0.0
+    for it in range(iters):
+        q = qs[it % n_query_sets]
+        flush.max()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(s)
+        plan.score(q, kmin, kmax, table_d, seq)
+        plan.select()
+        e[1].record(s)
+        plan.attend(q, k_pool, v_pool, table_d, seq)
+        e[2].record(s)
+        e[2].synchronize()
+        t_step += e[0].elapsed_time(e[2])
+        t_attn += e[1].elapsed_time(e[2])
+    # appending one token to every sequence (each call grows seq by one)
+    kn = torch.randn((c.B, c.Hkv, c.D), generator=g, device="cuda", dtype=torch.bfloat16)
+    ms_append = _timed(lambda: plan.append(kn, kn, table_d, seq, k_pool, v_pool, kmin, kmax), 8, torch)
+    ms_step, ms_attn = t_step / iters, t_attn / iters
+    nbytes = float(np.mean(sel_bytes))
+    gbs = nbytes / (ms_attn * 1e-3) / 1e9
+    del k_pool, v_pool, kmin, kmax, plan, flush, qs
+    return {"workload": f"paged pool: B=16 lengths U[64K,128K] (total {int(lens.sum())} tokens), "
+                        f"page=64 in random pool order, Hq=32 Hkv=8 D=128, top {c.topk} pages",
+            "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.B / (ms_step * 1e-3), 1),
+            "attn_ms": round(ms_attn, 4), "selected_bytes": int(nbytes),
+            "attn_hbm_gbs": round(gbs, 1), "attn_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "append_us": round(ms_append * 1e3, 2)}
+
+
 def bench_per_head(torch, iters=10):
     """The 16K prefill path with per-query-head selection (every query head
     ranks blocks by its own pooled score and keeps its own list): scores,
@@ -372,7 +452,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward", "per_head",
-                                       "dma"], default=None)
+                                       "dma", "paged"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -436,6 +516,8 @@ def main():
         extra["per_head_selection"] = bench_per_head(torch)
     if args.only in (None, "dma"):
         extra["dma_mask"] = bench_dma(torch)
+    if args.only in (None, "paged"):
+        extra["paged_decode"] = bench_paged(torch)
     line.update(extra)
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         line["cpu_baseline"] = cpu_baseline()

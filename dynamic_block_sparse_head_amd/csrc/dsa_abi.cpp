@@ -319,7 +319,6 @@ int dsa_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int 
   REQUIRE(page >= 1, DSA_E_ARG, "page must be >= 1 (got %d)", page);
   REQUIRE(L >= page && L % page == 0, DSA_E_ARG, "L (%d) must be a positive multiple of page (%d)",
           L, page);
-  REQUIRE(L / page <= 65535, DSA_E_UNSUPPORTED, "at most 65535 pages per sequence");
   REQUIRE_PTR(k);
   REQUIRE_PTR(kmin);
   REQUIRE_PTR(kmax);
