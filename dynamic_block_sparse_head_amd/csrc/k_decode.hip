@@ -6,7 +6,7 @@
 // streamed with coalesced 16-byte loads.
 //
 // Work split: every (sequence, KV group) row of selected pages is cut into
-// chunks of up to 512 tokens' worth of pages; one workgroup per chunk
+// chunks of about 512 tokens' worth of pages; one workgroup per chunk
 // computes, for the group's G query heads, the chunk's running max, exp-sum
 // and unnormalised weighted value sum.  A merge kernel combines the chunks
 // of each (sequence, head) in chunk order (deterministic, no atomics).
@@ -21,6 +21,28 @@ constexpr int kMaxTok = 512;   // tokens per workgroup: 8 pages of 64, 4 of 128,
 constexpr int kBatch = 4;      // token rows per thread per pipeline stage
 
 int pages_per_split(int page) { return page >= kMaxTok ? 1 : kMaxTok / page; }
+
+// Chunks per (sequence, KV head) row of selected pages: about kMaxTok tokens
+// each, with the count nudged so the grid fills whole rounds of the chip's
+// concurrent workgroups (256 CUs x 2 at this kernel's register use): a
+// partly filled last round would leave most CUs idle while its few chunks
+// stream.  The row's pages are then spread evenly over its chunks.
+constexpr int kSlots = 256 * 2;
+int split_count(int rows, int idx_width, int page) {
+  const int pps = pages_per_split(page);
+  const int base = (idx_width + pps - 1) / pps;
+  int best = base;
+  long long best_cost = -1;
+  for (int n = max(1, base - base / 4); n <= base + base / 4 + 1; ++n) {
+    const long long rounds = (static_cast<long long>(rows) * n + kSlots - 1) / kSlots;
+    const long long cost = rounds * ((idx_width + n - 1) / n);   // rounds x pages per chunk
+    if (best_cost < 0 || cost < best_cost) {
+      best = n;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 __device__ __forceinline__ void unpack8(const u32x4& w, float* f) {
 #pragma unroll
@@ -53,7 +75,7 @@ __device__ __forceinline__ float row_sum(float x) {
 // scalar row offset; the next slab's K and V are in flight while the
 // current one is used.  The NG group partials are merged in LDS in order.
 template <int D, int G, int PAGE, bool PAGED>
-__global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsplit, int ppsplit) {
+__global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsplit) {
   constexpr int CPR = D / 8;              // lanes per token row (8 dims each)
   constexpr int NG = kThreads / CPR;      // token groups
   constexpr int SLAB = kBatch * NG;       // tokens per pipeline stage
@@ -67,8 +89,8 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
   const int cnt = min(a.count[bg], a.idx_width);
   const int len = PAGED ? a.seq_len[b] : a.L;        // tokens in this sequence's cache
   const int n_pages = (len + PAGE - 1) / PAGE;
-  const int p0 = split * ppsplit;
-  const int np = max(0, min(cnt, p0 + ppsplit) - p0);
+  const int p0 = int((static_cast<long long>(split) * max(cnt, 0)) / nsplit);
+  const int np = int((static_cast<long long>(split + 1) * max(cnt, 0)) / nsplit) - p0;
   const int ntok = np * PAGE;
   const int dc = threadIdx.x % CPR, tg = threadIdx.x / CPR;
   const float c = a.scale * kLog2e;
@@ -276,12 +298,11 @@ __global__ __launch_bounds__(D) void k_decode_merge(const float* __restrict__ pa
 
 template <int D, int G, int PAGE>
 hipError_t run(const DecodeArgs& a, hipStream_t s) {
-  const int pps = pages_per_split(PAGE);
-  const int nsplit = (a.idx_width + pps - 1) / pps;
+  const int nsplit = split_count(a.B * a.Hkv, a.idx_width, PAGE);
   if (a.page_table)
-    k_decode_split<D, G, PAGE, true><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
+    k_decode_split<D, G, PAGE, true><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit);
   else
-    k_decode_split<D, G, PAGE, false><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit, pps);
+    k_decode_split<D, G, PAGE, false><<<dim3(nsplit, a.B * a.Hkv), kThreads, 0, s>>>(a, nsplit);
   k_decode_merge<D><<<a.B * a.Hq, D, 0, s>>>(a.partial, nsplit, static_cast<uint16_t*>(a.out));
   return hipGetLastError();
 }
@@ -357,9 +378,7 @@ hipError_t launch_paged_append(const void* k_new, const void* v_new, int B, int 
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int idx_width, int page, int D) {
-  (void)Hkv;
-  const int pps = pages_per_split(page);
-  const size_t nsplit = (size_t(idx_width) + pps - 1) / pps;
+  const size_t nsplit = split_count(B * Hkv, idx_width, page);
   return size_t(B) * Hq * nsplit * (D + 2) * sizeof(float);
 }
 
