@@ -33,6 +33,11 @@ something other than itself):
                                                        the overlap-fraction mapping itself is a
                                                        reading, so its split rule is only pinned
                                                        by those two (documented as partly pinned)
+  nsa.cmp_token_scores                               — hand example (golden file), row mass = 1,
+                                                       block mean = cmp_block_scores
+  prefill.select_blocks(row_block)                   — lexsort brute force per token with ties
+  nsa.token_sparse_attention                         — dense SDPA with the explicit per-row
+                                                       mask; all blocks selected = dense causal
   nsa.window_attention                               — W >= S dense limit, W = 1 identity
   nsa.combine                                        — closed form when branches coincide
   dma.softplus, dma.dynamic_weights                  — softplus identities and limits, v = 0 and

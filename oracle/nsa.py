@@ -17,6 +17,11 @@ Readings taken where the page is silent:
     in proportion to the overlap, summed over the block's rows and the
     group's heads, and divided by (rows x heads) so scores lie in [0, 1];
     candidates are blocks j <= i, top-k, nothing forced;
+  * per-token selection (the finer granularity of the original method):
+    every query token ranks the blocks for its own KV group, with the same
+    overlap split of its branch-1 probabilities, averaged over the group's
+    heads; its candidates are blocks j <= t // sel_block; all heads of the
+    group attend to that token's blocks (keys <= t);
   * the sliding branch sees keys t-W+1 .. t;
   * gates: out = sum over branches of sigmoid(z_b) * o_b (no normalisation).
 """
@@ -127,6 +132,55 @@ def cmp_block_scores(probs, Hkv, length, stride, sel_block, S, q_blocks=None):
     return out
 
 
+def cmp_token_scores(probs, Hkv, length, stride, sel_block, S):
+    """Per-token selection scores: score[b, g, t, j] is the branch-1
+    probability mass of row t inside key block j (each summary split in
+    proportion to its overlap with the block), averaged over the query heads
+    of group g, so that each row of a token that sees a summary sums to 1.
+
+    probs from cmp_attention [B,Hq,R,n] (R rows in the order evaluated).
+    Returns [B,Hkv,R,nB].
+    """
+    B, Hq, R, n = probs.shape
+    G = Hq // Hkv
+    nB = -(-S // sel_block)
+    w = overlap_weights(n, length, stride, sel_block, nB)
+    out = np.zeros((B, Hkv, R, nB))
+    for b in range(B):
+        for g in range(Hkv):
+            mass = probs[b, g * G:(g + 1) * G].sum(axis=0)   # [R, n]
+            out[b, g] = (mass @ w) / G
+    return out
+
+
+def token_sparse_attention(q, k, v, idx, count, block, scale, rows=None):
+    """Selected branch with per-token lists: row t of every query head of
+    group g attends to the keys s <= t inside the blocks idx[b, g, t, :count].
+
+    q [B,Hq,S,D]; k/v [B,Hkv,S,D]; idx [B,Hkv,S,W]; count [B,Hkv,S].  rows:
+    optional positions to evaluate (others NaN).  Returns out, lse.
+    """
+    from .prefill import visible_keys
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    rows = range(S) if rows is None else rows
+    out = np.full((B, Hq, S, D), np.nan)
+    lse = np.full((B, Hq, S), np.nan)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for t in rows:
+                keys = visible_keys(idx[b, g, t], int(count[b, g, t]), block, S)
+                o, l = masked_softmax_attention(q[b, h, t][None, :], np.array([t]), keys,
+                                                k[b, g], v[b, g], scale)
+                out[b, h, t] = o[0]
+                lse[b, h, t] = l[0]
+    return out, lse
+
+
 def window_attention(q, k, v, window, scale, rows=None):
     """Branch 3: row t attends to keys max(0, t-window+1) .. t."""
     q = np.asarray(q, dtype=np.float64)
@@ -166,18 +220,24 @@ def combine(o_cmp, o_sel, o_win, z):
             + gate[..., 2:3] * np.asarray(o_win, dtype=np.float64))
 
 
-def forward(q, k, v, z, length, stride, sel_block, sel_k, window, scale):
-    """All three branches and the gated combine ([NSA] §03), in order."""
+def forward(q, k, v, z, length, stride, sel_block, sel_k, window, scale, per_token=False):
+    """All three branches and the gated combine ([NSA] §03), in order.
+    per_token: rank blocks per query token instead of per query block."""
     from .prefill import select_blocks, sparse_attention
     S = q.shape[2]
     ck = compress(k, length, stride)
     cv = compress(v, length, stride)
     o1, lse1, p1 = cmp_attention(q, ck, cv, length, stride, scale)
-    scores = cmp_block_scores(p1, k.shape[1], length, stride, sel_block, S)
+    if per_token:
+        scores = cmp_token_scores(p1, k.shape[1], length, stride, sel_block, S)
+        idx, cnt = select_blocks(scores, sel_k, 0, causal=True, row_block=sel_block)
+        o2, _ = token_sparse_attention(q, k, v, idx, cnt, sel_block, scale)
+    else:
+        scores = cmp_block_scores(p1, k.shape[1], length, stride, sel_block, S)
+        # causal candidates are blocks j <= i: no forced window (n_local = 0)
+        idx, cnt = select_blocks(scores, sel_k, 0, causal=True)
+        o2, _ = sparse_attention(q, k, v, idx, cnt, sel_block, scale)
     nB = scores.shape[-1]
-    # causal candidates are blocks j <= i: no forced window (n_local = 0)
-    idx, cnt = select_blocks(scores, sel_k, 0, causal=True)
-    o2, _ = sparse_attention(q, k, v, idx, cnt, sel_block, scale)
     o3, _ = window_attention(q, k, v, window, scale)
     out = combine(o1, o2, o3, z)
     return {"ck": ck, "cv": cv, "o_cmp": o1, "lse_cmp": lse1, "scores": scores,

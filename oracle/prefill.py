@@ -83,11 +83,13 @@ def _rank_key(score: float, j: int):
     return (1, 0.0, j) if math.isnan(score) else (0, -score, j)
 
 
-def select_blocks(scores: np.ndarray, k: int, n_local: int, causal: bool):
+def select_blocks(scores: np.ndarray, k: int, n_local: int, causal: bool, row_block: int = 1):
     """Top-k selection plus the local window, per score row.
 
-    scores [..., nQ, nK].  For row i (causal): candidates are key blocks
-    0 .. i - n_local, the window is blocks max(0, i-n_local+1) .. i.
+    scores [..., nQ, nK].  For row r (causal) with i = r // row_block (rows
+    are query blocks when row_block = 1, tokens of `row_block`-token blocks
+    otherwise): candidates are key blocks 0 .. i - n_local, the window is
+    blocks max(0, i-n_local+1) .. i.
     Non-causal rows (decode, one row per group): candidates are blocks
     0 .. nK-1-n_local, the window is the last n_local blocks.
     Candidates are ordered by (score descending, index ascending) and the
@@ -102,8 +104,9 @@ def select_blocks(scores: np.ndarray, k: int, n_local: int, causal: bool):
     idx = np.full(lead + (nQ, width), -1, dtype=np.int32)
     cnt = np.zeros(lead + (nQ,), dtype=np.int32)
     for pos in np.ndindex(*lead) if lead else [()]:
-        for i in range(nQ):
-            row = scores[pos + (i,)]
+        for r in range(nQ):
+            row = scores[pos + (r,)]
+            i = r // row_block
             if causal:
                 last = i - n_local
                 window = list(range(max(0, i - n_local + 1), i + 1))
@@ -115,8 +118,8 @@ def select_blocks(scores: np.ndarray, k: int, n_local: int, causal: bool):
                 cands.sort(key=lambda j: _rank_key(float(row[j]), j))
                 cands = cands[:k]
             chosen = sorted(set(cands) | set(window))
-            idx[pos + (i,)][:len(chosen)] = chosen
-            cnt[pos + (i,)] = len(chosen)
+            idx[pos + (r,)][:len(chosen)] = chosen
+            cnt[pos + (r,)] = len(chosen)
     return idx, cnt
 
 

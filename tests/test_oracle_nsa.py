@@ -142,3 +142,101 @@ def test_combine_gates():
     z[..., 1] = 60.0
     z[..., 0] = z[..., 2] = -60.0
     assert np.allclose(N.combine(*o, z), o[1], atol=1e-15, rtol=0)
+
+
+# ----------------------------------------------------- per-token selection
+def test_token_scores_hand_example():
+    """Uniform logits (q = 0), two identical heads: per-row scores worked out
+    by hand in the golden file; the head mean leaves them unchanged."""
+    with open(os.path.join(GOLDEN, "nsa_token_scores_example.json")) as f:
+        ex = json.load(f)
+    S, L, st, sb = ex["S"], ex["len"], ex["stride"], ex["sel_block"]
+    rng = np.random.default_rng(1)
+    q = np.zeros((1, 2, S, 4))
+    k = rng.standard_normal((1, 1, S, 4))
+    v = rng.standard_normal((1, 1, S, 4))
+    ck, cv = N.compress(k, L, st), N.compress(v, L, st)
+    _, _, p = N.cmp_attention(q, ck, cv, L, st, 0.5)
+    s = N.cmp_token_scores(p, 1, L, st, sb, S)
+    assert s.shape == (1, 1, S, 2)
+    for t0, t1, e0, e1 in ex["rows"]:
+        want = np.array([eval(e0, {}), eval(e1, {})])
+        assert np.max(np.abs(s[0, 0, t0:t1 + 1] - want)) < 1e-14, (t0, t1)
+
+
+def test_token_scores_mass_and_block_mean():
+    """A token's scores sum to 1 once it sees a summary (0 before), nothing
+    falls after its own block, and the mean over a query block's rows is the
+    (separately pinned) per-block score of that block."""
+    c, q, k, v, _ = _small(S=320)
+    ck, cv = N.compress(k, c.cmp_len, c.cmp_stride), N.compress(v, c.cmp_len, c.cmp_stride)
+    _, _, p = N.cmp_attention(q, ck, cv, c.cmp_len, c.cmp_stride, c.scale)
+    s = N.cmp_token_scores(p, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
+    t = np.arange(c.S)
+    want = (t >= c.cmp_len - 1).astype(np.float64)
+    assert np.max(np.abs(s.sum(-1) - want)) < 1e-13
+    for tt in range(c.S):
+        assert (s[:, :, tt, tt // c.sel_block + 1:] == 0).all()
+    sb = N.cmp_block_scores(p, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
+    for i in range(c.n_blocks):
+        rows = slice(i * c.sel_block, min((i + 1) * c.sel_block, c.S))
+        assert np.max(np.abs(s[:, :, rows].mean(axis=2) - sb[:, :, i])) < 1e-14
+
+
+def test_per_token_selection_brute_force():
+    """Per-token candidates are blocks 0 .. t // block; against a lexsort of
+    each row's candidates (ties broken by lower index), with planted ties."""
+    rng = np.random.default_rng(3)
+    S, blk, nK, k = 200, 16, 13, 4
+    s = rng.integers(0, 5, size=(2, S, nK)).astype(np.float64)   # many ties
+    idx, cnt = P.select_blocks(s, k, 0, causal=True, row_block=blk)
+    for r in range(2):
+        for t in range(S):
+            cands = np.arange(t // blk + 1)
+            order = np.lexsort((cands, -s[r, t, cands]))
+            want = np.sort(cands[order[:k]])
+            assert cnt[r, t] == len(want)
+            assert list(idx[r, t, :cnt[r, t]]) == list(want)
+            assert (idx[r, t, cnt[r, t]:] == -1).all()
+
+
+def _dense_masked(q, k, v, mask, scale):
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    return F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
+                                          scale=scale).numpy()
+
+
+def test_token_attention_matches_dense_masked_sdpa():
+    """Every head of a group attends, per row, to the keys <= t of that
+    row's own blocks: a dense SDPA with the explicit boolean mask."""
+    rng = np.random.default_rng(4)
+    B, Hq, Hkv, S, D, blk, kk = 1, 4, 2, 96, 8, 16, 2
+    q = rng.standard_normal((B, Hq, S, D))
+    k = rng.standard_normal((B, Hkv, S, D))
+    v = rng.standard_normal((B, Hkv, S, D))
+    s = rng.standard_normal((B, Hkv, S, S // blk))
+    idx, cnt = P.select_blocks(s, kk, 0, causal=True, row_block=blk)
+    out, lse = N.token_sparse_attention(q, k, v, idx, cnt, blk, 0.3)
+    G = Hq // Hkv
+    for h in range(Hq):
+        g = h // G
+        mask = np.zeros((S, S), dtype=bool)
+        for t in range(S):
+            for j in idx[0, g, t, :cnt[0, g, t]]:
+                mask[t, j * blk:(j + 1) * blk] = True
+        mask &= np.tril(np.ones((S, S), dtype=bool))
+        ref = _dense_masked(q[0, h][None], k[0, g][None], v[0, g][None], mask, 0.3)[0]
+        assert np.max(np.abs(out[0, h] - ref)) < 1e-12
+        logits = np.where(mask, 0.3 * q[0, h] @ k[0, g].T, -np.inf)
+        m = logits.max(-1)
+        assert np.max(np.abs(lse[0, h] - (m + np.log(np.exp(logits - m[:, None]).sum(-1))))) < 1e-12
+
+
+def test_per_token_forward_dense_limit():
+    """With at least as many selected blocks as there are blocks, the
+    per-token selected branch is dense causal attention."""
+    c, q, k, v, z = _small(S=256, Hq=4, Hkv=1)
+    res = N.forward(q, k, v, z, c.cmp_len, c.cmp_stride, c.sel_block, c.n_blocks, c.window,
+                    c.scale, per_token=True)
+    assert res["scores"].shape == (1, 1, c.S, c.n_blocks)
+    assert np.max(np.abs(res["o_sel"] - _sdpa_causal(q, k, v, c.scale))) < 1e-12
