@@ -53,6 +53,11 @@ SIGNATURES = {
     "dsa_nsa_cmp_attn": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 8
                          + [_c_float, _vp, _vp, _vp, _vp]),
     "dsa_nsa_combine": (_c_int, [_c_int, _vp, _vp, _vp, _vp] + [_c_int] * 4 + [_vp, _vp]),
+    "dsa_nsa_cmp_token_scores": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 8
+                                 + [_c_float, _vp, _vp]),
+    "dsa_topk_select_tokens": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
+    "dsa_sparse_attn_tokens": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                               + [_c_int] * 2 + [_c_float, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -285,6 +290,39 @@ def dsa_nsa_cmp_attn(q, ck, cv, length, stride, sel_block, scale, out, lse, bloc
         _ptr(lse, "lse", torch.float32), _ptr(block_scores, "block_scores", torch.float32),
         _stream(stream))
     _check(st, "dsa_nsa_cmp_attn")
+
+
+def dsa_nsa_cmp_token_scores(q, ck, lse, length, stride, sel_block, scale, scores, stream=None):
+    """Per-token selection scores [B,Hkv,S,nb] from the compressed branch's lse."""
+    B, Hq, S, D = q.shape
+    Hkv = ck.shape[1]
+    st = load().dsa_nsa_cmp_token_scores(
+        _dtype_code(q), _ptr(q, "q"), _ptr(ck, "ck", q.dtype), _ptr(lse, "lse", torch.float32), B,
+        Hq, Hkv, S, D, length, stride, sel_block, float(scale),
+        _ptr(scores, "scores", torch.float32), _stream(stream))
+    _check(st, "dsa_nsa_cmp_token_scores")
+
+
+def dsa_topk_select_tokens(scores, k, n_local, block, idx, count, stream=None):
+    """scores [..., S, n_k] float32 (one row per token) -> idx [..., S, k+n_local],
+    count [..., S] int32; token t's candidates are blocks 0 .. t // block - n_local."""
+    S, n_k = scores.shape[-2], scores.shape[-1]
+    rows = scores.numel() // (S * n_k)
+    st = load().dsa_topk_select_tokens(_ptr(scores, "scores", torch.float32), rows, S, n_k, k,
+                                       n_local, block, _ptr(idx, "idx", torch.int32),
+                                       _ptr(count, "count", torch.int32), _stream(stream))
+    _check(st, "dsa_topk_select_tokens")
+
+
+def dsa_sparse_attn_tokens(q, k, v, idx, count, block, scale, out, lse=None, stream=None):
+    """Selected branch with per-token lists idx [B,Hkv,S,W], count [B,Hkv,S]."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    st = load().dsa_sparse_attn_tokens(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S,
+        D, _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), idx.shape[-1], block,
+        float(scale), _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream))
+    _check(st, "dsa_sparse_attn_tokens")
 
 
 def dsa_nsa_combine(o_cmp, o_sel, o_win, gate_logits, out, stream=None):

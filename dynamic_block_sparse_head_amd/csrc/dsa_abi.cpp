@@ -158,9 +158,29 @@ int dsa_topk_select(const float* scores, int rows, int n_q, int n_k, int k, int 
   REQUIRE(rows_fit(rows, n_q, 1), DSA_E_ARG, "rows*n_q too large");
   REQUIRE_PTR(scores);
   REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
-  return hip_status(dsa::launch_topk(scores, rows, n_q, n_k, k, n_local, causal, idx, count,
+  return hip_status(dsa::launch_topk(scores, rows, n_q, n_k, k, n_local, causal, 1, idx, count,
                                      static_cast<hipStream_t>(stream)),
                     "dsa_topk_select");
+}
+
+int dsa_topk_select_tokens(const float* scores, int rows, int S, int n_k, int k, int n_local,
+                           int block, int32_t* idx, int32_t* count, void* stream) {
+  g_err.clear();
+  REQUIRE(rows >= 1 && S >= 1 && n_k >= 1, DSA_E_ARG,
+          "rows, S, n_k must be >= 1 (got %d, %d, %d)", rows, S, n_k);
+  REQUIRE(block >= 1, DSA_E_ARG, "block must be >= 1 (got %d)", block);
+  REQUIRE(k >= 0, DSA_E_ARG, "k must be >= 0 (got %d)", k);
+  REQUIRE(n_local >= 0, DSA_E_ARG, "n_local must be >= 0 (got %d)", n_local);
+  REQUIRE(k + n_local >= 1, DSA_E_ARG, "k + n_local must be >= 1");
+  REQUIRE(n_k <= 8192, DSA_E_UNSUPPORTED, "n_k %d exceeds 8192", n_k);
+  REQUIRE((S + block - 1) / block <= n_k, DSA_E_ARG,
+          "the last token's block (%d) is past n_k (%d)", (S + block - 1) / block - 1, n_k);
+  REQUIRE(rows_fit(rows, S, 1), DSA_E_ARG, "rows*S too large");
+  REQUIRE_PTR(scores);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  return hip_status(dsa::launch_topk(scores, rows, S, n_k, k, n_local, 1, block, idx, count,
+                                     static_cast<hipStream_t>(stream)),
+                    "dsa_topk_select_tokens");
 }
 
 static int prefill_impl(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
@@ -466,6 +486,85 @@ int dsa_nsa_compress(int dtype, const void* k, const void* v, int B, int Hkv, in
   return hip_status(dsa::launch_nsa_compress(k, v, B, Hkv, S, D, len, stride, ck, cv,
                                              static_cast<hipStream_t>(stream)),
                     "dsa_nsa_compress");
+}
+
+int dsa_nsa_cmp_token_scores(int dtype, const void* q, const void* ck, const float* lse, int B,
+                             int Hq, int Hkv, int S, int D, int len, int stride, int sel_block,
+                             float scale, float* scores, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_dim(D));
+  TRY(check_block(sel_block, "sel_block"));
+  REQUIRE(len >= 1 && stride >= 1, DSA_E_ARG, "len and stride must be >= 1 (got %d, %d)", len,
+          stride);
+  REQUIRE(S >= len, DSA_E_ARG, "S (%d) must be >= len (%d)", S, len);
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE(Hq / Hkv <= 16, DSA_E_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
+          Hq / Hkv);
+  REQUIRE((sel_block + len - 2) / stride <= 31, DSA_E_UNSUPPORTED,
+          "a selection block may overlap at most 32 summaries (sel_block %d, len %d, stride %d)",
+          sel_block, len, stride);
+  const int nb = (S + sel_block - 1) / sel_block;
+  REQUIRE(rows_fit(B * Hkv, S, nb), DSA_E_ARG, "B*Hkv*S*nb too large");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(ck);
+  REQUIRE_PTR(lse);
+  REQUIRE_PTR(scores);
+  const int n_cmp = (S - len) / stride + 1;
+  dsa::CmpScoreArgs c{q, ck, lse, B, Hq, Hkv, S, n_cmp, D, len, stride, sel_block, scale, scores};
+  return hip_status(dsa::launch_cmp_token_scores(c, static_cast<hipStream_t>(stream)),
+                    "dsa_nsa_cmp_token_scores");
+}
+
+int dsa_sparse_attn_tokens(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                           int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
+                           int idx_width, int block, float scale, void* out, float* lse,
+                           void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  TRY(check_block(block, "block"));
+  REQUIRE(D == 128, DSA_E_UNSUPPORTED, "per-token lists need D = 128 (got %d)", D);
+  REQUIRE(Hq / Hkv <= 16, DSA_E_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
+          Hq / Hkv);
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE(idx_width >= 1 && idx_width <= 64, DSA_E_UNSUPPORTED,
+          "idx_width must be in [1, 64] (got %d)", idx_width);
+  REQUIRE((S + block - 1) / block <= 8192, DSA_E_UNSUPPORTED, "at most 8192 key blocks");
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  REQUIRE(rows_fit(B * Hkv, S, idx_width), DSA_E_ARG, "B*Hkv*S*idx_width too large");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  dsa::AttnArgs a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.idx = idx;
+  a.count = count;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.Skv = S;
+  a.D = D;
+  a.block = block;
+  a.idx_width = idx_width;
+  a.mode = dsa::MODE_INDEX;
+  a.sel_heads = Hq / Hkv;
+  a.scale = scale;
+  REQUIRE(dsa::token_attention_supported(a), DSA_E_UNSUPPORTED,
+          "no per-token attention kernel for this configuration");
+  return hip_status(dsa::launch_token_attention(a, static_cast<hipStream_t>(stream)),
+                    "dsa_sparse_attn_tokens");
 }
 
 int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, int B, int Hq,

@@ -43,8 +43,10 @@ hipError_t launch_page_scores(const PageScoreArgs& a, hipStream_t s);
 hipError_t launch_page_minmax(int dtype, const void* k, int B, int Hkv, int L, int D, int page,
                               void* kmin, void* kmax, hipStream_t s);
 
+// Row r of each n_q-row matrix belongs to query block (r % n_q) / row_block
+// (row_block = 1: the rows are the query blocks; > 1: per-token rows).
 hipError_t launch_topk(const float* scores, int rows, int n_q, int n_k, int k, int n_local,
-                       int causal, int32_t* idx, int32_t* count, hipStream_t s);
+                       int causal, int row_block, int32_t* idx, int32_t* count, hipStream_t s);
 
 enum AttnMode { MODE_INDEX = 0, MODE_WINDOW = 1, MODE_CMP = 2 };
 
@@ -70,6 +72,11 @@ struct AttnArgs {
 // Whether some kernel serves this configuration (host-side check).
 bool attention_supported(const AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+// Per-token lists (idx [B,Hkv,S,idx_width], count [B,Hkv,S]; key blocks of
+// a.block tokens): every head of group g at row t attends to keys <= t of
+// the blocks listed for (b, g, t).
+bool token_attention_supported(const AttnArgs& a);
+hipError_t launch_token_attention(const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_dma_weights(int dtype, const void* v, int B, int Hkv, int S, int D,
                               const float* proj, const float* gain, int block, float* weights,
@@ -126,6 +133,9 @@ struct CmpScoreArgs {
   float* scores;        // [B,Hkv,nb,nb]
 };
 hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s);
+// scores [B,Hkv,S,nb]: per query token (sum over the group's heads / G);
+// needs Hq/Hkv <= 16 and (sel_block + len - 2) / stride <= 31
+hipError_t launch_cmp_token_scores(const CmpScoreArgs& a, hipStream_t s);
 
 hipError_t launch_nsa_combine(const void* o1, const void* o2, const void* o3, const float* z,
                               int B, int Hq, int S, int D, void* out, hipStream_t s);

@@ -11,6 +11,8 @@
 //    in proportion to the overlap: the importance that ranks blocks for the
 //    selected branch.  One workgroup per (group, query block), so the
 //    reduction order is fixed.
+//  * k_cmp_token_scores: the same probabilities kept per query token (summed
+//    over the group's heads only): per-token selection scores.
 //  * k_combine: out = sum over branches of sigmoid(gate logit) * branch output.
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -204,6 +206,178 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
   }
 }
 
+// Per-token selection scores (the method's own granularity: each query token
+// ranks the key blocks for its KV group).  One workgroup per (group, 32
+// consecutive tokens); wave w holds the Q operands of heads w, w + 4, ...
+// (HPW heads, G <= 4 HPW), so the summary tile staged in LDS is shared by
+// all heads of the group.  Per summary tile each wave adds its heads'
+// probabilities into one 32 x 32 partial (token x summary) and parks it in
+// LDS; the workgroup then forms the block scores of the blocks whose last
+// overlapping summary lies in this tile, reading this tile's and the
+// previous tile's partials (a block spans fewer than 32 summaries, checked
+// by the caller).  Blocks past the last tile any of the 32 tokens can see
+// are written at the last tile (their remaining summaries are invisible, 0).
+// Output [B,Hkv,S,nb]; the head mean makes a row that sees a summary sum to 1.
+constexpr int kTokRows = 32;
+constexpr int kPStride = 33;   // padded partial row (floats)
+
+template <int D, int HPW>
+__global__ __launch_bounds__(kNW * 64) void k_cmp_token_scores(CmpScoreArgs a, int ntt) {
+  constexpr int CSTR = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int CPT = (32 * CPR + kNW * 64 - 1) / (kNW * 64);
+  __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][32 * CSTR];
+  __shared__ float part[2][kNW][kTokRows * kPStride];
+  __shared__ __attribute__((aligned(16))) float lse_lds[kNW * HPW][kTokRows];
+
+  const int bg = blockIdx.x / ntt, tt = blockIdx.x % ntt;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int t0 = tt * kTokRows, t1 = min(a.S, t0 + kTokRows) - 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const float c = a.scale * kLog2e;
+  const int nb = (a.S + a.sel_block - 1) / a.sel_block;
+  float* out = a.scores + (size_t(bg) * a.S + t0) * nb;
+  const float inv_g = 1.f / float(G);
+
+  int c_hi = -1;
+  if (t1 >= a.len - 1) c_hi = min(a.n_cmp - 1, (t1 - (a.len - 1)) / a.stride);
+  const int nkt = c_hi < 0 ? 0 : c_hi / 32 + 1;
+  if (nkt == 0) {   // no token of the tile sees a summary: all scores 0
+    for (int e = threadIdx.x; e < (t1 - t0 + 1) * nb; e += kNW * 64) out[e] = 0.f;
+    return;
+  }
+
+  // Q operands of this wave's heads (rows = the 32 tokens), base-2 lse in LDS
+  bf16x8 qf[HPW][D / 16];
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q);
+#pragma unroll
+  for (int hi = 0; hi < HPW; ++hi) {
+    const int h = hi * kNW + wave;
+    const int t = t0 + col;
+    const bool ok = h < G && t <= t1;
+    const uint16_t* src = qp + ((size_t(b) * a.Hq + g * G + (ok ? h : 0)) * a.S + (ok ? t : t0)) * D + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + ks * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[hi][ks][e] = ok ? v[e] : static_cast<__bf16>(0.0f);
+    }
+    if (half == 0) {
+      float l2 = __builtin_inff();   // no such head / token: probability 0
+      if (ok) {
+        const float l = a.lse[(size_t(b) * a.Hq + g * G + h) * a.S + t] * kLog2e;
+        l2 = (l == -__builtin_inff()) ? 0.f : l;   // sees no summary: cut by the mask
+      }
+      lse_lds[hi * kNW + wave][col] = l2;
+    }
+  }
+
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(static_cast<const uint16_t*>(a.ck) + size_t(bg) * a.n_cmp * D,
+                                               uint32_t(a.n_cmp) * D * 2);
+  u32x4 st[CPT];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int e = threadIdx.x + cc * kNW * 64;
+      if (e < 32 * CPR)
+        st[cc] = __builtin_amdgcn_raw_buffer_load_b128(crs, uint32_t(((kt * 32 + e / CPR) * D + (e % CPR) * 8) * 2), 0, 0);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc) {
+      const int e = threadIdx.x + cc * kNW * 64;
+      if (e < 32 * CPR) *reinterpret_cast<u32x4*>(&c_lds[buf][(e / CPR) * CSTR + (e % CPR) * 8]) = st[cc];
+    }
+  };
+
+  // last token of each accumulator row held by this lane (-1 past the sequence)
+  int tlim[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int tt2 = t0 + (rr >> 2) * 8 + half * 4 + (rr & 3);
+    tlim[rr] = tt2 <= t1 ? tt2 : -1;
+  }
+
+  // blocks emitted after tile m: those whose last overlapping summary
+  // floor((j*sb + sb - 1) / stride) lies at or before tile m's last summary
+  auto last_block = [&](int m) {
+    const int v = (32 * m + 32) * a.stride - a.sel_block;
+    return v < 0 ? -1 : v / a.sel_block;
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  int jlo = 0;
+  for (int m = 0; m < nkt; ++m) {
+    const int buf = m & 1;
+    if (m + 1 < nkt) load(m + 1);
+    float acc[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) acc[rr] = 0.f;
+    const int cs = m * 32 + col;                    // this lane's summary
+    const int cend = cs * a.stride + a.len - 1;     // its last token
+    const bool all_vis = (m * 32 + 31) * a.stride + a.len - 1 <= t0;
+    bf16x8 cb[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      cb[ks] = *reinterpret_cast<const bf16x8*>(&c_lds[buf][col * CSTR + ks * 16 + half * 8]);
+#pragma unroll
+    for (int hi = 0; hi < HPW; ++hi) {
+      if (hi * kNW + wave >= G) break;   // wave-uniform
+      floatx16 sacc = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hi][ks], cb[ks], sacc, 0, 0, 0);
+      const float* lrow = lse_lds[hi * kNW + wave];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(lrow + q4 * 8 + half * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = q4 * 4 + r;
+          const float p = fast_exp2(fmaf(sacc[rr], c, -l4[r]));
+          acc[rr] += (all_vis || cend <= tlim[rr]) ? p : 0.f;
+        }
+      }
+    }
+    float* pw = part[buf][wave];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) pw[((rr >> 2) * 8 + half * 4 + (rr & 3)) * kPStride + col] = acc[rr];
+    if (m + 1 < nkt) store(buf ^ 1);
+    __syncthreads();
+
+    // block scores of blocks jlo .. jhi for the 32 tokens
+    const int jhi = (m == nkt - 1) ? nb - 1 : min(nb - 1, last_block(m));
+    const int nbt = jhi - jlo + 1;
+    const int cmax = min(32 * m + 31, a.n_cmp - 1);
+    for (int e = threadIdx.x; e < kTokRows * nbt; e += kNW * 64) {
+      const int r = e / nbt, j = jlo + e % nbt;
+      if (t0 + r > t1) continue;
+      const int j0 = j * a.sel_block, j1 = j0 + a.sel_block - 1;
+      int c0 = j0 - a.len + 1;
+      c0 = c0 <= 0 ? 0 : (c0 + a.stride - 1) / a.stride;
+      const int c1 = min(cmax, j1 / a.stride);
+      float v = 0.f;
+      for (int cc = c0; cc <= c1; ++cc) {
+        const int a0 = cc * a.stride, a1 = a0 + a.len - 1;
+        const int ov = min(a1, j1) - max(a0, j0) + 1;
+        const float* pc = &part[(cc >> 5) & 1][0][r * kPStride + (cc & 31)];
+        float ps = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kNW; ++w2) ps += pc[w2 * kTokRows * kPStride];
+        if (ov > 0) v += ps * (float(ov) / float(a.len));
+      }
+      out[size_t(r) * nb + j] = v * inv_g;
+    }
+    jlo = jhi + 1;
+    __syncthreads();   // the partials of tile m - 1 are overwritten next
+  }
+}
+
 // grid-stride over 8-element chunks of the outputs
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ o1,
                                                  const uint16_t* __restrict__ o2,
@@ -254,6 +428,24 @@ hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s) {
     k_cmp_block_scores<128><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
   else
     k_cmp_block_scores<64><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
+  return hipGetLastError();
+}
+
+hipError_t launch_cmp_token_scores(const CmpScoreArgs& a, hipStream_t s) {
+  const int ntt = (a.S + kTokRows - 1) / kTokRows;
+  const int G = a.Hq / a.Hkv;
+  const int grid = a.B * a.Hkv * ntt;
+#define DSA_TS(DD, HH) k_cmp_token_scores<DD, HH><<<grid, kNW * 64, 0, s>>>(a, ntt)
+  if (a.D == 128) {
+    if (G <= 4) DSA_TS(128, 1);
+    else if (G <= 8) DSA_TS(128, 2);
+    else DSA_TS(128, 4);
+  } else {
+    if (G <= 4) DSA_TS(64, 1);
+    else if (G <= 8) DSA_TS(64, 2);
+    else DSA_TS(64, 4);
+  }
+#undef DSA_TS
   return hipGetLastError();
 }
 

@@ -105,14 +105,14 @@ __device__ __forceinline__ int chunk_prefix(const int (&mine)[E], int (&base)[E]
 template <int E, int W>
 __global__ __launch_bounds__(W == 1 ? 256 : 64 * W) void k_topk(
     const float* __restrict__ scores, int n_rows, int n_q, int n_k, int k, int n_local, int causal,
-    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+    int row_block, int32_t* __restrict__ idx, int32_t* __restrict__ count) {
   __shared__ int red[2][W];
   __shared__ int pre[E * W + 1];
   const int lane = threadIdx.x & 63;
   const int w = (W == 1) ? 0 : (threadIdx.x >> 6);
   const int row = (W == 1) ? blockIdx.x * 4 + (threadIdx.x >> 6) : blockIdx.x;
   if (row >= n_rows) return;  // W == 1: the whole wave; W > 1: the whole workgroup
-  const int i = row % n_q;
+  const int i = (row % n_q) / row_block;   // the row's query block
   const float* srow = scores + size_t(row) * n_k;
   const int width = k + n_local;
   int last, w0, w1;
@@ -188,12 +188,12 @@ __global__ __launch_bounds__(W == 1 ? 256 : 64 * W) void k_topk(
 
 template <int W>
 hipError_t launch_w(int E, const float* scores, int n_rows, int n_q, int n_k, int k, int n_local,
-                    int causal, int32_t* idx, int32_t* count, hipStream_t s) {
+                    int causal, int row_block, int32_t* idx, int32_t* count, hipStream_t s) {
   const int threads = (W == 1) ? 256 : 64 * W;
   const int grid = (W == 1) ? (n_rows + 3) / 4 : n_rows;
 #define DSA_TOPK(EE)                                                                          \
-  k_topk<EE, W><<<grid, threads, 0, s>>>(scores, n_rows, n_q, n_k, k, n_local, causal, idx, \
-                                         count)
+  k_topk<EE, W><<<grid, threads, 0, s>>>(scores, n_rows, n_q, n_k, k, n_local, causal, \
+                                         row_block, idx, count)
   switch (E) {
     case 1: DSA_TOPK(1); break;
     case 2: DSA_TOPK(2); break;
@@ -219,14 +219,14 @@ int pow2_at_least(int x) {
 // are short); otherwise eight waves share a row so that few long rows (decode:
 // one per sequence and KV head) still spread over many CUs.
 hipError_t launch_topk(const float* scores, int rows, int n_q, int n_k, int k, int n_local,
-                       int causal, int32_t* idx, int32_t* count, hipStream_t s) {
+                       int causal, int row_block, int32_t* idx, int32_t* count, hipStream_t s) {
   const int n_rows = rows * n_q;
   if (n_rows == 0) return hipSuccess;
   if ((n_rows >= 512 && n_k <= 2048) || n_k <= 256)
     return launch_w<1>(pow2_at_least((n_k + 63) / 64), scores, n_rows, n_q, n_k, k, n_local,
-                       causal, idx, count, s);
+                       causal, row_block, idx, count, s);
   return launch_w<8>(pow2_at_least((n_k + 511) / 512), scores, n_rows, n_q, n_k, k, n_local,
-                     causal, idx, count, s);
+                     causal, row_block, idx, count, s);
 }
 
 }  // namespace dsa

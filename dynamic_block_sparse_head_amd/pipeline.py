@@ -192,7 +192,7 @@ class NSAPlan:
     sliding branch; gated combine ([NSA] §03)."""
 
     def __init__(self, B, Hq, Hkv, S, D, cmp_len, cmp_stride, sel_block, sel_k, window, dtype,
-                 device, scale=None):
+                 device, scale=None, per_token=False):
         self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
         self.cmp_len, self.cmp_stride = cmp_len, cmp_stride
         self.sel_block, self.sel_k, self.window = sel_block, sel_k, window
@@ -203,20 +203,33 @@ class NSAPlan:
         self.cv = _empty((B, Hkv, self.n_cmp, D), dtype, device)
         self.o_cmp = _empty((B, Hq, S, D), dtype, device)
         self.lse_cmp = _empty((B, Hq, S), torch.float32, device)
-        self.scores = _empty((B, Hkv, self.nb, self.nb), torch.float32, device)
-        self.idx = _empty((B, Hkv, self.nb, sel_k), torch.int32, device)
-        self.count = _empty((B, Hkv, self.nb), torch.int32, device)
+        # per_token: every query token ranks the blocks for its group
+        self.per_token = per_token
+        rows = S if per_token else self.nb
+        self.scores = _empty((B, Hkv, rows, self.nb), torch.float32, device)
+        self.idx = _empty((B, Hkv, rows, sel_k), torch.int32, device)
+        self.count = _empty((B, Hkv, rows), torch.int32, device)
         self.o_sel = _empty((B, Hq, S, D), dtype, device)
         self.o_win = _empty((B, Hq, S, D), dtype, device)
         self.out = _empty((B, Hq, S, D), dtype, device)
 
     def run(self, q, k, v, z):
         L.dsa_nsa_compress(k, v, self.cmp_len, self.cmp_stride, self.ck, self.cv)
-        L.dsa_nsa_cmp_attn(q, self.ck, self.cv, self.cmp_len, self.cmp_stride, self.sel_block,
-                           self.scale, self.o_cmp, self.lse_cmp, self.scores)
-        L.dsa_topk_select(self.scores, self.sel_k, 0, True, self.idx, self.count)
-        L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.sel_block, 0, self.scale,
-                                  self.o_sel)
+        if self.per_token:
+            L.dsa_nsa_cmp_attn(q, self.ck, self.cv, self.cmp_len, self.cmp_stride, self.sel_block,
+                               self.scale, self.o_cmp, self.lse_cmp)
+            L.dsa_nsa_cmp_token_scores(q, self.ck, self.lse_cmp, self.cmp_len, self.cmp_stride,
+                                       self.sel_block, self.scale, self.scores)
+            L.dsa_topk_select_tokens(self.scores, self.sel_k, 0, self.sel_block, self.idx,
+                                     self.count)
+            L.dsa_sparse_attn_tokens(q, k, v, self.idx, self.count, self.sel_block, self.scale,
+                                     self.o_sel)
+        else:
+            L.dsa_nsa_cmp_attn(q, self.ck, self.cv, self.cmp_len, self.cmp_stride,
+                               self.sel_block, self.scale, self.o_cmp, self.lse_cmp, self.scores)
+            L.dsa_topk_select(self.scores, self.sel_k, 0, True, self.idx, self.count)
+            L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.sel_block, 0,
+                                      self.scale, self.o_sel)
         L.dsa_sparse_attn_prefill(q, k, v, None, None, self.sel_block, self.window, self.scale,
                                   self.o_win)
         L.dsa_nsa_combine(self.o_cmp, self.o_sel, self.o_win, z, self.out)

@@ -302,6 +302,46 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv,
                      float scale, void* out, float* lse, float* block_scores, void* stream);
 
 /*
+ * Per-token selection for the selected branch ([NSA] §03 at the granularity
+ * of the original method: each query token ranks the key blocks for its own
+ * KV group from its compressed-branch attention, and every query head of
+ * the group then attends to that token's blocks).
+ *
+ * dsa_nsa_cmp_token_scores: scores [B,Hkv,S,nb] float32 (nb =
+ * ceil(S/sel_block)); for token t and key block j, the compressed-branch
+ * probability of the summaries overlapping block j, each split in
+ * proportion to its overlap, averaged over the group's query heads (a row
+ * that sees a summary sums to 1; blocks after t's own block get 0).  q
+ * [B,Hq,S,D] and ck [B,Hkv,n_cmp,D] bf16 as given to dsa_nsa_cmp_attn, lse
+ * [B,Hq,S] the log-sum-exp it wrote.  Limits: Hq/Hkv <= 16;
+ * (sel_block + len - 2) / stride <= 31 (a block overlaps at most 32
+ * summaries); else DSA_E_UNSUPPORTED.
+ *
+ * dsa_topk_select_tokens: as dsa_topk_select with causal candidates per
+ * token: row t of each S-row score matrix [rows, S, n_k] draws its top-k
+ * from blocks 0 .. t/block - n_local and keeps the window
+ * t/block - n_local + 1 .. t/block.  idx [rows, S, k+n_local], count
+ * [rows, S].  Needs ceil(S/block) <= n_k <= 8192.
+ *
+ * dsa_sparse_attn_tokens: out [B,Hq,S,D] bf16: row t of every query head of
+ * group g attends to the keys s <= t of the key blocks (block tokens each)
+ * listed in idx [B,Hkv,S,idx_width] (ascending, -1 padded) with count
+ * [B,Hkv,S]; lse [B,Hq,S] float32 may be NULL (as dsa_sparse_attn_prefill).
+ * Blocks must be ascending and below ceil(S/block); a block listed twice is
+ * used once.  Limits: bf16, D = 128, Hq/Hkv <= 16, block in {32, 64, 128},
+ * idx_width <= 64, ceil(S/block) <= 8192 (else DSA_E_UNSUPPORTED).
+ */
+int dsa_nsa_cmp_token_scores(int dtype, const void* q, const void* ck, const float* lse, int B,
+                             int Hq, int Hkv, int S, int D, int len, int stride, int sel_block,
+                             float scale, float* scores, void* stream);
+int dsa_topk_select_tokens(const float* scores, int rows, int S, int n_k, int k, int n_local,
+                           int block, int32_t* idx, int32_t* count, void* stream);
+int dsa_sparse_attn_tokens(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                           int Hkv, int S, int D, const int32_t* idx, const int32_t* count,
+                           int idx_width, int block, float scale, void* out, float* lse,
+                           void* stream);
+
+/*
  * Gated combine of the three branches ([NSA] §03: each token and head
  * weighs the compressed, selected and sliding outputs):
  * out[b,h,t] = sigmoid(z0)*o_cmp + sigmoid(z1)*o_sel + sigmoid(z2)*o_win with

@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -217,3 +217,35 @@ def test_binding_refuses_cpu_tensors():
     cnt = torch.zeros(1, 4, dtype=torch.int32)
     with pytest.raises(ValueError):
         L.dsa_topk_select(s, 1, 1, True, idx, cnt)
+
+
+def test_per_token_selection_validation():
+    """Every call below fails validation (one bad argument each), so nothing
+    is launched with the fake pointers."""
+    lib = L.load()
+    ts = lib.dsa_nsa_cmp_token_scores
+    args = [1, FAKE, FAKE, FAKE, 1, 64, 4, 32768, 128, 32, 16, 64, 0.1, FAKE, None]
+    a = list(args); a[5] = 68
+    assert ts(*a) == L.DSA_E_UNSUPPORTED                           # G = 17
+    a = list(args); a[10] = 2
+    assert ts(*a) == L.DSA_E_UNSUPPORTED                           # block spans 47 summaries
+    a = list(args); a[3] = None
+    assert ts(*a) == L.DSA_E_ARG and "lse" in _err()
+    a = list(args); a[0] = 0
+    assert ts(*a) == L.DSA_E_UNSUPPORTED                           # float32
+    tk = lib.dsa_topk_select_tokens
+    assert tk(FAKE, 4, 32768, 511, 16, 0, 64, FAKE, FAKE, None) == L.DSA_E_ARG   # n_k < blocks
+    assert tk(FAKE, 4, 32768, 512, 16, 0, 0, FAKE, FAKE, None) == L.DSA_E_ARG    # block 0
+    assert tk(None, 4, 32768, 512, 16, 0, 64, FAKE, FAKE, None) == L.DSA_E_ARG
+    at = lib.dsa_sparse_attn_tokens
+    args = [1, FAKE, FAKE, FAKE, 1, 64, 4, 32768, 128, FAKE, FAKE, 16, 64, 0.1, FAKE, None, None]
+    a = list(args); a[8] = 64
+    assert at(*a) == L.DSA_E_UNSUPPORTED                           # D = 64
+    a = list(args); a[11] = 65
+    assert at(*a) == L.DSA_E_UNSUPPORTED                           # list too wide
+    a = list(args); a[12] = 96
+    assert at(*a) == L.DSA_E_UNSUPPORTED                           # block 96
+    a = list(args); a[10] = None
+    assert at(*a) == L.DSA_E_ARG
+    a = list(args); a[5] = 128
+    assert at(*a) == L.DSA_E_UNSUPPORTED                           # G = 32
