@@ -13,7 +13,7 @@ variants, decode over a paged pool with variable lengths, and the CPU oracle
 timed on a bounded sample of the headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|long|nsa|backward|per_head|dma|paged]
+                    [--only prefill|decode|long|nsa|nsa_tokens|backward|per_head|dma|paged]
                     [--copy-calibration]
 """
 from __future__ import annotations
@@ -391,6 +391,46 @@ def bench_nsa(torch, iters=5):
             "effective_tflops_whole_step": round((f1 + f2 + f3) / (ms * 1e-3) / 1e12, 2)}
 
 
+def bench_nsa_tokens(torch, iters=5):
+    """The 32K three-branch step with per-token selection (every query token
+    ranks the blocks of its group from its own compressed-branch attention):
+    per-kernel times and the selected branch's rate.  Its FLOPs count each
+    (token, listed block) pair as 4 D x block x G, as the block-level figure
+    counts each (query block, key block) pair."""
+    from dynamic_block_sparse_head_amd import binding as L
+    from dynamic_block_sparse_head_amd import configs, inputs
+    from dynamic_block_sparse_head_amd.pipeline import NSAPlan
+
+    c = configs.NSA_32K
+    x = inputs.nsa_inputs(c, seed=0, device="cuda")
+    p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
+                x["q"].dtype, "cuda", per_token=True)
+    q, k, v, z = x["q"], x["k"], x["v"], x["z"]
+    p.run(q, k, v, z)
+    ms = _timed(lambda: p.run(q, k, v, z), iters, torch)
+    ms_scores = _timed(lambda: L.dsa_nsa_cmp_token_scores(q, p.ck, p.lse_cmp, c.cmp_len,
+                                                          c.cmp_stride, c.sel_block, p.scale,
+                                                          p.scores), iters, torch)
+    ms_topk = _timed(lambda: L.dsa_topk_select_tokens(p.scores, c.sel_k, 0, c.sel_block, p.idx,
+                                                      p.count), iters, torch)
+    ms_attn = _timed(lambda: L.dsa_sparse_attn_tokens(q, k, v, p.idx, p.count, c.sel_block,
+                                                      p.scale, p.o_sel), iters, torch)
+    pairs = int(p.count.to(torch.int64).sum().item())      # (token, group, block) triples
+    flops = 4.0 * c.D * c.sel_block * c.G * pairs
+    # K/V bytes the selected branch would read with no sharing between tokens
+    kv_unshared = pairs * c.sel_block * c.D * 2 * 2
+    del x, p, q, k, v, z
+    return {"workload": f"{c.name}: per-token selection, S=32768 Hq=64 Hkv=4 D=128; summaries "
+                        "32/16, top-16 of 64-token blocks per token, window 512, sigmoid gates",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(c.S / (ms * 1e-3), 1),
+            "token_scores_ms": round(ms_scores, 4), "topk_ms": round(ms_topk, 4),
+            "selected_attn_ms": round(ms_attn, 4),
+            "selected_attn_effective_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
+            "selected_attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12
+                                                     / MFMA_BF16_PEAK_TFLOPS, 4),
+            "selected_attn_unshared_kv_gb": round(kv_unshared / 1e9, 2)}
+
+
 def cpu_baseline(budget_s=20.0):
     """The oracle, untouched, on a bounded sample of the headline workload:
     pooled scores for every block, then selection and attention (all 32 heads)
@@ -451,8 +491,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "backward", "per_head",
-                                       "dma", "paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "nsa_tokens", "backward",
+                                       "per_head", "dma", "paged"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -510,6 +550,8 @@ def main():
         extra["long_prefill"] = bench_long_prefill(torch)
     if args.only in (None, "nsa"):
         extra["nsa"] = bench_nsa(torch)
+    if args.only in (None, "nsa_tokens"):
+        extra["nsa_per_token"] = bench_nsa_tokens(torch)
     if args.only in (None, "backward"):
         extra["backward"] = bench_backward(torch)
     if args.only in (None, "per_head"):
