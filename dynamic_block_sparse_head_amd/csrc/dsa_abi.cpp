@@ -532,7 +532,6 @@ int dsa_sparse_attn_tokens(int dtype, const void* q, const void* k, const void* 
   REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
   REQUIRE(idx_width >= 1 && idx_width <= 64, DSA_E_UNSUPPORTED,
           "idx_width must be in [1, 64] (got %d)", idx_width);
-  REQUIRE((S + block - 1) / block <= 8192, DSA_E_UNSUPPORTED, "at most 8192 key blocks");
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
   REQUIRE(rows_fit(B * Hkv, S, idx_width), DSA_E_ARG, "B*Hkv*S*idx_width too large");
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");

@@ -327,9 +327,9 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv,
  * group g attends to the keys s <= t of the key blocks (block tokens each)
  * listed in idx [B,Hkv,S,idx_width] (ascending, -1 padded) with count
  * [B,Hkv,S]; lse [B,Hq,S] float32 may be NULL (as dsa_sparse_attn_prefill).
- * Blocks must be ascending and below ceil(S/block); a block listed twice is
- * used once.  Limits: bf16, D = 128, Hq/Hkv <= 16, block in {32, 64, 128},
- * idx_width <= 64, ceil(S/block) <= 8192 (else DSA_E_UNSUPPORTED).
+ * Lists hold distinct blocks (as dsa_topk_select_tokens writes them); keys
+ * of a listed block outside [0, t] are masked.  Limits: bf16, D = 128,
+ * Hq/Hkv <= 16, block = 64, idx_width <= 64 (else DSA_E_UNSUPPORTED).
  */
 int dsa_nsa_cmp_token_scores(int dtype, const void* q, const void* ck, const float* lse, int B,
                              int Hq, int Hkv, int S, int D, int len, int stride, int sel_block,

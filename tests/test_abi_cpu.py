@@ -245,6 +245,8 @@ def test_per_token_selection_validation():
     assert at(*a) == L.DSA_E_UNSUPPORTED                           # list too wide
     a = list(args); a[12] = 96
     assert at(*a) == L.DSA_E_UNSUPPORTED                           # block 96
+    a = list(args); a[12] = 128
+    assert at(*a) == L.DSA_E_UNSUPPORTED                           # block 128
     a = list(args); a[10] = None
     assert at(*a) == L.DSA_E_ARG
     a = list(args); a[5] = 128

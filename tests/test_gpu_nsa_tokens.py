@@ -97,12 +97,13 @@ def _lists(B, Hkv, S, block, k, seed):
     return Op.select_blocks(s, k, 0, causal=True, row_block=block)
 
 
-@pytest.mark.parametrize("S,Hq,Hkv,block,k", [(1000, 32, 2, 64, 16), (523, 16, 1, 32, 7),
-                                               (700, 8, 2, 128, 3), (257, 12, 1, 64, 40)])
+@pytest.mark.parametrize("S,Hq,Hkv,block,k", [(1000, 32, 2, 64, 16), (523, 16, 1, 64, 7),
+                                               (701, 8, 2, 64, 3), (257, 12, 1, 64, 40),
+                                               (130, 2, 2, 64, 1)])
 def test_token_attention(S, Hq, Hkv, block, k):
     """Per-token selected branch against the oracle on the same lists: ragged
-    S (a partial tile of 8 tokens, a partial last block), G = 16, 16, 4, 12,
-    blocks of 32/64/128, lists narrower and wider than the candidates."""
+    S (a partial tile of 4 tokens, a partial last block), G = 16, 16, 4, 12,
+    1, lists narrower and wider than the candidates."""
     c = replace(configs.NSA_32K, S=S, Hq=Hq, Hkv=Hkv)
     x = inputs.nsa_inputs(c, seed=S + block, device=DEV)
     idx, cnt = _lists(c.B, Hkv, S, block, k, seed=S)
