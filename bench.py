@@ -377,6 +377,24 @@ def bench_nsa(torch, iters=5):
     args = (x["q"], x["k"], x["v"], x["z"])
     p.run(*args)
     ms = _timed(lambda: p.run(*args), iters, torch)
+    # the step's calls one by one (same inputs, outputs rewritten identically)
+    from dynamic_block_sparse_head_amd import binding as L
+    q, k, v, z = args
+    calls = {
+        "compress": lambda: L.dsa_nsa_compress(k, v, c.cmp_len, c.cmp_stride, p.ck, p.cv),
+        "cmp_attn": lambda: L.dsa_nsa_cmp_attn(q, p.ck, p.cv, c.cmp_len, c.cmp_stride, c.sel_block,
+                                               p.scale, p.o_cmp, p.lse_cmp),
+        "cmp_attn_with_block_scores": lambda: L.dsa_nsa_cmp_attn(
+            q, p.ck, p.cv, c.cmp_len, c.cmp_stride, c.sel_block, p.scale, p.o_cmp, p.lse_cmp,
+            p.scores),
+        "topk": lambda: L.dsa_topk_select(p.scores, c.sel_k, 0, True, p.idx, p.count),
+        "selected_attn": lambda: L.dsa_sparse_attn_prefill(q, k, v, p.idx, p.count, c.sel_block, 0,
+                                                           p.scale, p.o_sel),
+        "window_attn": lambda: L.dsa_sparse_attn_prefill(q, k, v, None, None, c.sel_block,
+                                                         c.window, p.scale, p.o_win),
+        "combine": lambda: L.dsa_nsa_combine(p.o_cmp, p.o_sel, p.o_win, z, p.out),
+    }
+    per_call = {name: round(_timed(fn, iters, torch), 4) for name, fn in calls.items()}
     # exact-pair FLOPs of branches 1 and 3, selected-block FLOPs of branch 2
     S, G, D = c.S, c.G, c.D
     f1 = sum(max(0, (t - (c.cmp_len - 1)) // c.cmp_stride + 1) if t >= c.cmp_len - 1 else 0
@@ -388,7 +406,11 @@ def bench_nsa(torch, iters=5):
                         "blocks, window 512, sigmoid gates",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(S / (ms * 1e-3), 1),
             "branch_flops": f1 + f2 + f3,
-            "effective_tflops_whole_step": round((f1 + f2 + f3) / (ms * 1e-3) / 1e12, 2)}
+            "effective_tflops_whole_step": round((f1 + f2 + f3) / (ms * 1e-3) / 1e12, 2),
+            "per_call_ms": per_call,
+            "cmp_attn_tflops": round(f1 / (per_call["cmp_attn"] * 1e-3) / 1e12, 2),
+            "selected_attn_tflops": round(f2 / (per_call["selected_attn"] * 1e-3) / 1e12, 2),
+            "window_attn_tflops": round(f3 / (per_call["window_attn"] * 1e-3) / 1e12, 2)}
 
 
 def bench_nsa_tokens(torch, iters=5):

@@ -154,7 +154,12 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VSTR];
 
-  const int w = xcd_work_id(per_xcd);
+  // Contiguous work per XCD keeps a group's K/V in that XCD's L2.  The
+  // compressed branch is the exception: its work grows with the query block
+  // (a contiguous range would give some XCDs only the longest blocks) and its
+  // summaries are small, so its workgroups stay in dispatch order, dealt
+  // round-robin over the XCDs.
+  const int w = a.mode == MODE_CMP ? int(blockIdx.x) : xcd_work_id(per_xcd);
   if (w >= total) return;
   const int sub = w % wg_per_qb;
   const int rest = w / wg_per_qb;
@@ -460,7 +465,12 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VBYTES];
   __shared__ __attribute__((aligned(16))) float kbias[2][BIAS ? KT : 4];   // key_bias / scale
 
-  const int w = xcd_work_id(per_xcd);
+  // Contiguous work per XCD keeps a group's K/V in that XCD's L2.  The
+  // compressed branch is the exception: its work grows with the query block
+  // (a contiguous range would give some XCDs only the longest blocks) and its
+  // summaries are small, so its workgroups stay in dispatch order, dealt
+  // round-robin over the XCDs.
+  const int w = a.mode == MODE_CMP ? int(blockIdx.x) : xcd_work_id(per_xcd);
   if (w >= total) return;
   const int sub = w % wg_per_qb;
   const int rest = w / wg_per_qb;

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
   __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][32 * CSTR];
   extern __shared__ float colsum[];
 
-  const int bg = blockIdx.x / nqb, i = blockIdx.x % nqb;
+  // later query blocks see more summaries: start them first
+  const int bg = blockIdx.x / nqb, i = nqb - 1 - int(blockIdx.x % nqb);
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int sb = a.sel_block;
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_token_scores(CmpScoreArgs a, i
   __shared__ float part[2][kNW][kTokRows * kPStride];
   __shared__ __attribute__((aligned(16))) float lse_lds[kNW * HPW][kTokRows];
 
-  const int bg = blockIdx.x / ntt, tt = blockIdx.x % ntt;
+  const int bg = blockIdx.x / ntt, tt = ntt - 1 - int(blockIdx.x % ntt);   // longest first
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int G = a.Hq / a.Hkv;
   const int t0 = tt * kTokRows, t1 = min(a.S, t0 + kTokRows) - 1;
