@@ -393,6 +393,8 @@ def bench_nsa(torch, iters=5):
         "window_attn": lambda: L.dsa_sparse_attn_prefill(q, k, v, None, None, c.sel_block,
                                                          c.window, p.scale, p.o_win),
         "combine": lambda: L.dsa_nsa_combine(p.o_cmp, p.o_sel, p.o_win, z, p.out),
+        "window_attn_with_combine": lambda: L.dsa_nsa_window_combine(
+            q, k, v, c.window, p.scale, p.o_cmp, p.o_sel, z, p.out),
     }
     per_call = {name: round(_timed(fn, iters, torch), 4) for name, fn in calls.items()}
     # exact-pair FLOPs of branches 1 and 3, selected-block FLOPs of branch 2

@@ -56,6 +56,8 @@ SIGNATURES = {
     "dsa_nsa_cmp_token_scores": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 8
                                  + [_c_float, _vp, _vp]),
     "dsa_topk_select_tokens": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
+    "dsa_nsa_window_combine": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 6
+                               + [_c_float, _vp, _vp, _vp, _vp, _vp]),
     "dsa_sparse_attn_tokens": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
                                + [_c_int] * 2 + [_c_float, _vp, _vp, _vp]),
 }
@@ -323,6 +325,17 @@ def dsa_sparse_attn_tokens(q, k, v, idx, count, block, scale, out, lse=None, str
         D, _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), idx.shape[-1], block,
         float(scale), _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _stream(stream))
     _check(st, "dsa_sparse_attn_tokens")
+
+
+def dsa_nsa_window_combine(q, k, v, window, scale, o_cmp, o_sel, gate_logits, out, stream=None):
+    """Sliding branch with the gated combine in its epilogue (o_win stays on chip)."""
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    st = load().dsa_nsa_window_combine(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S,
+        D, window, float(scale), _ptr(o_cmp, "o_cmp", q.dtype), _ptr(o_sel, "o_sel", q.dtype),
+        _ptr(gate_logits, "gate_logits", torch.float32), _ptr(out, "out", q.dtype), _stream(stream))
+    _check(st, "dsa_nsa_window_combine")
 
 
 def dsa_nsa_combine(o_cmp, o_sel, o_win, gate_logits, out, stream=None):

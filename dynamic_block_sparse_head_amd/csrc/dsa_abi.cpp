@@ -614,6 +614,54 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, i
   return hip_status(dsa::launch_cmp_block_scores(c, s), "dsa_nsa_cmp_attn");
 }
 
+int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                           int Hkv, int S, int D, int window, float scale, const void* o_cmp,
+                           const void* o_sel, const float* gate_logits, void* out,
+                           void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  REQUIRE(D == 128, DSA_E_UNSUPPORTED, "the fused combine needs D = 128 (got %d)", D);
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE(window >= 1, DSA_E_ARG, "window must be >= 1 (got %d)", window);
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(o_cmp);
+  REQUIRE_PTR(o_sel);
+  REQUIRE_PTR(gate_logits);
+  REQUIRE_PTR(out);
+  dsa::AttnArgs a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.Skv = S;
+  a.D = D;
+  a.block = 64;
+  a.mode = dsa::MODE_WINDOW;
+  a.window = window;
+  a.cmp_len = 1;
+  a.cmp_stride = 1;
+  a.sel_heads = Hq / Hkv;
+  a.gate_o1 = o_cmp;
+  a.gate_o2 = o_sel;
+  a.gate_z = gate_logits;
+  a.scale = scale;
+  REQUIRE(dsa::attention_supported(a), DSA_E_UNSUPPORTED,
+          "the fused combine needs at least 4 query heads per KV head and a window of at most "
+          "8000 tokens");
+  return hip_status(dsa::launch_attention(a, static_cast<hipStream_t>(stream)),
+                    "dsa_nsa_window_combine");
+}
+
 int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void* o_win,
                     const float* gate_logits, int B, int Hq, int S, int D, void* out,
                     void* stream) {

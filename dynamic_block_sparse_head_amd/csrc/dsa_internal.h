@@ -67,6 +67,12 @@ struct AttnArgs {
   int cmp_len, cmp_stride;  // compressed mode: summary c ends at c*stride+len-1
   int sel_heads;        // query heads sharing one index row (Hq/Hkv unless per-head lists)
   const float* key_bias;  // [B,Hkv,Skv] additive logit term per key, or null
+  // gated combine in the epilogue (gate_z != null): out = sigmoid(z0) gate_o1
+  // + sigmoid(z1) gate_o2 + sigmoid(z2) (this attention's output), z =
+  // gate_z[b][t][h][0..2]; gate_o1 / gate_o2 [B,Hq,S,D] in the output dtype
+  const void* gate_o1;
+  const void* gate_o2;
+  const float* gate_z;
   float scale;
 };
 // Whether some kernel serves this configuration (host-side check).

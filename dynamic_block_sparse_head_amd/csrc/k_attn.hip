@@ -741,16 +741,52 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   const float lt = half_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (!row_ok) return;
-  uint16_t* dst = op + ((size_t(b) * a.Hq + row_h) * a.S + row_t) * D;
+  const size_t orow = ((size_t(b) * a.Hq + row_h) * a.S + row_t) * D;
+  uint16_t* dst = op + orow;
+  if (a.gate_z != nullptr) {
+    // gated combine with the other two branches' outputs (this branch in
+    // float32, the others as stored), rounded once
+    const float* z = a.gate_z + ((size_t(b) * a.S + row_t) * a.Hq + row_h) * 3;
+    const float g1 = 1.f / (1.f + __expf(-z[0]));
+    const float g2 = 1.f / (1.f + __expf(-z[1]));
+    const float g3 = inv / (1.f + __expf(-z[2]));
+    const uint16_t* p1 = static_cast<const uint16_t*>(a.gate_o1) + orow;
+    const uint16_t* p2 = static_cast<const uint16_t*>(a.gate_o2) + orow;
+    // all loads first: the stores below may alias them as far as the
+    // compiler knows, so interleaving would serialise every load
+    u32x2 w1[D / 32][4], w2[D / 32][4];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
-      pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
-      *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
-    }
+      for (int rr = 0; rr < 4; ++rr) {
+        const int off = dt * 32 + rr * 8 + half * 4;
+        w1[dt][rr] = *reinterpret_cast<const u32x2*>(p1 + off);
+        w2[dt][rr] = *reinterpret_cast<const u32x2*>(p2 + off);
+      }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 pk;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const float lo = g1 * bf16lo(w1[dt][rr][x]) + g2 * bf16lo(w2[dt][rr][x]) + g3 * o[dt][rr * 4 + 2 * x];
+          const float hi = g1 * bf16hi(w1[dt][rr][x]) + g2 * bf16hi(w2[dt][rr][x]) + g3 * o[dt][rr * 4 + 2 * x + 1];
+          pk[x] = pack_bf16x2(lo, hi);
+        }
+        *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+      }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+        pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+      }
+  }
   if (a.lse && half == 0)
     a.lse[(size_t(b) * a.Hq + row_h) * a.S + row_t] =
         lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
@@ -854,7 +890,9 @@ bool uses_d128(const AttnArgs& a) {
 }  // namespace
 
 bool attention_supported(const AttnArgs& a) {
-  // the additive key term exists in the float32 kernel and the D = 128 one
+  // the additive key term exists in the float32 kernel and the D = 128 one;
+  // the gated-combine epilogue in the D = 128 one
+  if (a.gate_z != nullptr && !uses_d128(a)) return false;
   return a.key_bias == nullptr || a.dtype == 0 || uses_d128(a);
 }
 

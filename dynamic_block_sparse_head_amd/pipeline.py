@@ -192,7 +192,7 @@ class NSAPlan:
     sliding branch; gated combine ([NSA] §03)."""
 
     def __init__(self, B, Hq, Hkv, S, D, cmp_len, cmp_stride, sel_block, sel_k, window, dtype,
-                 device, scale=None, per_token=False):
+                 device, scale=None, per_token=False, fuse_combine=None):
         self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
         self.cmp_len, self.cmp_stride = cmp_len, cmp_stride
         self.sel_block, self.sel_k, self.window = sel_block, sel_k, window
@@ -205,6 +205,9 @@ class NSAPlan:
         self.lse_cmp = _empty((B, Hq, S), torch.float32, device)
         # per_token: every query token ranks the blocks for its group
         self.per_token = per_token
+        # the sliding branch with the gated combine in its epilogue (D = 128,
+        # at least 4 query heads per KV head), unless asked otherwise
+        self.fuse_combine = (D == 128 and Hq // Hkv >= 4) if fuse_combine is None else fuse_combine
         rows = S if per_token else self.nb
         self.scores = _empty((B, Hkv, rows, self.nb), torch.float32, device)
         self.idx = _empty((B, Hkv, rows, sel_k), torch.int32, device)
@@ -230,6 +233,10 @@ class NSAPlan:
             L.dsa_topk_select(self.scores, self.sel_k, 0, True, self.idx, self.count)
             L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.sel_block, 0,
                                       self.scale, self.o_sel)
+        if self.fuse_combine:
+            L.dsa_nsa_window_combine(q, k, v, self.window, self.scale, self.o_cmp, self.o_sel, z,
+                                     self.out)
+            return self.out
         L.dsa_sparse_attn_prefill(q, k, v, None, None, self.sel_block, self.window, self.scale,
                                   self.o_win)
         L.dsa_nsa_combine(self.o_cmp, self.o_sel, self.o_win, z, self.out)

@@ -351,6 +351,20 @@ int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void*
                     const float* gate_logits, int B, int Hq, int S, int D, void* out,
                     void* stream);
 
+/*
+ * The sliding branch and the gated combine in one call ([NSA] §03): the
+ * window attention of dsa_sparse_attn_prefill (window mode, 64-token query
+ * blocks) whose epilogue forms out = sigmoid(z0)*o_cmp + sigmoid(z1)*o_sel +
+ * sigmoid(z2)*o_win from its own float32 result, so o_win never goes through
+ * memory.  Same layouts as dsa_nsa_combine; q, k, v as dsa_sparse_attn_prefill.
+ * Rounded once to bf16 (the two-call path rounds o_win first).  Limits: bf16,
+ * D = 128, Hq/Hkv >= 4, window <= 8000 (else DSA_E_UNSUPPORTED).
+ */
+int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* v, int B, int Hq,
+                           int Hkv, int S, int D, int window, float scale, const void* o_cmp,
+                           const void* o_sel, const float* gate_logits, void* out,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -251,3 +251,19 @@ def test_per_token_selection_validation():
     assert at(*a) == L.DSA_E_ARG
     a = list(args); a[5] = 128
     assert at(*a) == L.DSA_E_UNSUPPORTED                           # G = 32
+
+
+def test_window_combine_validation():
+    lib = L.load()
+    f = lib.dsa_nsa_window_combine
+    args = [1, FAKE, FAKE, FAKE, 1, 64, 4, 32768, 128, 512, 0.1, FAKE, FAKE, FAKE, FAKE, None]
+    a = list(args); a[8] = 64
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # D = 64
+    a = list(args); a[9] = 0
+    assert f(*a) == L.DSA_E_ARG                                    # no window
+    a = list(args); a[13] = None
+    assert f(*a) == L.DSA_E_ARG and "gate_logits" in _err()
+    a = list(args); a[5] = 8
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # G = 2: fewer than 256 rows
+    a = list(args); a[9] = 9000
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # window too long

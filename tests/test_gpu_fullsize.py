@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+from dynamic_block_sparse_head_amd import binding as L
 from dynamic_block_sparse_head_amd import configs, inputs
 from dynamic_block_sparse_head_amd.pipeline import DecodePlan, NSAPlan, PrefillPlan
 from oracle import decode as Od
@@ -89,8 +90,11 @@ def test_nsa_32k_full_size():
     c = configs.NSA_32K
     x = inputs.nsa_inputs(c, seed=0, device=DEV)
     plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
-                   c.window, x["q"].dtype, DEV)
+                   c.window, x["q"].dtype, DEV, fuse_combine=False)
     plan.run(x["q"], x["k"], x["v"], x["z"])
+    fused = torch.empty_like(plan.out)
+    L.dsa_nsa_window_combine(x["q"], x["k"], x["v"], c.window, c.scale, plan.o_cmp, plan.o_sel,
+                             x["z"], fused)
     torch.cuda.synchronize()
     g = 1
     heads = slice(g * c.G, (g + 1) * c.G)
@@ -119,3 +123,4 @@ def test_nsa_32k_full_size():
     check_bf16(to_np(plan.o_win[:, heads][:, :, rows]), o3[:, :, rows], "o_win")
     ref = On.combine(o1[:, :, rows], o2[:, :, rows], o3[:, :, rows], z[:, rows])
     check_bf16(to_np(plan.out[:, heads][:, :, rows]), ref, "nsa out")
+    check_bf16(to_np(fused[:, heads][:, :, rows]), ref, "nsa out, fused window + combine")

@@ -207,7 +207,7 @@ def test_nsa_pipeline_small():
     c = replace(configs.NSA_32K, S=2048 + 64, Hq=16, Hkv=1)
     x = inputs.nsa_inputs(c, seed=0, device=DEV)
     plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
-                   c.window, x["q"].dtype, DEV)
+                   c.window, x["q"].dtype, DEV, fuse_combine=False)
     plan.run(x["q"], x["k"], x["v"], x["z"])
     _sync()
     q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
@@ -233,6 +233,28 @@ def test_nsa_pipeline_small():
     # and end to end against the oracle's own chain
     full = On.combine(o1, o2, o3, z)
     check_bf16(to_np(plan.out), full, "nsa end to end")
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,window", [(2048 + 64, 16, 1, 512), (1000, 8, 2, 512),
+                                              (777, 4, 1, 100)])
+def test_nsa_window_combine_fused(S, Hq, Hkv, window):
+    """Sliding branch with the gated combine in its epilogue: against the
+    oracle's window branch combined with the GPU's other two branches, and
+    against the two-call path (which rounds o_win to bf16 first)."""
+    c = replace(configs.NSA_32K, S=S, Hq=Hq, Hkv=Hkv, window=window)
+    x = inputs.nsa_inputs(c, seed=S, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV, fuse_combine=False)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    fused = torch.full_like(plan.out, float("nan"))
+    L.dsa_nsa_window_combine(x["q"], x["k"], x["v"], c.window, c.scale, plan.o_cmp, plan.o_sel,
+                             x["z"], fused)
+    _sync()
+    q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
+    o3, _ = On.window_attention(q, k, v, c.window, c.scale)
+    ref = On.combine(to_np(plan.o_cmp), to_np(plan.o_sel), o3, z)
+    check_bf16(to_np(fused), ref, "fused window + combine")
+    check_bf16(to_np(fused), to_np(plan.out), "fused against two calls")
 
 
 def test_nsa_combine_only():
