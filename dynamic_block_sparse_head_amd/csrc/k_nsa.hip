@@ -56,7 +56,8 @@ constexpr int kRows = kNW * 32 * kQT;
 // grid (B*Hkv*nqb); dynamic LDS: colsum[kNW][n_cmp] floats (one row per wave,
 // so a wave adds its partial column sums without waiting for the others)
 template <int D>
-__global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
   constexpr int CSTR = D + 8;
   constexpr int CPR = D / 8;                                  // 16-byte chunks per summary
   constexpr int CPT = (32 * CPR + kNW * 64 - 1) / (kNW * 64); // chunks per thread per tile
@@ -104,11 +105,13 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
   const int total_rows = G * sb;
   const int nchunks = (total_rows + kRows - 1) / kRows;
   for (int chunk = 0; chunk < nchunks; ++chunk) {
-    // this wave's query rows, their Q operands, base-2 log-sum-exp and the
-    // last token each accumulator row may see (-1: not a row of this block)
+    // this wave's query rows, their Q operands and base-2 log-sum-exp.  A
+    // 32-row tile lies in one head (sel_block is a multiple of 32), so the
+    // token of accumulator row (rr/4)*8 + half*4 + rr%4 is tbase + (rr/4)*8
+    // + rr%4: the visibility test needs no per-row table
     bf16x8 qf[kQT][D / 16];
     float lse2[kQT][16];
-    int tlim[kQT][16];
+    int tbase[kQT];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       const int r = chunk * kRows + wave * 32 * kQT + qt * 32 + col;
@@ -124,6 +127,7 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
       }
       // rows of the accumulator tile held by this lane: (rr/4)*8 + half*4 + rr%4
       const int rbase = chunk * kRows + wave * 32 * kQT + qt * 32;
+      tbase[qt] = t0 + rbase % sb + half * 4;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int r2 = rbase + (rr >> 2) * 8 + half * 4 + (rr & 3);
@@ -131,9 +135,8 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
         const bool ok2 = h2 < G && tt <= t1;
         const float l2 = ok2 ? a.lse[(size_t(b) * a.Hq + g * G + h2) * a.S + tt] * kLog2e : 0.f;
         // rows outside the block get +inf (probability 0 everywhere); rows
-        // that see no summary have lse -inf and are cut by tlim
+        // that see no summary have lse -inf and are cut by the visibility test
         lse2[qt][rr] = !ok2 ? __builtin_inff() : (l2 == -__builtin_inff() ? 0.f : l2);
-        tlim[qt][rr] = ok2 ? tt : -1;
       }
     }
 
@@ -156,23 +159,26 @@ __global__ __launch_bounds__(kNW * 64) void k_cmp_block_scores(CmpScoreArgs a, i
       // lane holds summary kt*32+col for 16 rows of each row tile
       const int cs = kt * 32 + col;
       const int cend = cs * a.stride + a.len - 1;   // its last token
-      float part = 0.f;
+      float pp[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains
       if ((kt * 32 + 31) * a.stride + a.len - 1 <= t0) {
         // every summary of the tile ends before the block's first row: all
         // rows of the block see all of them (rows outside it add 0)
 #pragma unroll
         for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) part += fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
+          for (int rr = 0; rr < 16; ++rr) pp[rr & 3] += fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
       } else {
 #pragma unroll
-        for (int qt = 0; qt < kQT; ++qt)
+        for (int qt = 0; qt < kQT; ++qt) {
+          const int lim = tbase[qt] - cend;   // row visible iff its offset >= -lim
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const float p = fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
-            part += (cend <= tlim[qt][rr]) ? p : 0.f;
+            pp[rr & 3] += ((rr >> 2) * 8 + (rr & 3) + lim >= 0) ? p : 0.f;
           }
+        }
       }
+      float part = (pp[0] + pp[1]) + (pp[2] + pp[3]);
       part += __shfl_xor(part, 32);
       if (half == 0 && cs < a.n_cmp) my_colsum[cs] += part;
       if (kt + 1 < nkt) store(buf ^ 1);
@@ -223,7 +229,8 @@ constexpr int kTokRows = 32;
 constexpr int kPStride = 33;   // padded partial row (floats)
 
 template <int D, int HPW>
-__global__ __launch_bounds__(kNW * 64) void k_cmp_token_scores(CmpScoreArgs a, int ntt) {
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_cmp_token_scores(CmpScoreArgs a, int ntt) {
   constexpr int CSTR = D + 8;
   constexpr int CPR = D / 8;
   constexpr int CPT = (32 * CPR + kNW * 64 - 1) / (kNW * 64);
