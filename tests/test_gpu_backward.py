@@ -62,6 +62,14 @@ def test_backward_16k_shape(S):
     _parity(configs.PREFILL_16K.with_seq(S))
 
 
+def test_backward_batch_of_two():
+    """Two sequences: the staged D = 128 kernels and the generic ones."""
+    _parity(replace(configs.PREFILL_16K.with_seq(1000), B=2), seed=5)
+    _parity(replace(configs.PREFILL_16K, name="b32d64", B=2, S=600, D=64, block=32, topk=4,
+                    window=64, q_std=0.125, kv_std=0.125, v_std=0.125, needles=2,
+                    needle_alpha=0.5), seed=6)
+
+
 def test_backward_64k_shape_mixture_ragged():
     _parity(configs.PREFILL_64K.with_seq(6080))
 

@@ -1,6 +1,8 @@
 """GPU parity of the value-driven dynamic mask ([DMA] §四-§五): weights and
 block scores, selection, and attention with each kept key's weight added to
 its logit, against the float64 oracle."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -54,6 +56,10 @@ def _run(c, seed=0, plant=None):
 def test_dma_16k_shape(S):
     exact, _, _ = _run(configs.PREFILL_16K.with_seq(S))
     assert exact > 0.9
+
+
+def test_dma_batch_of_two():
+    _run(replace(configs.PREFILL_16K.with_seq(1000), B=2), seed=7)
 
 
 def test_dma_64k_shape():

@@ -121,6 +121,48 @@ def test_prefill_bf16_block32_and_d64():
     _prefill_parity(c)
 
 
+@pytest.mark.parametrize("which", ["bf16", "f32", "b32d64"])
+def test_prefill_batch_of_two(which):
+    """Two sequences in one call (every kernel indexes by sequence): the 16K
+    shape with a ragged tail, the float32 workload and the D = 64 / 32-token
+    generic kernel."""
+    if which == "bf16":
+        c = replace(configs.PREFILL_16K.with_seq(1000), B=2)
+    elif which == "f32":
+        c = replace(configs.TINY_F32, B=2)
+    else:
+        c = replace(configs.PREFILL_16K, name="b32d64", B=2, S=700, D=64, block=32, topk=5,
+                    window=64, q_std=0.125, kv_std=0.125, v_std=0.125, needles=2,
+                    needle_alpha=0.5)
+    _prefill_parity(c, seed=3)
+
+
+def test_nsa_pipeline_batch_of_two():
+    """The three-branch step on two sequences, fused and two-call combines."""
+    c = replace(configs.NSA_32K, B=2, S=1100, Hq=8, Hkv=2)
+    x = inputs.nsa_inputs(c, seed=4, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV, fuse_combine=False)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    fused = torch.empty_like(plan.out)
+    L.dsa_nsa_window_combine(x["q"], x["k"], x["v"], c.window, c.scale, plan.o_cmp, plan.o_sel,
+                             x["z"], fused)
+    _sync()
+    q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
+    gck, gcv = to_np(plan.ck), to_np(plan.cv)
+    o1, lse1, p1 = On.cmp_attention(q, gck, gcv, c.cmp_len, c.cmp_stride, c.scale)
+    check_bf16(to_np(plan.o_cmp), o1, "o_cmp")
+    sc = On.cmp_block_scores(p1, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
+    assert np.abs(to_np(plan.scores) - sc).max() < 1e-6
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    check_indices(sc, gi, gc, c.sel_k, 0, True)
+    o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale)
+    o3, _ = On.window_attention(q, k, v, c.window, c.scale)
+    ref = On.combine(o1, o2, o3, z)
+    check_bf16(to_np(plan.out), ref, "nsa out, batch of two")
+    check_bf16(to_np(fused), ref, "nsa out fused, batch of two")
+
+
 def test_prefill_all_blocks_equals_dense():
     """k >= number of blocks: the kernel reproduces dense causal attention."""
     c = configs.PREFILL_16K.with_seq(1024)

@@ -53,6 +53,10 @@ def test_per_head_16k_shape(S):
     assert _per_head(configs.PREFILL_16K.with_seq(S)) > 0.99
 
 
+def test_per_head_batch_of_two():
+    _per_head(replace(configs.PREFILL_16K.with_seq(1000), B=2), seed=8)
+
+
 def test_per_head_64k_shape_mixture():
     _per_head(configs.PREFILL_64K.with_seq(6144 - 64))
 
