@@ -62,6 +62,29 @@ def test_backward_16k_shape(S):
     _parity(configs.PREFILL_16K.with_seq(S))
 
 
+@pytest.mark.parametrize("S", [37, 65])
+def test_backward_short_sequences(S):
+    _parity(replace(configs.PREFILL_16K.with_seq(S), needles=0), seed=S)
+
+
+def test_backward_single_token():
+    """S = 1: the row's only key is itself, p = 1, so dS = p (dP - D) is zero
+    in exact arithmetic (dout.v - dout.out with out = v) and dq, dk hold only
+    the rounding of the two float32 dot products; dv = dout."""
+    c = replace(configs.PREFILL_16K.with_seq(1), needles=0)
+    x, dout, plan, got = _forward_backward(c, seed=1)
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    ref = Ob.sparse_attention_backward(to_np(x["q"]), to_np(x["k"]), to_np(x["v"]), gi, gc,
+                                       c.block, c.scale, to_np(dout))
+    assert (ref[0] == 0).all() and (ref[1] == 0).all()
+    # |dout| |v| over D = 128 terms, each product exact in float32: the two
+    # sums differ by at most ~D * 2^-24 * sum|dout v|; scaled by 1/sqrt(D) |k|
+    bound = 2.0 ** -16 * np.abs(to_np(dout)).max() * np.abs(to_np(x["v"])).max() * \
+        np.abs(to_np(x["k"])).max() * c.D
+    assert np.abs(got[0]).max() <= bound and np.abs(got[1]).max() <= bound
+    check_grad(got[2], ref[2], f"{c.name} dv")
+
+
 def test_backward_batch_of_two():
     """Two sequences: the staged D = 128 kernels and the generic ones."""
     _parity(replace(configs.PREFILL_16K.with_seq(1000), B=2), seed=5)

@@ -163,6 +163,15 @@ def test_nsa_pipeline_batch_of_two():
     check_bf16(to_np(fused), ref, "nsa out fused, batch of two")
 
 
+@pytest.mark.parametrize("S", [1, 37, 64, 65])
+@pytest.mark.parametrize("which", ["bf16", "f32"])
+def test_prefill_short_sequences(S, which):
+    """Degenerate lengths: one token, less than one block, exactly one block,
+    one block and a single-token tail."""
+    base = configs.PREFILL_16K if which == "bf16" else configs.TINY_F32
+    _prefill_parity(replace(base.with_seq(S), needles=0), seed=S)
+
+
 def test_prefill_all_blocks_equals_dense():
     """k >= number of blocks: the kernel reproduces dense causal attention."""
     c = configs.PREFILL_16K.with_seq(1024)
