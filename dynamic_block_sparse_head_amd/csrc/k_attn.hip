@@ -42,6 +42,9 @@
 #define DSA_ATTN_PRIO 1
 #endif
 // Minimum waves per SIMD the register allocation must allow.
+#ifndef DSA_ATTN_PERSIST
+#define DSA_ATTN_PERSIST 1
+#endif
 #ifndef DSA_ATTN_WAVES_PER_EU
 #define DSA_ATTN_WAVES_PER_EU 2
 #endif
@@ -445,6 +448,8 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
 //  * Query rows load through one buffer descriptor per group, and the first
 //    key of every tile is kept in a lane and read with v_readlane, so the
 //    tile loop touches memory only for the K/V stream.
+// persistent workgroups per XCD: 32 CUs, one resident workgroup each
+constexpr int kAttnSlotsPerXcd = 32;
 namespace d128 {
 constexpr int D = 128, KT = 64, NW = 8, NT = NW * 64;
 constexpr int KCH = 1040, VCH = 1088;  // chunk pitch in bytes
@@ -470,8 +475,23 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   // (a contiguous range would give some XCDs only the longest blocks) and its
   // summaries are small, so its workgroups stay in dispatch order, dealt
   // round-robin over the XCDs.
+#if DSA_ATTN_PERSIST
+  // Persistent workgroups: one per slot of the chip; workgroup j of XCD x
+  // takes items x * per_xcd + j, + nwg, ... of that XCD's range, so one
+  // item's epilogue stores drain while the next item's first loads are in
+  // flight.  The compressed branch is launched with one workgroup per item
+  // (w_step = grid = total: a single pass).
+  const int nwg = int(gridDim.x) / kNumXcd;
+  const int xcd = int(blockIdx.x) % kNumXcd, slot = int(blockIdx.x) / kNumXcd;
+  const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd * per_xcd + slot;
+  const int w_end = a.mode == MODE_CMP ? total : min(total, (xcd + 1) * per_xcd);
+  const int w_step = a.mode == MODE_CMP ? int(gridDim.x) : nwg;
+  for (int w = w_first; w < w_end; w += w_step) {
+#else
+  for (int once = 0; once < 1; ++once) {
   const int w = a.mode == MODE_CMP ? int(blockIdx.x) : xcd_work_id(per_xcd);
   if (w >= total) return;
+#endif
   const int sub = w % wg_per_qb;
   const int rest = w / wg_per_qb;
   const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
@@ -740,7 +760,7 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
   const float lt = half_sum(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (!row_ok) return;
+  if (!row_ok) continue;
   const size_t orow = ((size_t(b) * a.Hq + row_h) * a.S + row_t) * D;
   uint16_t* dst = op + orow;
   if (a.gate_z != nullptr) {
@@ -790,6 +810,7 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   if (a.lse && half == 0)
     a.lse[(size_t(b) * a.Hq + row_h) * a.S + row_t] =
         lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+  }
 }
 
 // ----------------------------------------------------------------- float32
@@ -929,10 +950,18 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int wg_per_qb = (a.sel_heads * a.block + ROWS - 1) / ROWS;
     const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+#if DSA_ATTN_PERSIST
+    // one resident workgroup per CU (registers allow two waves per SIMD); the
+    // compressed branch, whose items differ in length, keeps one workgroup
+    // per item so that the dispatcher balances them
+    const int grid = a.mode == MODE_CMP ? total : kNumXcd * min(per_xcd, kAttnSlotsPerXcd);
+#else
+    const int grid = per_xcd * kNumXcd;
+#endif
     if (a.key_bias)
-      k_attn_bf16_d128<true><<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+      k_attn_bf16_d128<true><<<grid, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     else
-      k_attn_bf16_d128<false><<<per_xcd * kNumXcd, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+      k_attn_bf16_d128<false><<<grid, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();
   }
 #endif
