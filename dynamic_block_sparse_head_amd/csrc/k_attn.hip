@@ -461,7 +461,11 @@ constexpr int kMaxTiles = 128;         // key tiles per query block (lane table)
 
 // BIAS: every key carries an additive logit term (key_bias, per KV head and
 // position), staged per tile next to K.
-template <bool BIAS>
+// UNION: per-query-head lists (one selection unit per head).  A workgroup
+// still packs the group's heads into its rows; it walks the union of its
+// heads' lists (each tile staged once) and every wave runs the products
+// only for the tiles its own head selected.
+template <bool BIAS, bool UNION = false>
 __global__ __launch_bounds__(d128::NT) __attribute__((amdgpu_waves_per_eu(DSA_ATTN_WAVES_PER_EU)))
 void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
   using namespace d128;
@@ -469,6 +473,9 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][VBYTES];
   __shared__ __attribute__((aligned(16))) float kbias[2][BIAS ? KT : 4];   // key_bias / scale
+  __shared__ uint32_t ubits[UNION ? 256 : 1];        // union bitmap over key blocks
+  __shared__ int ulist[UNION ? kMaxTiles : 1];       // union, ascending
+  __shared__ int ucount;
 
   // Contiguous work per XCD keeps a group's K/V in that XCD's L2.  The
   // compressed branch is the exception: its work grows with the query block
@@ -496,8 +503,9 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   const int rest = w / wg_per_qb;
   const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
   // (sequence, selection unit): SH query heads sharing one index list and
-  // their KV head (SH = G unless the caller selects per query head)
-  const int SH = a.sel_heads, U = a.Hq / SH;
+  // their KV head (SH = G unless the caller selects per query head; the
+  // union variant maps rows as per group and reads each head's own list)
+  const int SH = UNION ? a.Hq / a.Hkv : a.sel_heads, U = a.Hq / SH;
   const int bu = rest / nqb;
   const int b = bu / U, u = bu % U;
   const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
@@ -546,14 +554,86 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   row_range(a, t0, dummy, blk_hi);
 
   TileSpec ts;
-  const int ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
+  int ntiles;
+  uint64_t sel_lo = ~0ull, sel_hi = ~0ull;   // UNION: the tiles this wave's head selected
+  if constexpr (UNION) {
+    // union of the lists of the heads in this workgroup (64-token blocks:
+    // one tile per block), via a bitmap over the key blocks
+    const int nbk = (a.Skv + KT - 1) / KT, nwords = (nbk + 31) >> 5;
+    for (int e = threadIdx.x; e < nwords; e += NT) ubits[e] = 0u;
+    __syncthreads();
+    const int hw = (sub * ROWS + wave * 32) / a.block;   // this wave's head in the group
+    const bool hw_ok = hw < SH;
+    const size_t lrow = (size_t(b) * a.Hq + u * SH + (hw_ok ? hw : 0)) * nqb + i;
+    const int cnt = hw_ok ? max(0, min(a.count[lrow], a.idx_width)) : 0;
+    const int32_t* lst = a.idx + lrow * a.idx_width;
+    for (int e = lane; e < cnt; e += 64) {
+      const int j = lst[e];
+      if (j >= 0 && j < nbk) atomicOr(&ubits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {   // bitmap -> ascending list (lane l scans words 4l .. 4l + 3)
+      uint32_t wv[4];
+      int c4 = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int wi = lane * 4 + x;
+        wv[x] = wi < nwords ? ubits[wi] : 0u;
+        c4 += __popc(wv[x]);
+      }
+      int incl = c4;
+#pragma unroll
+      for (int o2 = 1; o2 < 64; o2 <<= 1) {
+        const int y = __shfl_up(incl, o2);
+        if (lane >= o2) incl += y;
+      }
+      int pos = incl - c4;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        uint32_t bits = wv[x];
+        while (bits) {
+          if (pos < kMaxTiles) ulist[pos] = (lane * 4 + x) * 32 + __builtin_ctz(bits);
+          ++pos;
+          bits &= bits - 1;
+        }
+      }
+      if (lane == 63) ucount = min(incl, kMaxTiles);
+    }
+    __syncthreads();
+    ntiles = ucount;
+    // membership of union tile n in this wave's list: binary search (the
+    // list is ascending)
+    auto member = [&](int n) -> bool {
+      if (n >= ntiles) return false;
+      const int j = ulist[n];
+      int lo = 0, hi = cnt - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const int v = lst[mid];
+        if (v == j) return true;
+        if (v < j) lo = mid + 1; else hi = mid - 1;
+      }
+      return false;
+    };
+    sel_lo = __ballot(member(lane));
+    sel_hi = __ballot(member(lane + 64));
+    ts.mode = MODE_INDEX;
+  } else {
+    ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
+  }
   const float c = a.scale * kLog2e;
   // First key of every tile, held across lanes (tile n in lane n % 64 of
   // word n / 64) and read back with v_readlane: no memory access and no wait
   // inside the tile loop.  The launcher sends query blocks with more than
   // kMaxTiles tiles to k_attn_bf16.
-  const int key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
-  const int key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
+  int key0_w0, key0_w1;
+  if constexpr (UNION) {
+    key0_w0 = lane < ntiles ? ulist[lane] * KT : 0;
+    key0_w1 = lane + 64 < ntiles ? ulist[lane + 64] * KT : 0;
+  } else {
+    key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
+    key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
+  }
   auto key0_of = [&](int n) __attribute__((always_inline)) -> int {
     const int lo = __builtin_amdgcn_readlane(key0_w0, n & 63);
     const int hi = __builtin_amdgcn_readlane(key0_w1, n & 63);
@@ -743,13 +823,16 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
       load_k(n + 1);
       load_v(n + 1);
     }
-    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
-    qk(n & 1);
-    __builtin_amdgcn_s_setprio(0);
-    softmax(n);
-    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
-    pv(n & 1);
-    __builtin_amdgcn_s_setprio(0);
+    const bool mine = !UNION || (((n < 64 ? sel_lo : sel_hi) >> (n & 63)) & 1);   // wave-uniform
+    if (mine) {
+      __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+      qk(n & 1);
+      __builtin_amdgcn_s_setprio(0);
+      softmax(n);
+      __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+      pv(n & 1);
+      __builtin_amdgcn_s_setprio(0);
+    }
     if (more) {
       store_k((n + 1) & 1);
       store_v((n + 1) & 1);
@@ -899,6 +982,21 @@ hipError_t run_bf16(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 namespace {
+// per-query-head lists through the union kernel: 64-token blocks, the
+// group's heads filling whole workgroups, every union within the lane table
+bool uses_d128_union(const AttnArgs& a) {
+#if defined(DSA_ATTN_LEGACY) || !DSA_ATTN_PERSIST
+  return false;
+#else
+  constexpr int ROWS = d128::NW * 32;
+  const int G = a.Hq / a.Hkv;
+  const int heads_per_wg = ROWS / 64;
+  return a.dtype == 1 && a.D == 128 && a.mode == MODE_INDEX && a.block == 64 && a.sel_heads == 1 &&
+         G > 1 && (G * 64) % ROWS == 0 && a.key_bias == nullptr && a.gate_z == nullptr &&
+         heads_per_wg * a.idx_width <= d128::kMaxTiles && (a.S + 63) / 64 <= 256 * 32;
+#endif
+}
+
 bool uses_d128(const AttnArgs& a) {
 #ifdef DSA_ATTN_LEGACY
   return false;
@@ -936,6 +1034,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   // a selection unit with fewer rows than an eight-wave workgroup (per-head
   // selection) runs the generic kernel with as many waves as it has rows
   const int unit_rows = a.sel_heads * a.block;
+#ifndef DSA_ATTN_LEGACY
+  if (uses_d128_union(a)) {
+    constexpr int ROWS = d128::NW * 32;
+    const int wg_per_qb = ((a.Hq / a.Hkv) * a.block + ROWS - 1) / ROWS;
+    const int total = a.B * a.Hkv * nqb * wg_per_qb;
+    const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+    const int grid = kNumXcd * min(per_xcd, kAttnSlotsPerXcd);
+    k_attn_bf16_d128<false, true><<<grid, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    return hipGetLastError();
+  }
+#endif
   if (unit_rows < 256) {
     const int nw = unit_rows <= 64 ? 2 : 4;
     if (a.D == 128)
