@@ -58,7 +58,8 @@ def _build(full_pages, n_append, Hkv=8, G=4, D=128, page=64, spare=5, seed=0):
                 tok_v=tok_v, max_pages=max_pages, plan=plan)
 
 
-@pytest.mark.parametrize("full_pages,n_append", [([10, 3, 0, 7], 101), ([4, 4], 64), ([2, 9, 1], 1)])
+@pytest.mark.parametrize("full_pages,n_append", [([10, 3, 0, 7], 101), ([4, 4], 64), ([2, 9, 1], 1),
+                                                ([0, 5, 2], 0)])
 def test_paged_decode_parity(full_pages, n_append):
     c = _build(full_pages, n_append)
     page, lens, table = c["page"], c["lens"], c["table"]
