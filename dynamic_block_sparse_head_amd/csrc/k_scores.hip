@@ -95,9 +95,10 @@ __global__ __launch_bounds__(kThreads) void k_pool(const T* __restrict__ q, cons
 // heads per sequence).  32x32 output tile per workgroup; thread (ti, tj)
 // owns rows ti, ti+16 and columns tj, tj+16, i.e. four independent float64
 // dot products fed from LDS (two query and two key values per step).
+template <int D>
 __global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restrict__ qs,
                                                          const double* __restrict__ kb, int nb,
-                                                         int D, int U, int Hkv,
+                                                         int U, int Hkv,
                                                          float* __restrict__ scores) {
   extern __shared__ double lds[];  // [32][D+2] queries, then [32][D+2] keys
   const int bg = blockIdx.z;
@@ -118,14 +119,24 @@ __global__ __launch_bounds__(kThreads) void k_pooled_dot(const double* __restric
   const int ld = D + 2;  // even: rows stay 16-byte aligned
   double* lq = lds;
   double* lk = lds + 32 * ld;
-  const int hd = D / 2;
-  for (int e = threadIdx.x; e < 32 * hd; e += kThreads) {
+  // all loads of the two 32-row slabs are issued before any LDS store
+  constexpr int hd = D / 2, NPT = 32 * hd / kThreads;
+  double2 ra[NPT], rc[NPT];
+#pragma unroll
+  for (int x = 0; x < NPT; ++x) {
+    const int e = threadIdx.x + x * kThreads;
     const int r = e / hd, d = (e % hd) * 2;
-    double2 a = {0.0, 0.0}, c = {0.0, 0.0};
-    if (i0 + r < nb) a = *reinterpret_cast<const double2*>(qs + (size_t(bg) * nb + i0 + r) * D + d);
-    if (j0 + r < nb) c = *reinterpret_cast<const double2*>(kb + (size_t(kvh) * nb + j0 + r) * D + d);
-    *reinterpret_cast<double2*>(lq + r * ld + d) = a;
-    *reinterpret_cast<double2*>(lk + r * ld + d) = c;
+    ra[x] = double2{0.0, 0.0};
+    rc[x] = double2{0.0, 0.0};
+    if (i0 + r < nb) ra[x] = *reinterpret_cast<const double2*>(qs + (size_t(bg) * nb + i0 + r) * D + d);
+    if (j0 + r < nb) rc[x] = *reinterpret_cast<const double2*>(kb + (size_t(kvh) * nb + j0 + r) * D + d);
+  }
+#pragma unroll
+  for (int x = 0; x < NPT; ++x) {
+    const int e = threadIdx.x + x * kThreads;
+    const int r = e / hd, d = (e % hd) * 2;
+    *reinterpret_cast<double2*>(lq + r * ld + d) = ra[x];
+    *reinterpret_cast<double2*>(lk + r * ld + d) = rc[x];
   }
   __syncthreads();
   const double* q0 = lq + ti * ld;
@@ -384,8 +395,12 @@ hipError_t launch_pooled_scores(const PoolScoreArgs& a, hipStream_t s) {
                                             a.block, a.sel_heads, a.Hkv, a.ws_q, a.ws_k);
   const int nt = (nb + 31) / 32;
   const size_t lds = size_t(2) * 32 * (a.D + 2) * sizeof(double);
-  k_pooled_dot<<<dim3(nt, nt, a.B * U), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, a.D, U, a.Hkv,
-                                                            a.scores);
+  if (a.D == 128)
+    k_pooled_dot<128><<<dim3(nt, nt, a.B * U), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, U, a.Hkv,
+                                                                   a.scores);
+  else
+    k_pooled_dot<64><<<dim3(nt, nt, a.B * U), kThreads, lds, s>>>(a.ws_q, a.ws_k, nb, U, a.Hkv,
+                                                                  a.scores);
   return hipGetLastError();
 }
 
