@@ -73,6 +73,21 @@ def _timed(fn, iters, torch):
     return e0.elapsed_time(e1) / iters
 
 
+def _timed_each(fn, iters, torch):
+    """Per-call ms of `iters` calls, each bracketed by its own HIP events on
+    the current stream: (median, min, max)."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for e0, e1 in ev:
+        e0.record(s)
+        fn()
+        e1.record(s)
+    ev[-1][1].synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    return t[len(t) // 2], t[0], t[-1]
+
+
 def bench_prefill(args, torch):
     from dynamic_block_sparse_head_amd import configs, inputs
     from dynamic_block_sparse_head_amd.pipeline import GraphedStep, PrefillPlan
@@ -98,6 +113,7 @@ def bench_prefill(args, torch):
     ms_scores = _timed(lambda: plan.score(q, k), reps, torch)
     ms_topk = _timed(plan.select, reps, torch)
     ms_attn = _timed(lambda: plan.attend(q, k, v), reps, torch)
+    attn_each = _timed_each(lambda: plan.attend(q, k, v), max(reps, 20), torch)
     count = plan.count.to(torch.int64)
     sel = int(count.sum().item())                      # (group, query block, key block) triples
     flops = 4.0 * c.D * c.block * c.block * c.G * sel  # each selected block as a full tile
@@ -105,6 +121,7 @@ def bench_prefill(args, torch):
     return {
         "cfg": c, "ms_step": ms_step, "wall_s": wall, "ms_scores": ms_scores, "ms_topk": ms_topk,
         "ms_attn": ms_attn, "ms_graph": ms_graph, "selected_block_pairs": sel, "effective_flops": flops,
+        "attn_each": attn_each,
         "tokens_per_step": tokens,
     }
 
@@ -562,6 +579,7 @@ def main():
             "prefill": {"step_ms_graph_replay": round(r["ms_graph"], 4),
                         "scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
                         "attn_ms": round(r["ms_attn"], 4),
+                        "attn_ms_per_call_median_min_max": [round(x, 4) for x in r["attn_each"]],
                         "attn_tokens_per_s": round(c.S / (r["ms_attn"] * 1e-3), 1),
                         "selected_block_pairs": r["selected_block_pairs"],
                         "effective_tflops": round(tflops, 2)},
