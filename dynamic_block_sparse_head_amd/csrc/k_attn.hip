@@ -41,10 +41,15 @@
 #ifndef DSA_ATTN_PRIO
 #define DSA_ATTN_PRIO 1
 #endif
-// Minimum waves per SIMD the register allocation must allow.
+// D = 128: persistent workgroups (one per CU slot) walk the work items.
 #ifndef DSA_ATTN_PERSIST
 #define DSA_ATTN_PERSIST 1
 #endif
+// D = 128 epilogue: output rows staged through LDS for whole-row stores.
+#ifndef DSA_ATTN_OSTAGE
+#define DSA_ATTN_OSTAGE 1
+#endif
+// Minimum waves per SIMD the register allocation must allow.
 #ifndef DSA_ATTN_WAVES_PER_EU
 #define DSA_ATTN_WAVES_PER_EU 2
 #endif
@@ -476,6 +481,10 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   __shared__ uint32_t ubits[UNION ? 256 : 1];        // union bitmap over key blocks
   __shared__ int ulist[UNION ? kMaxTiles : 1];       // union, ascending
   __shared__ int ucount;
+  // epilogue: each wave's 32 output rows, 16-byte chunks XOR-swizzled by
+  // row, and their log-sum-exp values
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[DSA_ATTN_OSTAGE ? NW : 1][32 * D * 2];
+  __shared__ float lstage[DSA_ATTN_OSTAGE ? NW : 1][32];
 
   // Contiguous work per XCD keeps a group's K/V in that XCD's L2.  The
   // compressed branch is the exception: its work grows with the query block
@@ -484,160 +493,37 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   // round-robin over the XCDs.
 #if DSA_ATTN_PERSIST
   // Persistent workgroups: one per slot of the chip; workgroup j of XCD x
-  // takes items x * per_xcd + j, + nwg, ... of that XCD's range, so one
-  // item's epilogue stores drain while the next item's first loads are in
-  // flight.  The compressed branch is launched with one workgroup per item
-  // (w_step = grid = total: a single pass).
+  // takes items x * per_xcd + j, + nwg, ... of that XCD's range.  The
+  // compressed branch is launched with one workgroup per item (w_step =
+  // grid = total: a single pass).
   const int nwg = int(gridDim.x) / kNumXcd;
   const int xcd = int(blockIdx.x) % kNumXcd, slot = int(blockIdx.x) / kNumXcd;
   const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd * per_xcd + slot;
   const int w_end = a.mode == MODE_CMP ? total : min(total, (xcd + 1) * per_xcd);
   const int w_step = a.mode == MODE_CMP ? int(gridDim.x) : nwg;
-  for (int w = w_first; w < w_end; w += w_step) {
 #else
-  for (int once = 0; once < 1; ++once) {
-  const int w = a.mode == MODE_CMP ? int(blockIdx.x) : xcd_work_id(per_xcd);
-  if (w >= total) return;
+  const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd_work_id(per_xcd);
+  const int w_end = min(total, w_first + 1), w_step = 1;
 #endif
-  const int sub = w % wg_per_qb;
-  const int rest = w / wg_per_qb;
-  const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
+  if (w_first >= w_end) return;
+
   // (sequence, selection unit): SH query heads sharing one index list and
   // their KV head (SH = G unless the caller selects per query head; the
   // union variant maps rows as per group and reads each head's own list)
   const int SH = UNION ? a.Hq / a.Hkv : a.sel_heads, U = a.Hq / SH;
-  const int bu = rest / nqb;
-  const int b = bu / U, u = bu % U;
-  const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
-  const int t0 = i * a.block;
-  const int t1 = min(a.S, t0 + a.block) - 1;
-
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31, half = lane >> 5;
-
   const uint32_t kv_bytes = uint32_t(a.Skv) * D * 2;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D, kv_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D, kv_bytes);
-
-  // this lane's query row; rows past the group or the sequence read zeros
-  const int r = sub * ROWS + wave * 32 + col;
-  const int hh = r / a.block;
-  const int row_t = t0 + r % a.block;
-  const bool row_ok = hh < SH && row_t < a.S;
-  const int row_h = u * SH + (row_ok ? hh : 0);
-  bf16x8 qf[D / 16];
-  {
-    // one descriptor over the unit's query heads; rows that are not ours
-    // get an offset past its end and read zeros
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
-        static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(u) * SH) * a.S * D,
-        uint32_t(SH) * a.S * D * 2);
-    const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + half * 8) * 2) : 0x80000000u;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, ks * 32, 0));
-  }
-
-  floatx16 o[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float m = -__builtin_inff(), l = 0.f;
-  int row_lo, row_hi;
-  row_range(a, row_t, row_lo, row_hi);
-  row_lo -= half * 4;
-  row_hi -= half * 4;
-  int blk_lo, blk_hi, dummy;
-  row_range(a, t1, blk_lo, dummy);
-  row_range(a, t0, dummy, blk_hi);
-
-  TileSpec ts;
-  int ntiles;
-  uint64_t sel_lo = ~0ull, sel_hi = ~0ull;   // UNION: the tiles this wave's head selected
-  if constexpr (UNION) {
-    // union of the lists of the heads in this workgroup (64-token blocks:
-    // one tile per block), via a bitmap over the key blocks
-    const int nbk = (a.Skv + KT - 1) / KT, nwords = (nbk + 31) >> 5;
-    for (int e = threadIdx.x; e < nwords; e += NT) ubits[e] = 0u;
-    __syncthreads();
-    const int hw = (sub * ROWS + wave * 32) / a.block;   // this wave's head in the group
-    const bool hw_ok = hw < SH;
-    const size_t lrow = (size_t(b) * a.Hq + u * SH + (hw_ok ? hw : 0)) * nqb + i;
-    const int cnt = hw_ok ? max(0, min(a.count[lrow], a.idx_width)) : 0;
-    const int32_t* lst = a.idx + lrow * a.idx_width;
-    for (int e = lane; e < cnt; e += 64) {
-      const int j = lst[e];
-      if (j >= 0 && j < nbk) atomicOr(&ubits[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    if (wave == 0) {   // bitmap -> ascending list (lane l scans words 4l .. 4l + 3)
-      uint32_t wv[4];
-      int c4 = 0;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int wi = lane * 4 + x;
-        wv[x] = wi < nwords ? ubits[wi] : 0u;
-        c4 += __popc(wv[x]);
-      }
-      int incl = c4;
-#pragma unroll
-      for (int o2 = 1; o2 < 64; o2 <<= 1) {
-        const int y = __shfl_up(incl, o2);
-        if (lane >= o2) incl += y;
-      }
-      int pos = incl - c4;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        uint32_t bits = wv[x];
-        while (bits) {
-          if (pos < kMaxTiles) ulist[pos] = (lane * 4 + x) * 32 + __builtin_ctz(bits);
-          ++pos;
-          bits &= bits - 1;
-        }
-      }
-      if (lane == 63) ucount = min(incl, kMaxTiles);
-    }
-    __syncthreads();
-    ntiles = ucount;
-    // membership of union tile n in this wave's list: binary search (the
-    // list is ascending)
-    auto member = [&](int n) -> bool {
-      if (n >= ntiles) return false;
-      const int j = ulist[n];
-      int lo = 0, hi = cnt - 1;
-      while (lo <= hi) {
-        const int mid = (lo + hi) >> 1;
-        const int v = lst[mid];
-        if (v == j) return true;
-        if (v < j) lo = mid + 1; else hi = mid - 1;
-      }
-      return false;
-    };
-    sel_lo = __ballot(member(lane));
-    sel_hi = __ballot(member(lane + 64));
-    ts.mode = MODE_INDEX;
-  } else {
-    ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
-  }
   const float c = a.scale * kLog2e;
-  // First key of every tile, held across lanes (tile n in lane n % 64 of
-  // word n / 64) and read back with v_readlane: no memory access and no wait
-  // inside the tile loop.  The launcher sends query blocks with more than
-  // kMaxTiles tiles to k_attn_bf16.
-  int key0_w0, key0_w1;
-  if constexpr (UNION) {
-    key0_w0 = lane < ntiles ? ulist[lane] * KT : 0;
-    key0_w1 = lane + 64 < ntiles ? ulist[lane + 64] * KT : 0;
-  } else {
-    key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
-    key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
-  }
-  auto key0_of = [&](int n) __attribute__((always_inline)) -> int {
-    const int lo = __builtin_amdgcn_readlane(key0_w0, n & 63);
-    const int hi = __builtin_amdgcn_readlane(key0_w1, n & 63);
-    return n < 64 ? lo : hi;
+  const float inv_scale = 1.f / a.scale;
+  // The lane index as an opaque value: per-item address arithmetic derived
+  // from it is redone per item instead of being hoisted out of the item
+  // loop, where it would hold registers across the tile loop.
+  auto item_lane = [&]() __attribute__((always_inline)) -> int {
+    int x = lane;
+    asm volatile("" : "+v"(x));
+    return x;
   };
 
   // Staging: wave w moves K chunks and V chunks 2w and 2w + 1 of a tile;
@@ -652,12 +538,32 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
       vvo[j2] = uint32_t((16 * (j / 4) + 4 * q + (j % 4)) * 256 + c16 * 16);
     }
   }
+  // per-lane byte offsets of the operand reads (the rest are immediates)
+  const uint32_t k_rd = (col & 15) * KCH + (col >> 4) * 256 + half * 16;
+  const uint32_t v_rd = ((lane & 15) >> 2) * VCH + half * 256 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+
+  // ---- the running item: set by begin() while the previous item finishes
+  int sub = 0, b = 0, u = 0, t0 = 0;       // unit coordinates (uniform)
+  int row_t = 0, row_h = 0;                // this lane's query row
+  bool row_ok = false;
+  int row_lo = 0, row_hi = -1, blk_lo = 0, blk_hi = -1;
+  int ntiles = 0;
+  uint64_t sel_lo = ~0ull, sel_hi = ~0ull;   // UNION: the tiles this wave's head selected
+  // First key of every tile, held across lanes (tile n in lane n % 64 of
+  // word n / 64) and read back with v_readlane: no memory access and no wait
+  // inside the tile loop.  The launcher sends query blocks with more than
+  // kMaxTiles tiles to k_attn_bf16.
+  int key0_w0 = 0, key0_w1 = 0;
+  __amdgpu_buffer_rsrc_t krs = make_rsrc(a.k, 0u), vrs = make_rsrc(a.v, 0u), brs = make_rsrc(a.q, 0u);
+  bf16x8 qf[D / 16];
   u32x4 stk[2], stv[2];
   u32x4 stb = {0u, 0u, 0u, 0u};   // BIAS: four key terms (wave 0, lanes 0..15)
-  // (BIAS only; without it the descriptor covers nothing and is never used)
-  const __amdgpu_buffer_rsrc_t brs =
-      make_rsrc(BIAS ? a.key_bias + size_t(bg) * a.Skv : a.q, BIAS ? uint32_t(a.Skv) * 4 : 0u);
-  const float inv_scale = 1.f / a.scale;
+
+  auto key0_of = [&](int n) __attribute__((always_inline)) -> int {
+    const int lo = __builtin_amdgcn_readlane(key0_w0, n & 63);
+    const int hi = __builtin_amdgcn_readlane(key0_w1, n & 63);
+    return n < 64 ? lo : hi;
+  };
   auto load_k = [&](int n) __attribute__((always_inline)) {
     const uint32_t base = uint32_t(key0_of(n)) * uint32_t(D * 2);
 #pragma unroll
@@ -689,12 +595,161 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
       *reinterpret_cast<u32x4*>(&vbuf[buf][(2 * wave + j2) * VCH + lane * 16]) = stv[j2];
   };
 
-  // per-lane byte offsets of the operand reads (the rest are immediates)
-  const uint32_t k_rd = (col & 15) * KCH + (col >> 4) * 256 + half * 16;
-  const uint32_t v_rd = ((lane & 15) >> 2) * VCH + half * 256 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  // list row of item w in index mode (per selection unit and query block)
+  auto item_lrow = [&](int w) __attribute__((always_inline)) -> size_t {
+    const int rest = w / wg_per_qb;
+    return size_t(rest / nqb) * nqb + (nqb - 1 - rest % nqb);
+  };
+  const bool prefetch_list = !UNION && a.mode == MODE_INDEX;
+  // index mode: the next item's count and list entries lane, lane + 64,
+  // requested while the running item computes
+  int nx_cnt = 0, nx_e0 = 0, nx_e1 = 0;
+  auto fetch_list = [&](int w) __attribute__((always_inline)) {
+    if constexpr (!UNION) {
+      const size_t lrow = item_lrow(w);
+      const int32_t* lst = a.idx + lrow * a.idx_width;
+      const int ln = item_lane();
+      nx_cnt = a.count[lrow];
+      nx_e0 = ln < a.idx_width ? lst[ln] : 0;
+      nx_e1 = ln + 64 < a.idx_width ? lst[ln + 64] : 0;
+    }
+  };
+
+  // begin(w): coordinates of item w, its query rows (registers), its key
+  // tiles and the loads of its first tile.  In index mode the list comes
+  // from fetch_list(w), issued earlier.
+  auto begin = [&](int w) __attribute__((always_inline)) {
+    sub = w % wg_per_qb;
+    const int rest = w / wg_per_qb;
+    const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
+    const int bu = rest / nqb;
+    b = bu / U;
+    u = bu % U;
+    const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
+    t0 = i * a.block;
+    const int t1 = min(a.S, t0 + a.block) - 1;
+    krs = make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D, kv_bytes);
+    vrs = make_rsrc(static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D, kv_bytes);
+    // (BIAS only; without it the descriptor covers nothing and is never used)
+    brs = make_rsrc(BIAS ? a.key_bias + size_t(bg) * a.Skv : a.q, BIAS ? uint32_t(a.Skv) * 4 : 0u);
+
+    // this lane's query row; rows past the group or the sequence read zeros
+    const int ln = item_lane();
+    const int r = sub * ROWS + wave * 32 + (ln & 31);
+    const int hh = r / a.block;
+    row_t = t0 + r % a.block;
+    row_ok = hh < SH && row_t < a.S;
+    row_h = u * SH + (row_ok ? hh : 0);
+    row_range(a, row_t, row_lo, row_hi);
+    row_lo -= half * 4;
+    row_hi -= half * 4;
+    int dummy;
+    row_range(a, t1, blk_lo, dummy);
+    row_range(a, t0, dummy, blk_hi);
+
+    if constexpr (UNION) {
+      // union of the lists of the heads in this workgroup (64-token blocks:
+      // one tile per block), via a bitmap over the key blocks
+      const int nbk = (a.Skv + KT - 1) / KT, nwords = (nbk + 31) >> 5;
+      for (int e = threadIdx.x; e < nwords; e += NT) ubits[e] = 0u;
+      __syncthreads();
+      const int hw = (sub * ROWS + wave * 32) / a.block;   // this wave's head in the group
+      const bool hw_ok = hw < SH;
+      const size_t lrow = (size_t(b) * a.Hq + u * SH + (hw_ok ? hw : 0)) * nqb + i;
+      const int cnt = hw_ok ? max(0, min(a.count[lrow], a.idx_width)) : 0;
+      const int32_t* lst = a.idx + lrow * a.idx_width;
+      for (int e = lane; e < cnt; e += 64) {
+        const int j = lst[e];
+        if (j >= 0 && j < nbk) atomicOr(&ubits[j >> 5], 1u << (j & 31));
+      }
+      __syncthreads();
+      if (wave == 0) {   // bitmap -> ascending list (lane l scans words 4l .. 4l + 3)
+        uint32_t wv[4];
+        int c4 = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int wi = lane * 4 + x;
+          wv[x] = wi < nwords ? ubits[wi] : 0u;
+          c4 += __popc(wv[x]);
+        }
+        int incl = c4;
+#pragma unroll
+        for (int o2 = 1; o2 < 64; o2 <<= 1) {
+          const int y = __shfl_up(incl, o2);
+          if (lane >= o2) incl += y;
+        }
+        int pos = incl - c4;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          uint32_t bits = wv[x];
+          while (bits) {
+            if (pos < kMaxTiles) ulist[pos] = (lane * 4 + x) * 32 + __builtin_ctz(bits);
+            ++pos;
+            bits &= bits - 1;
+          }
+        }
+        if (lane == 63) ucount = min(incl, kMaxTiles);
+      }
+      __syncthreads();
+      ntiles = ucount;
+      // membership of union tile n in this wave's list: binary search (the
+      // list is ascending)
+      auto member = [&](int n) -> bool {
+        if (n >= ntiles) return false;
+        const int j = ulist[n];
+        int lo = 0, hi = cnt - 1;
+        while (lo <= hi) {
+          const int mid = (lo + hi) >> 1;
+          const int v = lst[mid];
+          if (v == j) return true;
+          if (v < j) lo = mid + 1; else hi = mid - 1;
+        }
+        return false;
+      };
+      sel_lo = __ballot(member(lane));
+      sel_hi = __ballot(member(lane + 64));
+      key0_w0 = lane < ntiles ? ulist[lane] * KT : 0;
+      key0_w1 = lane + 64 < ntiles ? ulist[lane + 64] * KT : 0;
+    } else if (a.mode == MODE_INDEX) {
+      // tile n is part n % tpb of listed block n / tpb (list entries past
+      // the count are never used)
+      const int tpb = a.block / KT;
+      ntiles = max(0, min(nx_cnt, a.idx_width)) * tpb;
+      auto key0 = [&](int n) -> int {
+        const int e = n / tpb;
+        const int v0 = __shfl(nx_e0, e & 63), v1 = __shfl(nx_e1, e & 63);
+        return (e < 64 ? v0 : v1) * a.block + (n % tpb) * KT;
+      };
+      const int k0 = key0(ln), k1 = key0(ln + 64);
+      key0_w0 = ln < ntiles ? k0 : 0;
+      key0_w1 = ln + 64 < ntiles ? k1 : 0;
+    } else {
+      TileSpec ts;
+      ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
+      key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
+      key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
+    }
+    {
+      // one descriptor over the unit's query heads; rows that are not ours
+      // get an offset past its end and read zeros
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+          static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(u) * SH) * a.S * D,
+          uint32_t(SH) * a.S * D * 2);
+      const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + (ln >> 5) * 8) * 2) : 0x80000000u;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, ks * 32, 0));
+    }
+    if (ntiles > 0) {
+      load_k(0);
+      load_v(0);
+    }
+  };
 
   float alpha = 1.f;     // pending rescale of o (lazy softmax)
   bool rescale = false;
+  floatx16 o[D / 32];
+  float m, l;
   floatx16 s[KT / 32];   // S^T of the tile between its Q.K and its softmax
   bf16x8 pb[KT / 16];    // P^T of the tile between its softmax and its P.V
 
@@ -810,89 +865,181 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
     l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
-  if (ntiles > 0) {
-    load_k(0);
-    load_v(0);
-    store_k(0);
-    store_v(0);
-  }
-  __syncthreads();
-  for (int n = 0; n < ntiles; ++n) {
-    const bool more = n + 1 < ntiles;
-    if (more) {
-      load_k(n + 1);
-      load_v(n + 1);
+  // Per item: the first tile goes to LDS (its loads were issued while the
+  // previous item finished), then the previous item's staged output leaves,
+  // then the tile loop; the epilogue requests the next item's query rows and
+  // first tile before it stages this item's output, so no wait for those
+  // loads ever covers output stores.
+  bool pend = false;   // staged output of the previous item still in LDS (uniform)
+  int p_b = 0, p_u = 0, p_sub = 0, p_t0 = 0;
+  uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
+  auto flush = [&]() __attribute__((always_inline)) {
+#if DSA_ATTN_OSTAGE
+    // the wave's 32 rows: consecutive positions of one head (the launcher
+    // sends blocks that are not a multiple of 32 rows elsewhere); four whole
+    // 256-byte rows per store, marked streaming (nothing here reads them
+    // back, and they should not displace K/V lines from the caches)
+    const uint8_t* stg = &ostage[wave][0];
+    const int rw = p_sub * ROWS + wave * 32;
+    const int hr = rw / a.block;
+    const int tr0 = p_t0 + rw % a.block;
+    if (hr < SH) {
+      uint16_t* wb = op + ((size_t(p_b) * a.Hq + p_u * SH + hr) * a.S + tr0) * D;
+      const int ln = item_lane();
+      const int c16 = ln & 15;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int R = 4 * j + (ln >> 4);
+        const u32x4 v4 = *reinterpret_cast<const u32x4*>(stg + R * 256 + ((c16 ^ (R & 15)) << 4));
+        if (tr0 + R < a.S) __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(wb + R * D + c16 * 8));
+      }
+      if (a.lse && ln < 32 && tr0 + ln < a.S)
+        a.lse[(size_t(p_b) * a.Hq + p_u * SH + hr) * a.S + tr0 + ln] = lstage[wave][ln];
     }
-    const bool mine = !UNION || (((n < 64 ? sel_lo : sel_hi) >> (n & 63)) & 1);   // wave-uniform
-    if (mine) {
-      __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
-      qk(n & 1);
-      __builtin_amdgcn_s_setprio(0);
-      softmax(n);
-      __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
-      pv(n & 1);
-      __builtin_amdgcn_s_setprio(0);
-    }
-    if (more) {
-      store_k((n + 1) & 1);
-      store_v((n + 1) & 1);
+#endif
+  };
+
+  if (prefetch_list) fetch_list(w_first);
+  begin(w_first);
+  for (int w = w_first; w < w_end; w += w_step) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+    m = -__builtin_inff();
+    l = 0.f;
+    alpha = 1.f;
+    rescale = false;
+    // the next item, or this one again after the last: begin() and
+    // fetch_list() then run unconditionally (their registers need no merge
+    // of two versions; the repeated loads are never used)
+    const int w_next = w + w_step < w_end ? w + w_step : w;   // uniform
+
+    if (ntiles > 0) {
+      store_k(0);
+      store_v(0);
     }
     __syncthreads();
-  }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): query rows and first tile landed on every path
+    if (pend) {
+      flush();
+      pend = false;
+    }
+    if (prefetch_list) fetch_list(w_next);
+    for (int n = 0; n < ntiles; ++n) {
+      const bool more = n + 1 < ntiles;
+      if (more) {
+        load_k(n + 1);
+        load_v(n + 1);
+      }
+      const bool mine = !UNION || (((n < 64 ? sel_lo : sel_hi) >> (n & 63)) & 1);   // wave-uniform
+      if (mine) {
+        __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+        qk(n & 1);
+        __builtin_amdgcn_s_setprio(0);
+        softmax(n);
+        __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+        pv(n & 1);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (more) {
+        store_k((n + 1) & 1);
+        store_v((n + 1) & 1);
+      }
+      __syncthreads();
+    }
 
-  uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
-  const float lt = half_sum(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (!row_ok) continue;
-  const size_t orow = ((size_t(b) * a.Hq + row_h) * a.S + row_t) * D;
-  uint16_t* dst = op + orow;
-  if (a.gate_z != nullptr) {
-    // gated combine with the other two branches' outputs (this branch in
-    // float32, the others as stored), rounded once
-    const float* z = a.gate_z + ((size_t(b) * a.S + row_t) * a.Hq + row_h) * 3;
-    const float g1 = 1.f / (1.f + __expf(-z[0]));
-    const float g2 = 1.f / (1.f + __expf(-z[1]));
-    const float g3 = inv / (1.f + __expf(-z[2]));
-    const uint16_t* p1 = static_cast<const uint16_t*>(a.gate_o1) + orow;
-    const uint16_t* p2 = static_cast<const uint16_t*>(a.gate_o2) + orow;
-    // all loads first: the stores below may alias them as far as the
-    // compiler knows, so interleaving would serialise every load
-    u32x2 w1[D / 32][4], w2[D / 32][4];
+    const int e_sub = sub, e_b = b, e_u = u, e_t0 = t0;
+    const int e_row_t = row_t, e_row_h = row_h;
+    const bool e_row_ok = row_ok;
+    const float lt = half_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse_v = lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+    const size_t orow = ((size_t(e_b) * a.Hq + e_row_h) * a.S + e_row_t) * D;
+    uint16_t* dst = op + orow;
+    if (a.gate_z != nullptr || !DSA_ATTN_OSTAGE) {
+      if (a.gate_z != nullptr) {
+        if (e_row_ok) {
+          // gated combine with the other two branches' outputs (this branch
+          // in float32, the others as stored), rounded once
+          const float* z = a.gate_z + ((size_t(e_b) * a.S + e_row_t) * a.Hq + e_row_h) * 3;
+          const float g1 = 1.f / (1.f + __expf(-z[0]));
+          const float g2 = 1.f / (1.f + __expf(-z[1]));
+          const float g3 = inv / (1.f + __expf(-z[2]));
+          const uint16_t* p1 = static_cast<const uint16_t*>(a.gate_o1) + orow;
+          const uint16_t* p2 = static_cast<const uint16_t*>(a.gate_o2) + orow;
+          // a half row's loads before its stores: the stores may alias them
+          // as far as the compiler knows, so interleaving would serialise
+          // every load
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+          for (int d2 = 0; d2 < D / 64; ++d2) {
+            u32x2 w1[2][4], w2[2][4];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int off = dt * 32 + rr * 8 + half * 4;
-        w1[dt][rr] = *reinterpret_cast<const u32x2*>(p1 + off);
-        w2[dt][rr] = *reinterpret_cast<const u32x2*>(p2 + off);
-      }
+            for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+              for (int rr = 0; rr < 4; ++rr) {
+                const int off = (2 * d2 + dh) * 32 + rr * 8 + half * 4;
+                w1[dh][rr] = *reinterpret_cast<const u32x2*>(p1 + off);
+                w2[dh][rr] = *reinterpret_cast<const u32x2*>(p2 + off);
+              }
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 pk;
+            for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const float lo = g1 * bf16lo(w1[dt][rr][x]) + g2 * bf16lo(w2[dt][rr][x]) + g3 * o[dt][rr * 4 + 2 * x];
-          const float hi = g1 * bf16hi(w1[dt][rr][x]) + g2 * bf16hi(w2[dt][rr][x]) + g3 * o[dt][rr * 4 + 2 * x + 1];
-          pk[x] = pack_bf16x2(lo, hi);
+              for (int rr = 0; rr < 4; ++rr) {
+                const int dt = 2 * d2 + dh;
+                u32x2 pk;
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                  const float lo = g1 * bf16lo(w1[dh][rr][x]) + g2 * bf16lo(w2[dh][rr][x]) + g3 * o[dt][rr * 4 + 2 * x];
+                  const float hi = g1 * bf16hi(w1[dh][rr][x]) + g2 * bf16hi(w2[dh][rr][x]) + g3 * o[dt][rr * 4 + 2 * x + 1];
+                  pk[x] = pack_bf16x2(lo, hi);
+                }
+                *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+              }
+          }
         }
-        *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
-      }
-  } else {
+      } else {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
-        pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+          for (int rr = 0; rr < 4; ++rr) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+            pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+            if (e_row_ok) *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+          }
       }
+      if (a.lse && half == 0 && e_row_ok) a.lse[(size_t(e_b) * a.Hq + e_row_h) * a.S + e_row_t] = lse_v;
+    }
+    begin(w_next);
+    if (a.gate_z == nullptr && DSA_ATTN_OSTAGE) {
+      // A lane holds 8-byte pieces of its own row, so direct stores would
+      // touch 32 rows per instruction.  The wave's 32 rows go to LDS (16-byte
+      // chunks XOR-swizzled by row) and leave as whole rows in flush().
+      uint8_t* stg = &ostage[wave][0];
+      const int ln = item_lane();
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+          pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(stg + (ln & 31) * 256 + (((dt * 4 + rr) ^ (ln & 15)) << 4) + (ln >> 5) * 8) = pk;
+        }
+      if (ln < 32) lstage[wave][ln] = lse_v;
+      pend = true;
+      p_b = e_b;
+      p_u = e_u;
+      p_sub = e_sub;
+      p_t0 = e_t0;
+    }
   }
-  if (a.lse && half == 0)
-    a.lse[(size_t(b) * a.Hq + row_h) * a.S + row_t] =
-        lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+  if (pend) {   // this wave's own LDS writes, read back in program order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    flush();
   }
 }
 
@@ -1002,7 +1149,7 @@ bool uses_d128(const AttnArgs& a) {
   return false;
 #else
   const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
-  return a.dtype == 1 && a.D == 128 && !kt32 && a.sel_heads * a.block >= 256 &&
+  return a.dtype == 1 && a.D == 128 && !kt32 && a.block % 32 == 0 && a.sel_heads * a.block >= 256 &&
          attn_max_tiles(a, 64) <= d128::kMaxTiles;
 #endif
 }
