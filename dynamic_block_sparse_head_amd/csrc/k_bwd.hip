@@ -361,6 +361,22 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
+// Direct-to-LDS loads (16 or 4 bytes per lane; lane l writes at dst + l *
+// size, dst wave-uniform), written as inline assembly: issued through the
+// builtin, the compiler waits for every one of them in flight before the
+// next LDS read of any buffer, which would drain the prefetch of the next
+// tile before the current one is used.  The kernels wait for them
+// explicitly (wait_vm) instead.  They write no register, so nothing the
+// compiler tracks is left in flight.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
 // Rows 0..63 of a tile (src = row 0; rows >= nvalid read row nvalid - 1,
 // which may lie before the tile when nvalid <= 0 but is always a real row)
 // into dst[0 .. 16 KB); wave `wave` of `nw` issues runs wave, wave + nw, ...
@@ -370,7 +386,7 @@ __device__ __forceinline__ void dma_rows64(const uint16_t* src, int nvalid, uint
   for (int k = wave; k < 16; k += nw) {
     const int r = min(4 * k + (lane >> 4), nvalid - 1);
     const int c = cl ^ (k & 3);
-    __builtin_amdgcn_global_load_lds(src + ptrdiff_t(r) * D + c * 8, (lds_ptr)(dst + k * 1024), 16, 0, 0);
+    dma16(src + ptrdiff_t(r) * D + c * 8, dst + k * 1024);
   }
 }
 
@@ -385,7 +401,7 @@ __device__ __forceinline__ void dma_rows64_full(const uint16_t* src, uint8_t* ds
                                                 uint32_t lane_off) {
   const uint8_t* s8 = reinterpret_cast<const uint8_t*>(src) + lane_off;
   for (int k = wave, j = 0; k < 16; k += nw, ++j)
-    __builtin_amdgcn_global_load_lds(s8 + j * nw * 4 * ROWB, (lds_ptr)(dst + k * 1024), 16, 0, 0);
+    dma16(s8 + j * nw * 4 * ROWB, dst + k * 1024);
 }
 
 // MFMA operand (8 bf16 of one row) at per-lane base `base` (row * 256 with
@@ -639,8 +655,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int 
   auto stage_rt = [&](const Tile& tl, float* dst) __attribute__((always_inline)) {
     if (wave == 0) {
       const size_t rr = tl.row0 + min(tl.t0 + lane, a.S - 1);
-      __builtin_amdgcn_global_load_lds(a.lse2 + rr, (lds_ptr)dst, 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(a.dt + rr, (lds_ptr)(dst + 64), 4, 0, 0);
+      dma4(a.lse2 + rr, dst);
+      dma4(a.dt + rr, dst + 64);
     }
   };
 
