@@ -13,27 +13,37 @@
 //
 // One wave per (sequence, KV group, token), no barriers.  Different tokens'
 // lists overlap little, so each wave streams its own blocks in 32-key
-// halves, the next half in flight while the current one is used: K rows go
-// straight to registers (buffer loads, zero past the sequence), V rows to
-// the wave's own LDS slot (direct-to-LDS loads, two slots) from where the
-// transposed reads (ds_read_b64_tr_b16) form V^T.  V row r of a half is 256
-// bytes; chunk c sits at byte r * 256 + ((c ^ swz(r)) << 4) with
-// swz(r) = (r mod 16) ^ 4 (r / 16 mod 2), so the 16 rows that one transposed
-// read touches land on 16 different 16-byte bank groups.
+// halves, the next half in flight while the current one is used: K and V
+// rows go to the wave's own LDS slot (direct-to-LDS loads, two slots), K
+// read back as the A operand, V through transposed reads (ds_read_b64_tr_b16)
+// as V^T.  A row r of a half is 256 bytes; chunk c sits at byte
+// r * 256 + ((c ^ swz(r)) << 4) with swz(r) = (r mod 16) ^ 4 (r / 16 mod 2),
+// so the 16 rows that one transposed read touches, and the 16 rows whose
+// same chunk 16 lanes read for the A operand, land on 16 different 16-byte
+// bank groups.  The loads are issued from inline assembly: through the
+// builtin, the compiler would wait for all of them before any LDS read
+// (it cannot tell the slots apart), draining the next half's loads; the
+// loop waits for them itself (wait_vm).
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
 #define DSA_LDS_BF16X4(p) ((__attribute__((address_space(3))) bf16x4*)(p))
+
+// direct-to-LDS load of 16 bytes per lane: lane l writes dst + 16 l (dst
+// wave-uniform); writes no register
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
 
 constexpr int kD = 128;
 constexpr int kRowB = 256;     // bytes per K / V row
 constexpr int kTW = 4;         // tokens (waves) per workgroup
 constexpr int kMaxList = 64;   // blocks per token list
-constexpr int kHalfB = 32 * kRowB;   // V bytes of one 32-key half block
+constexpr int kHalfB = 32 * kRowB;   // K (or V) bytes of one 32-key half block
 constexpr float kLazy = 8.f;         // log2 headroom before the running maximum moves
 
 __device__ __forceinline__ int vswz(int r) { return (r & 15) ^ (((r >> 4) & 1) << 2); }
@@ -48,8 +58,9 @@ __device__ __forceinline__ void wait_vm() {
 
 __global__ __launch_bounds__(kTW * 64) void k_attn_tok(AttnArgs a, int ntile, int per_xcd) {
   constexpr int BLK = 64;
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[kTW][kHalfB];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[kTW][kHalfB];
+  // per wave, two slots of one half each: K rows, then V rows
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[kTW][2 * kHalfB];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[kTW][2 * kHalfB];
 
   const int id = xcd_work_id(per_xcd);
   if (id >= a.B * a.Hkv * ntile) return;
@@ -81,29 +92,37 @@ __global__ __launch_bounds__(kTW * 64) void k_attn_tok(AttnArgs a, int ntile, in
     }
   }
 
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const uint16_t*>(a.k) + size_t(bg) * a.S * kD,
-                                               uint32_t(a.S) * kRowB);
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + size_t(bg) * a.S * kD;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + size_t(bg) * a.S * kD;
-  // K A-operand rows of this lane in a half: sub-tile h -> key 8 (i16/4) + 4 h + i16 % 4
-  const uint32_t koff0 = uint32_t(((i16 >> 2) * 8 + (i16 & 3)) * kRowB + q4 * 16);
-  // V direct-to-LDS: run k (4 rows) -> rows 4k + lane/16, position lane % 16
+  // K A-operand rows of this lane in a half: sub-tile h -> key 8 (i16/4) + 4 h + i16 % 4;
+  // k-step ks reads chunk q4 + 4 ks of that row
+  uint32_t koff[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (i16 >> 2) * 8 + 4 * h + (i16 & 3);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[h][ks] = uint32_t(r * kRowB + (((q4 + 4 * ks) ^ vswz(r)) << 4));
+  }
+  // direct-to-LDS: run k (4 rows) -> rows 4k + lane/16, position lane % 16
   const int vr = lane >> 4;
 
   // half n of the list: block entry n / 2, keys 32 (n % 2) ..
   auto key0_of = [&](int n) { return __builtin_amdgcn_readlane(myent, n >> 1) * BLK + (n & 1) * 32; };
-  auto issue = [&](int key0, bf16x8 (&kr)[2][4], uint8_t* vdst) __attribute__((always_inline)) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        kr[h][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-            krs, koff0 + uint32_t(key0 * kRowB + h * 4 * kRowB + ks * 64), 0, 0));
+  // 16 loads per half: K runs into dst, V runs into dst + kHalfB
+  auto issue = [&](int key0, uint8_t* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int r = k * 4 + vr;
       const int row = max(0, min(key0 + r, a.S - 1));   // outside: masked keys, finite values
       const int c = (lane & 15) ^ vswz(r);
-      __builtin_amdgcn_global_load_lds(vbase + size_t(row) * kD + c * 8, (lds_ptr)(vdst + k * 1024), 16, 0, 0);
+      dma16(kbase + size_t(row) * kD + c * 8, dst + k * 1024);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = k * 4 + vr;
+      const int row = max(0, min(key0 + r, a.S - 1));
+      const int c = (lane & 15) ^ vswz(r);
+      dma16(vbase + size_t(row) * kD + c * 8, dst + kHalfB + k * 1024);
     }
   };
 
@@ -118,7 +137,13 @@ __global__ __launch_bounds__(kTW * 64) void k_attn_tok(AttnArgs a, int ntile, in
   const uint32_t ro1 = uint32_t(r1 * kRowB + ((i16 & 1) << 3)), ro2 = uint32_t(r2 * kRowB + ((i16 & 1) << 3));
   const int s1 = vswz(r1), s2 = vswz(r2), cl = (i16 & 3) >> 1;
 
-  auto compute = [&](int key0, const bf16x8 (&kr)[2][4], const uint8_t* vsrc) __attribute__((always_inline)) {
+  auto compute = [&](int key0, const uint8_t* slot) __attribute__((always_inline)) {
+    const uint8_t* vsrc = slot + kHalfB;
+    bf16x8 kr[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kr[h][ks] = *reinterpret_cast<const bf16x8*>(slot + koff[h][ks]);
     floatx4 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -175,23 +200,21 @@ __global__ __launch_bounds__(kTW * 64) void k_attn_tok(AttnArgs a, int ntile, in
   };
 
   const int total = 2 * cnt;
-  bf16x8 ka[2][4], kb[2][4];
-  uint8_t* va = vs0[wave];
-  uint8_t* vb = vs1[wave];
+  uint8_t* sa = vs0[wave];
+  uint8_t* sb = vs1[wave];
   // the half after the last one re-reads the last half into the idle slot,
-  // so every phase issues the same 16 operations and waits the same way
-  auto phase = [&](int n, bf16x8 (&kc)[2][4], const uint8_t* vc, bf16x8 (&kn)[2][4], uint8_t* vn)
-      __attribute__((always_inline)) {
-    issue(key0_of(min(n + 1, total - 1)), kn, vn);
-    wait_vm<16>();   // half n's V runs landed (the 8 K loads and 8 runs just issued may not)
-    compute(key0_of(n), kc, vc);
+  // so every phase issues the same 16 loads and waits the same way
+  auto phase = [&](int n, const uint8_t* sc, uint8_t* sn) __attribute__((always_inline)) {
+    issue(key0_of(min(n + 1, total - 1)), sn);
+    wait_vm<16>();   // half n's runs landed (the 16 just issued may not have)
+    compute(key0_of(n), sc);
   };
   if (total > 0) {
-    issue(key0_of(0), ka, va);
+    issue(key0_of(0), sa);
     for (int n = 0; n < total; n += 2) {
-      phase(n, ka, va, kb, vb);
+      phase(n, sa, sb);
       if (n + 1 >= total) break;
-      phase(n + 1, kb, vb, ka, va);
+      phase(n + 1, sb, sa);
     }
     wait_vm<0>();   // the spare re-read has landed before the wave ends
   }
