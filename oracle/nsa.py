@@ -23,7 +23,11 @@ Readings taken where the page is silent:
     heads; its candidates are blocks j <= t // sel_block; all heads of the
     group attend to that token's blocks (keys <= t);
   * the sliding branch sees keys t-W+1 .. t;
-  * gates: out = sum over branches of sigmoid(z_b) * o_b (no normalisation).
+  * gates: out = sum over branches of sigmoid(z_b) * o_b (no normalisation);
+  * summaries are stored in the dtype of the keys and values they summarise:
+    with bf16 inputs, each float64 mean is rounded once to the nearest
+    bfloat16 (ties to even) and branch 1 and the block scores use those
+    stored values.
 """
 from __future__ import annotations
 
@@ -46,6 +50,36 @@ def compress(x: np.ndarray, length: int, stride: int) -> np.ndarray:
     for c in range(n):
         out[..., c, :] = x[..., c * stride:c * stride + length, :].mean(axis=-2)
     return out
+
+
+def round_to_bf16(x):
+    """Each float64 value rounded to the nearest bfloat16 (8 significant bits,
+    exponent range of float32), ties to the even neighbour; returned as
+    float64.  Written from the format's definition: with |x| = m 2^e,
+    0.5 <= m < 1, the representable neighbours are multiples of the quantum
+    2^(e-8) (2^-133 below the normal range); magnitudes that round to 2^128
+    or above overflow to infinity.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])
+    quantum = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(x[fin], -quantum)), quantum)   # rint: ties to even
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, r), r)
+    out[fin] = r
+    return out
+
+
+def stored_summaries(x, length, stride, dtype):
+    """Summaries as the compressed branch stores them: the float64 means of
+    `compress`, rounded once to `dtype` ("bf16"), or kept exact (None)."""
+    ck = compress(x, length, stride)
+    if dtype is None:
+        return ck
+    if dtype == "bf16":
+        return round_to_bf16(ck)
+    raise ValueError(f"unknown summary dtype {dtype!r}")
 
 
 def summary_end(c, length, stride):
@@ -220,13 +254,16 @@ def combine(o_cmp, o_sel, o_win, z):
             + gate[..., 2:3] * np.asarray(o_win, dtype=np.float64))
 
 
-def forward(q, k, v, z, length, stride, sel_block, sel_k, window, scale, per_token=False):
+def forward(q, k, v, z, length, stride, sel_block, sel_k, window, scale, per_token=False,
+            summary_dtype=None):
     """All three branches and the gated combine ([NSA] §03), in order.
-    per_token: rank blocks per query token instead of per query block."""
+    per_token: rank blocks per query token instead of per query block.
+    summary_dtype: "bf16" stores the summaries rounded to bfloat16 before
+    branch 1 uses them (as a bf16 pipeline does); None keeps them exact."""
     from .prefill import select_blocks, sparse_attention
     S = q.shape[2]
-    ck = compress(k, length, stride)
-    cv = compress(v, length, stride)
+    ck = stored_summaries(k, length, stride, summary_dtype)
+    cv = stored_summaries(v, length, stride, summary_dtype)
     o1, lse1, p1 = cmp_attention(q, ck, cv, length, stride, scale)
     if per_token:
         scores = cmp_token_scores(p1, k.shape[1], length, stride, sel_block, S)

@@ -240,3 +240,62 @@ def test_per_token_forward_dense_limit():
                     c.scale, per_token=True)
     assert res["scores"].shape == (1, 1, c.S, c.n_blocks)
     assert np.max(np.abs(res["o_sel"] - _sdpa_causal(q, k, v, c.scale))) < 1e-12
+
+
+def test_round_to_bf16_hand_cases():
+    """bfloat16 keeps 8 significant bits: between 1 and 2 the spacing is
+    2^-7, so 1 + 2^-8 is a tie (to the even neighbour 1), 1 + 3*2^-8 a tie
+    between 1 + 2^-7 (odd last bit) and 1 + 2^-6 (even), and anything above
+    a half quantum rounds up.  Below 2^-126 the spacing is 2^-133."""
+    r = N.round_to_bf16
+    cases = [
+        (1.0, 1.0), (3.0, 3.0), (-2.5, -2.5), (0.0, 0.0),
+        (1 + 2.0 ** -8, 1.0), (-(1 + 2.0 ** -8), -1.0),
+        (1 + 3 * 2.0 ** -8, 1 + 2.0 ** -6),
+        (1 + 2.0 ** -8 + 2.0 ** -30, 1 + 2.0 ** -7),
+        (1 + 2.0 ** -8 - 2.0 ** -30, 1.0),
+        (2.0 ** -133, 2.0 ** -133), (2.0 ** -134, 0.0), (3 * 2.0 ** -134, 2.0 ** -132),
+        ((2 - 2.0 ** -7) * 2.0 ** 127, (2 - 2.0 ** -7) * 2.0 ** 127),
+        ((2 - 2.0 ** -8) * 2.0 ** 127, np.inf),
+        (np.inf, np.inf), (-np.inf, -np.inf),
+    ]
+    got = r(np.array([c[0] for c in cases]))
+    want = np.array([c[1] for c in cases])
+    assert np.array_equal(got, want), list(zip(got, want))
+    assert np.isnan(r(np.array([np.nan]))[0])
+
+
+def test_round_to_bf16_matches_torch_float32_conversion():
+    """For values a float32 holds exactly, rounding to bfloat16 is what
+    torch's float32 -> bfloat16 conversion (round to nearest, ties to even)
+    does: random bit patterns over the whole exponent range, and exact ties
+    (a bfloat16 value plus half its spacing)."""
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    base = torch.from_numpy(rng.standard_normal(50_000).astype(np.float32)).to(torch.bfloat16)
+    b64 = base.to(torch.float64).numpy()
+    _, e = np.frexp(b64)
+    ties = (b64 + np.ldexp(np.sign(b64), e - 9)).astype(np.float32)   # half a quantum
+    for arr in (x, ties):
+        want = torch.from_numpy(arr).to(torch.bfloat16).to(torch.float64).numpy()
+        got = N.round_to_bf16(arr.astype(np.float64))
+        same = (got == want) | (np.isnan(got) & np.isnan(want))
+        assert same.all(), (arr[~same][:5], got[~same][:5], want[~same][:5])
+
+
+def test_stored_summaries_of_bf16_values():
+    """len = stride = 1: every summary is one bf16 key, which rounding leaves
+    unchanged; len 2 of two equal keys likewise.  The stored summaries are
+    the exact means rounded once."""
+    c, q, k, v, _ = _small(S=96)
+    assert np.array_equal(N.stored_summaries(k, 1, 1, "bf16"), k)
+    kk = np.repeat(k[:, :, ::2], 2, axis=2)
+    assert np.array_equal(N.stored_summaries(kk, 2, 2, "bf16"), k[:, :, ::2])
+    exact = N.compress(k, 32, 16)
+    stored = N.stored_summaries(k, 32, 16, "bf16")
+    assert np.array_equal(stored, N.round_to_bf16(exact))
+    # one rounding: within half a spacing, the unit roundoff 2^-8 relative
+    assert (np.abs(stored - exact) <= 2.0 ** -8 * np.abs(exact) + 1e-300).all()
+    assert not np.array_equal(stored, exact)
