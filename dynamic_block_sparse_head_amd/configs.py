@@ -120,6 +120,8 @@ class NSAConfig:
     window: int = 512
     dtype: str = "bf16"
     std: float = 1.0 / math.sqrt(128)
+    needles: int = 0          # planted needle blocks per KV head (parity runs only)
+    needle_alpha: float = 0.0
 
     @property
     def G(self) -> int:

@@ -51,28 +51,26 @@ def _host_rng(seed: int, tag: str, tensor: str) -> np.random.Generator:
     return np.random.default_rng(_seed(seed, tag, tensor))
 
 
-def plan_needles(cfg: PrefillConfig, seed: int):
-    """(b, g, target_query_block, needle_key_block) for every planted needle.
-
-    A needle block must be a top-k candidate of its target (it lies before
-    the target's local window) and the targets and needles of one KV head are
-    all distinct blocks.  A sequence too short to hold them gets fewer (or
-    none): every needle placed satisfies those rules.
-    """
-    if cfg.needles == 0:
+def _needle_plan(tag, B, Hkv, n_blocks, n_local, topk, needles, target_range, seed):
+    """(b, g, target_query_block, needle_key_block) for `needles` needles per
+    KV head: each needle block lies before its target's n_local most recent
+    blocks (so it is a top-k candidate of the target) and the targets and
+    needles of one KV head are all distinct blocks.  A sequence too short to
+    hold them gets fewer (or none)."""
+    if needles == 0:
         return []
-    rng = _host_rng(seed, cfg.name, "needles")
-    nB, nl = cfg.n_blocks, cfg.n_local
+    rng = _host_rng(seed, tag, "needles")
+    nB, nl = n_blocks, n_local
     out = []
-    for b in range(cfg.B):
-        for g in range(cfg.Hkv):
+    for b in range(B):
+        for g in range(Hkv):
             used = set()
-            for _ in range(cfg.needles):
+            for _ in range(needles):
                 for _attempt in range(1000):
-                    if cfg.needle_target_range:
-                        lo, hi = cfg.needle_target_range
+                    if target_range:
+                        lo, hi = target_range
                     else:
-                        lo, hi = min(nl + cfg.topk + 8, nB - 1), nB - 1
+                        lo, hi = min(nl + topk + 8, nB - 1), nB - 1
                     t = int(rng.integers(lo, hi + 1))
                     last_cand = t - nl
                     if last_cand < 0:
@@ -86,6 +84,32 @@ def plan_needles(cfg: PrefillConfig, seed: int):
                 else:
                     break   # no room left on this KV head
     return out
+
+
+def plan_needles(cfg: PrefillConfig, seed: int):
+    """Needles of a prefill workload: candidates of a target lie before its
+    local window."""
+    return _needle_plan(cfg.name, cfg.B, cfg.Hkv, cfg.n_blocks, cfg.n_local, cfg.topk, cfg.needles,
+                        cfg.needle_target_range, seed)
+
+
+def plan_nsa_needles(cfg: NSAConfig, seed: int):
+    """Needles of a three-branch workload: every block up to the target is a
+    candidate; a needle is kept off the target block itself."""
+    return _needle_plan(cfg.name, cfg.B, cfg.Hkv, cfg.n_blocks, 1, cfg.sel_k, cfg.needles, (), seed)
+
+
+def _plant(q, k, needles, G, blk, alpha):
+    """Shift every key of each needle block by alpha along the unit direction
+    of the summed query rows of its target block (all query heads of the KV
+    group), so the needle lines up with what the target block asks for.
+    q in its final dtype, k in float32 before rounding (modified in place)."""
+    D = q.shape[-1]
+    for (b, g, t, n) in needles:
+        rows = q[b, g * G:(g + 1) * G, t * blk:(t + 1) * blk, :].to(torch.float64)
+        direction = rows.reshape(-1, D).sum(dim=0)
+        direction = direction / torch.linalg.vector_norm(direction)
+        k[b, g, n * blk:(n + 1) * blk, :] += (alpha * direction).to(torch.float32)
 
 
 def prefill_inputs(cfg: PrefillConfig, seed: int = 0, device="cpu"):
@@ -120,12 +144,7 @@ def prefill_inputs(cfg: PrefillConfig, seed: int = 0, device="cpu"):
     dt = _dtype(cfg.dtype)
     q = q.to(dt)
     needles = plan_needles(cfg, seed)
-    G, blk = cfg.G, cfg.block
-    for (b, g, t, n) in needles:
-        rows = q[b, g * G:(g + 1) * G, t * blk:(t + 1) * blk, :].to(torch.float64)
-        direction = rows.reshape(-1, D).sum(dim=0)
-        direction = direction / torch.linalg.vector_norm(direction)
-        k[b, g, n * blk:(n + 1) * blk, :] += (cfg.needle_alpha * direction).to(torch.float32)
+    _plant(q, k, needles, cfg.G, cfg.block, cfg.needle_alpha)
     return {"q": q.contiguous(), "k": k.to(dt).contiguous(), "v": v.to(dt).contiguous(),
             "needles": needles}
 
@@ -162,17 +181,24 @@ def decode_inputs(cfg: DecodeConfig, seed: int = 0, device="cpu"):
     return out
 
 
-def nsa_inputs(cfg: NSAConfig, seed: int = 0, device="cpu"):
+def nsa_inputs(cfg: NSAConfig, seed: int = 0, device="cpu", needle_alpha=None):
     """Q [B,Hq,S,D], K/V [B,Hkv,S,D] ~ N(0, std^2) in cfg.dtype; gate logits
-    z [B,S,Hq,3] ~ N(0,1) float32."""
+    z [B,S,Hq,3] ~ N(0,1) float32.  With cfg.needles > 0, needle blocks are
+    planted in K as for the prefill workloads (sel_block-token blocks,
+    strength needle_alpha, default cfg.needle_alpha); the draws do not depend
+    on the strength, so one seed gives the same tensors at every alpha."""
     dev = torch.device(device)
     dt = _dtype(cfg.dtype)
     q = _normal((cfg.B, cfg.Hq, cfg.S, cfg.D), cfg.std, _gen(dev, seed, cfg.name, "q"), dev)
     k = _normal((cfg.B, cfg.Hkv, cfg.S, cfg.D), cfg.std, _gen(dev, seed, cfg.name, "k"), dev)
     v = _normal((cfg.B, cfg.Hkv, cfg.S, cfg.D), cfg.std, _gen(dev, seed, cfg.name, "v"), dev)
     z = _normal((cfg.B, cfg.S, cfg.Hq, 3), 1.0, _gen(dev, seed, cfg.name, "gates"), dev)
-    return {"q": q.to(dt).contiguous(), "k": k.to(dt).contiguous(),
-            "v": v.to(dt).contiguous(), "z": z.contiguous()}
+    q = q.to(dt)
+    needles = plan_nsa_needles(cfg, seed)
+    alpha = cfg.needle_alpha if needle_alpha is None else needle_alpha
+    _plant(q, k, needles, cfg.G, cfg.sel_block, alpha)
+    return {"q": q.contiguous(), "k": k.to(dt).contiguous(),
+            "v": v.to(dt).contiguous(), "z": z.contiguous(), "needles": needles}
 
 
 def random_scores(rows: int, n: int, seed: int = 0, ties: bool = False, device="cpu"):
