@@ -35,6 +35,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// double -> bf16 bits, rounded once to nearest even.  The double is first
+// rounded to float toward zero with the last bit forced to 1 when inexact
+// ("round to odd": the discarded bits survive as a sticky bit), then the
+// float is rounded to bf16 to nearest even; with 16 spare bits between the
+// two formats the result equals direct rounding of the double.
+__device__ __forceinline__ uint16_t f64_to_bf16(double x) {
+  const float f = static_cast<float>(x);
+  uint32_t u = __float_as_uint(f);
+  const double back = static_cast<double>(f);
+  if (back != x && (u & 0x7f800000u) != 0x7f800000u) {
+    if (__builtin_fabs(back) > __builtin_fabs(x)) u -= 1u;   // one step toward zero
+    u |= 1u;
+  }
+  return f32_to_bf16(__uint_as_float(u));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Raw buffer descriptor over `bytes` bytes from `base`: buffer loads at byte

@@ -3,7 +3,7 @@
 // blocks, a sliding branch, fused per token by gates).
 //
 //  * k_compress: summaries = plain means of `len` keys (values) every
-//    `stride` tokens.
+//    `stride` tokens, rounded once to bf16.
 //  * k_cmp_block_scores: second pass of the compressed branch.  With the
 //    branch's log-sum-exp known, it recomputes each row's probabilities over
 //    the summaries (bf16 MFMA), sums them over the rows and heads of a query
@@ -20,7 +20,8 @@
 namespace dsa {
 namespace {
 
-// grid (ceil(n_cmp*D/8 / 256), B*Hkv, 2)
+// grid (ceil(n_cmp*D/8 / 256), B*Hkv, 2).  Sums in float64 (exact for
+// bf16 inputs of any realistic spread), one division, one rounding to bf16.
 __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k,
                                                   const uint16_t* __restrict__ v, int S, int D,
                                                   int len, int stride, int n_cmp,
@@ -32,19 +33,20 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
   const int cidx = e / cpr, dc = e % cpr;
   const int bg = blockIdx.y;
   const uint16_t* src = (blockIdx.z == 0 ? k : v) + (size_t(bg) * S + size_t(cidx) * stride) * D + dc * 8;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  double acc[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
   for (int r = 0; r < len; ++r) {
     const u32x4 w = *reinterpret_cast<const u32x4*>(src + size_t(r) * D);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      acc[2 * x] += bf16lo(w[x]);
-      acc[2 * x + 1] += bf16hi(w[x]);
+      acc[2 * x] += double(bf16lo(w[x]));
+      acc[2 * x + 1] += double(bf16hi(w[x]));
     }
   }
-  const float inv = 1.f / float(len);
+  const double n = double(len);
   u32x4 o;
 #pragma unroll
-  for (int x = 0; x < 4; ++x) o[x] = pack_bf16x2(acc[2 * x] * inv, acc[2 * x + 1] * inv);
+  for (int x = 0; x < 4; ++x)
+    o[x] = uint32_t(f64_to_bf16(acc[2 * x] / n)) | (uint32_t(f64_to_bf16(acc[2 * x + 1] / n)) << 16);
   uint16_t* dst = (blockIdx.z == 0 ? ck : cv) + (size_t(bg) * n_cmp + cidx) * D + dc * 8;
   *reinterpret_cast<u32x4*>(dst) = o;
 }

@@ -124,3 +124,18 @@ def check_lse(gpu, ref, tol, what=""):
     fin = np.isfinite(ref)
     assert (np.isneginf(gpu) == np.isneginf(ref)).all(), f"{what}: -inf pattern differs"
     assert np.abs(gpu[fin] - ref[fin]).max() <= tol, f"{what}: lse err {np.abs(gpu[fin]-ref[fin]).max()}"
+
+
+def nsa_check_summaries(c, x, gck, gcv, groups=None):
+    """The GPU's stored summaries against the oracle's (float64 mean rounded
+    once to bf16): bit for bit.  Returns the oracle's (ck, cv) of the groups
+    (all groups by default) as float64 arrays."""
+    from oracle import nsa as On
+    sl = slice(None) if groups is None else groups
+    k, v = to_np(x["k"][:, sl]), to_np(x["v"][:, sl])
+    ck = On.stored_summaries(k, c.cmp_len, c.cmp_stride, "bf16")
+    cv = On.stored_summaries(v, c.cmp_len, c.cmp_stride, "bf16")
+    gk, gv = to_np(gck[:, sl]), to_np(gcv[:, sl])
+    assert np.array_equal(gk, ck), f"ck differs in {int((gk != ck).sum())} elements"
+    assert np.array_equal(gv, cv), f"cv differs in {int((gv != cv).sum())} elements"
+    return ck, cv

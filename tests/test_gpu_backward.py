@@ -62,6 +62,28 @@ def test_backward_16k_shape(S):
     _parity(configs.PREFILL_16K.with_seq(S))
 
 
+def test_backward_16k_full_size_two_groups():
+    """The 16K workload at full length, in the configuration the benchmark
+    times (same plan, seed and upstream gradient): dq of every query head of
+    KV groups 0 and 5, and dk, dv of those groups, against the float64
+    oracle over the whole sequence; keys no row of a group sees get zero."""
+    c = configs.PREFILL_16K
+    x, dout, plan, got = _forward_backward(c, seed=0)
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    unseen = _unseen_keys(gi, gc, c.block, c.S)
+    for g in (0, 5):
+        heads = slice(g * c.G, (g + 1) * c.G)
+        ref = Ob.sparse_attention_backward(
+            to_np(x["q"][:, heads]), to_np(x["k"][:, g:g + 1]), to_np(x["v"][:, g:g + 1]),
+            gi[:, g:g + 1], gc[:, g:g + 1], c.block, c.scale, to_np(dout[:, heads]))
+        mine = (got[0][:, heads], got[1][:, g:g + 1], got[2][:, g:g + 1])
+        for name, gg, r in zip(("dq", "dk", "dv"), mine, ref):
+            m, n = check_grad(gg, r, f"16K g{g} {name}")
+            print(f"16K g{g} {name}: max err / max|ref| {m:.2e}, norm err {n:.2e}")
+        for name, gg in (("dk", mine[1]), ("dv", mine[2])):
+            assert (gg[unseen[:, g:g + 1]] == 0).all(), f"{name}: nonzero gradient on unseen keys"
+
+
 @pytest.mark.parametrize("S", [37, 65])
 def test_backward_short_sequences(S):
     _parity(replace(configs.PREFILL_16K.with_seq(S), needles=0), seed=S)

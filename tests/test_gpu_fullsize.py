@@ -4,6 +4,8 @@ every selected index row it can afford and sampled outputs: query blocks
 spread over the sequence (first, middle, last), sampled (sequence, KV head)
 pairs for decode, and sampled query blocks of one KV group for the
 three-branch path."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,7 @@ from oracle import decode as Od
 from oracle import nsa as On
 from oracle import prefill as Op
 
-from _parity import check_bf16, check_indices, check_lse, to_np
+from _parity import check_bf16, check_indices, check_lse, nsa_check_summaries, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -86,6 +88,43 @@ def test_decode_128k_full_size():
         check_bf16(to_np(plan.out[b:b + 1, heads]), out, f"decode b{b} g{g}")
 
 
+def _nsa_sampled(c, x, plan, g, blocks, fused=None):
+    """Group g of the three-branch step checked on the query blocks `blocks`
+    against the oracle run from the raw inputs: the group's summaries bit
+    for bit (oracle: float64 means rounded once to bf16), branch 1 on the
+    oracle's summaries, block scores and selection of those blocks, the
+    selected branch at the GPU's accepted lists, the sliding branch and the
+    gated output.  Returns the oracle's block scores [1,1,nb,nb] (rows of
+    other blocks NaN)."""
+    heads = slice(g * c.G, (g + 1) * c.G)
+    q = to_np(x["q"][:, heads])
+    k = to_np(x["k"][:, g:g + 1])
+    v = to_np(x["v"][:, g:g + 1])
+    z = to_np(x["z"][:, :, heads])
+    ck, cv = nsa_check_summaries(c, x, plan.ck, plan.cv, groups=slice(g, g + 1))
+    rows = [t for i in blocks for t in range(i * c.sel_block, min((i + 1) * c.sel_block, c.S))]
+    o1, lse1, p1 = On.cmp_attention(q, ck, cv, c.cmp_len, c.cmp_stride, c.scale, rows=rows)
+    check_bf16(to_np(plan.o_cmp[:, heads][:, :, rows]), o1[:, :, rows], "o_cmp")
+    check_lse(to_np(plan.lse_cmp[:, heads][:, :, rows]), lse1[:, :, rows], 2e-3, "lse_cmp")
+    sc = On.cmp_block_scores(p1, 1, c.cmp_len, c.cmp_stride, c.sel_block, c.S, q_blocks=blocks)
+    gsc = to_np(plan.scores[:, g:g + 1])
+    gi, gc = plan.idx[:, g:g + 1].cpu().numpy(), plan.count[:, g:g + 1].cpu().numpy()
+    for i in blocks:
+        assert np.abs(gsc[0, 0, i, :i + 1] - sc[0, 0, i, :i + 1]).max() < 1e-6
+        check_indices(sc[:, :, i:i + 1, :], gi[:, :, i:i + 1], gc[:, :, i:i + 1], c.sel_k, 0, True,
+                      rows=[i])
+    o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale, q_blocks=blocks)
+    check_bf16(to_np(plan.o_sel[:, heads][:, :, rows]), o2[:, :, rows], "o_sel")
+    o3, _ = On.window_attention(q, k, v, c.window, c.scale, rows=rows)
+    ref = On.combine(o1[:, :, rows], o2[:, :, rows], o3[:, :, rows], z[:, rows])
+    if not plan.fuse_combine:
+        check_bf16(to_np(plan.o_win[:, heads][:, :, rows]), o3[:, :, rows], "o_win")
+    check_bf16(to_np(plan.out[:, heads][:, :, rows]), ref, "nsa out")
+    if fused is not None:
+        check_bf16(to_np(fused[:, heads][:, :, rows]), ref, "nsa out, fused window + combine")
+    return sc
+
+
 def test_nsa_32k_full_size():
     c = configs.NSA_32K
     x = inputs.nsa_inputs(c, seed=0, device=DEV)
@@ -96,31 +135,57 @@ def test_nsa_32k_full_size():
     L.dsa_nsa_window_combine(x["q"], x["k"], x["v"], c.window, c.scale, plan.o_cmp, plan.o_sel,
                              x["z"], fused)
     torch.cuda.synchronize()
-    g = 1
-    heads = slice(g * c.G, (g + 1) * c.G)
-    q = to_np(x["q"][:, heads])
-    k = to_np(x["k"][:, g:g + 1])
-    v = to_np(x["v"][:, g:g + 1])
-    z = to_np(x["z"][:, :, heads])
-    ck, cv = On.compress(k, c.cmp_len, c.cmp_stride), On.compress(v, c.cmp_len, c.cmp_stride)
-    check_bf16(to_np(plan.ck[:, g:g + 1]), ck, "ck")
-    gck, gcv = to_np(plan.ck[:, g:g + 1]), to_np(plan.cv[:, g:g + 1])
-    blocks = [0, 1, 16, 300, 511]
-    rows = [t for i in blocks for t in range(i * c.sel_block, (i + 1) * c.sel_block)]
-    o1, lse1, p1 = On.cmp_attention(q, gck, gcv, c.cmp_len, c.cmp_stride, c.scale, rows=rows)
-    check_bf16(to_np(plan.o_cmp[:, heads][:, :, rows]), o1[:, :, rows], "o_cmp")
-    check_lse(to_np(plan.lse_cmp[:, heads][:, :, rows]), lse1[:, :, rows], 2e-3, "lse_cmp")
-    sc = On.cmp_block_scores(p1, 1, c.cmp_len, c.cmp_stride, c.sel_block, c.S, q_blocks=blocks)
-    gsc = to_np(plan.scores[:, g:g + 1])
-    gi, gc = plan.idx[:, g:g + 1].cpu().numpy(), plan.count[:, g:g + 1].cpu().numpy()
-    for i in blocks:
-        assert np.abs(gsc[0, 0, i] - sc[0, 0, i]).max() < 1e-6
-        check_indices(sc[:, :, i:i + 1, :], gi[:, :, i:i + 1], gc[:, :, i:i + 1], c.sel_k, 0, True,
-                      rows=[i])
-    o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale, q_blocks=blocks)
-    check_bf16(to_np(plan.o_sel[:, heads][:, :, rows]), o2[:, :, rows], "o_sel")
-    o3, _ = On.window_attention(q, k, v, c.window, c.scale, rows=rows)
-    check_bf16(to_np(plan.o_win[:, heads][:, :, rows]), o3[:, :, rows], "o_win")
-    ref = On.combine(o1[:, :, rows], o2[:, :, rows], o3[:, :, rows], z[:, rows])
-    check_bf16(to_np(plan.out[:, heads][:, :, rows]), ref, "nsa out")
-    check_bf16(to_np(fused[:, heads][:, :, rows]), ref, "nsa out, fused window + combine")
+    _nsa_sampled(c, x, plan, 1, [0, 1, 16, 300, 511], fused)
+
+
+def _needle_gaps(c, x):
+    """Oracle score margin of every planted needle at its target query block:
+    its score minus the best score outside the top-k (negative when the
+    needle is not in the oracle's top-k), from the raw inputs."""
+    gaps = []
+    for g in range(c.Hkv):
+        mine = [nd for nd in x["needles"] if nd[1] == g]
+        if not mine:
+            continue
+        targets = sorted({t for (_, _, t, _) in mine})
+        q = to_np(x["q"][:, g * c.G:(g + 1) * c.G])
+        ck = On.stored_summaries(to_np(x["k"][:, g:g + 1]), c.cmp_len, c.cmp_stride, "bf16")
+        rows = [t for i in targets for t in range(i * c.sel_block, (i + 1) * c.sel_block)]
+        _, _, p = On.cmp_attention(q, ck, ck, c.cmp_len, c.cmp_stride, c.scale, rows=rows)
+        sc = On.cmp_block_scores(p, 1, c.cmp_len, c.cmp_stride, c.sel_block, c.S, q_blocks=targets)
+        for (_, _, t, n) in mine:
+            s = sc[0, 0, t, :t + 1]
+            order = sorted(range(t + 1), key=lambda j: (-s[j], j))
+            gaps.append(float(s[n] - s[order[c.sel_k]]) if n in order[:c.sel_k] else -1.0)
+    return gaps
+
+
+def test_nsa_32k_planted_needles():
+    """The 32K three-branch workload with 4 needle blocks per KV group: the
+    needle strength starts at a quarter of the keys' norm scale and doubles
+    until the oracle ranks every needle in its target's top-16 with a score
+    margin of at least 1e-3; the GPU must then select every needle, and its
+    selection and outputs at the targets (and a few other blocks) must pass
+    the usual acceptance against the oracle."""
+    c = replace(configs.NSA_32K, needles=4)
+    alpha = 0.25
+    while True:
+        x = inputs.nsa_inputs(c, seed=0, device=DEV, needle_alpha=alpha)
+        gaps = _needle_gaps(c, x)
+        if min(gaps) >= 1e-3:
+            break
+        assert alpha < 1e6, "needles never reach a 1e-3 margin"
+        alpha *= 2
+        del x
+    print(f"needle strength {alpha}: oracle margins {min(gaps):.2e} .. {max(gaps):.2e}")
+    assert len(x["needles"]) == 4 * c.Hkv
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    torch.cuda.synchronize()
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    for (b, g, t, n) in x["needles"]:
+        assert n in gi[b, g, t, :gc[b, g, t]], f"needle {n} not selected for block {t} of group {g}"
+    for g in range(c.Hkv):
+        targets = sorted({t for (_, gg, t, _) in x["needles"] if gg == g})
+        _nsa_sampled(c, x, plan, g, targets + [0, 300])

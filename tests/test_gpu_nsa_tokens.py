@@ -14,7 +14,7 @@ from dynamic_block_sparse_head_amd.pipeline import NSAPlan
 from oracle import nsa as On
 from oracle import prefill as Op
 
-from _parity import check_bf16, check_indices, check_lse, to_np
+from _parity import check_bf16, check_indices, check_lse, nsa_check_summaries, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -38,15 +38,17 @@ def _branch1(c, x):
 
 @pytest.mark.parametrize("S,Hq,Hkv", [(1000, 16, 2), (777, 32, 2), (600, 4, 4), (300, 24, 2)])
 def test_token_scores(S, Hq, Hkv):
-    """Per-token scores against the oracle's probabilities on the GPU's own
-    summaries; ragged S, G = 8, 16, 1 and 12 (heads padded in the tile)."""
+    """Per-token scores against the oracle's probabilities on its own
+    summaries (the GPU's equal them bit for bit); ragged S, G = 8, 16, 1 and
+    12 (heads padded in the tile)."""
     c = replace(configs.NSA_32K, S=S, Hq=Hq, Hkv=Hkv)
     x = inputs.nsa_inputs(c, seed=S, device=DEV)
     ck, cv, lse = _branch1(c, x)
     sc = torch.full((c.B, c.Hkv, c.S, c.n_blocks), float("nan"), device=DEV)
     L.dsa_nsa_cmp_token_scores(x["q"], ck, lse, c.cmp_len, c.cmp_stride, c.sel_block, c.scale, sc)
     _sync()
-    _, _, p = On.cmp_attention(to_np(x["q"]), to_np(ck), to_np(cv), c.cmp_len, c.cmp_stride, c.scale)
+    rck, rcv = nsa_check_summaries(c, x, ck, cv)
+    _, _, p = On.cmp_attention(to_np(x["q"]), rck, rcv, c.cmp_len, c.cmp_stride, c.scale)
     ref = On.cmp_token_scores(p, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
     g = to_np(sc)
     assert np.isfinite(g).all()
@@ -70,7 +72,10 @@ def test_token_scores_other_geometry():
     sc = torch.empty(c.B, c.Hkv, c.S, nb, device=DEV)
     L.dsa_nsa_cmp_token_scores(x["q"], ck, lse, ln, st, sb, c.scale, sc)
     _sync()
-    _, _, p = On.cmp_attention(to_np(x["q"]), to_np(ck), to_np(cv), ln, st, c.scale)
+    rck = On.stored_summaries(to_np(x["k"]), ln, st, "bf16")
+    rcv = On.stored_summaries(to_np(x["v"]), ln, st, "bf16")
+    assert np.array_equal(to_np(ck), rck) and np.array_equal(to_np(cv), rcv)
+    _, _, p = On.cmp_attention(to_np(x["q"]), rck, rcv, ln, st, c.scale)
     ref = On.cmp_token_scores(p, c.Hkv, ln, st, sb, c.S)
     assert np.abs(to_np(sc) - ref).max() < SCORE_TOL
 
@@ -145,8 +150,10 @@ def test_token_attention_empty_and_single_lists():
 
 
 def test_nsa_pipeline_per_token_small():
-    """The whole per-token chain against the oracle's chain (selection
-    checked as an acceptable top-k under the oracle's scores)."""
+    """The whole per-token chain against the oracle's own chain from the raw
+    inputs (summaries bit for bit; selection checked as an acceptable top-k
+    under the oracle's scores; the selected branch at the GPU's accepted
+    lists, the oracle's own output wherever the lists agree)."""
     c = replace(configs.NSA_32K, S=2048 + 64, Hq=16, Hkv=1)
     x = inputs.nsa_inputs(c, seed=0, device=DEV)
     plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
@@ -154,17 +161,20 @@ def test_nsa_pipeline_per_token_small():
     plan.run(x["q"], x["k"], x["v"], x["z"])
     _sync()
     q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
-    gck, gcv = to_np(plan.ck), to_np(plan.cv)
-    o1, lse1, p1 = On.cmp_attention(q, gck, gcv, c.cmp_len, c.cmp_stride, c.scale)
-    sc = On.cmp_token_scores(p1, c.Hkv, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
-    assert np.abs(to_np(plan.scores) - sc).max() < SCORE_TOL
+    ref = On.forward(q, k, v, z, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window, c.scale,
+                     per_token=True, summary_dtype="bf16")
+    nsa_check_summaries(c, x, plan.ck, plan.cv)
+    check_bf16(to_np(plan.o_cmp), ref["o_cmp"], "o_cmp")
+    assert np.abs(to_np(plan.scores) - ref["scores"]).max() < SCORE_TOL
     gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
-    check_indices(sc, gi, gc, c.sel_k, 0, True, rows=[t // c.sel_block for t in range(c.S)])
-    o2, _ = On.token_sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale)
+    check_indices(ref["scores"], gi, gc, c.sel_k, 0, True, rows=[t // c.sel_block for t in range(c.S)])
+    if np.array_equal(gi, ref["idx"]) and np.array_equal(gc, ref["count"]):
+        o2, full = ref["o_sel"], ref["out"]
+    else:
+        o2, _ = On.token_sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale)
+        full = On.combine(ref["o_cmp"], o2, ref["o_win"], z)
     check_bf16(to_np(plan.o_sel), o2, "o_sel per token")
-    o3, _ = On.window_attention(q, k, v, c.window, c.scale)
-    full = On.combine(o1, o2, o3, z)
-    check_bf16(to_np(plan.out), full, "nsa per token end to end")
+    check_bf16(to_np(plan.out), full, "nsa per token, end to end")
 
 
 def test_nsa_per_token_32k_full_size():
@@ -181,9 +191,9 @@ def test_nsa_per_token_32k_full_size():
     q = to_np(x["q"][:, heads])
     k = to_np(x["k"][:, g:g + 1])
     v = to_np(x["v"][:, g:g + 1])
-    gck, gcv = to_np(plan.ck[:, g:g + 1]), to_np(plan.cv[:, g:g + 1])
+    rck, rcv = nsa_check_summaries(c, x, plan.ck, plan.cv, groups=slice(g, g + 1))
     rows = [0, 30, 31, 63, 64, 1000, 4095, 4096, 20000, 32700, 32767]
-    _, _, p1 = On.cmp_attention(q, gck, gcv, c.cmp_len, c.cmp_stride, c.scale, rows=rows)
+    _, _, p1 = On.cmp_attention(q, rck, rcv, c.cmp_len, c.cmp_stride, c.scale, rows=rows)
     sc = On.cmp_token_scores(p1, 1, c.cmp_len, c.cmp_stride, c.sel_block, c.S)
     gsc = to_np(plan.scores[:, g:g + 1])
     gi, gc = plan.idx[:, g:g + 1].cpu().numpy(), plan.count[:, g:g + 1].cpu().numpy()
