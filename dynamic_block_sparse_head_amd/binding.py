@@ -4,6 +4,11 @@ Argument marshalling only.  Tensors are torch tensors on the GPU (torch is
 used for device memory and the current HIP stream); every computation runs
 in the library's HIP kernels.  There is no fallback: without the built
 library, or without a GPU, these functions raise.
+
+The C calls take bare pointers to dense row-major buffers, so every tensor's
+full shape is checked here against the sizes derived from the call's
+primary input before anything is passed down; a mis-sized tensor raises
+ValueError and nothing is launched.
 """
 from __future__ import annotations
 
@@ -13,8 +18,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# DSA_LIBRARY may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("DSA_LIBRARY", os.path.join(_HERE, "libdsa.so"))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OK, DSA_E_ARG, DSA_E_UNSUPPORTED, DSA_E_WORKSPACE, DSA_E_HIP = 0, -1, -2, -3, -4
 DSA_F32, DSA_BF16 = 0, 1
@@ -116,6 +120,39 @@ def _ptr(t, name, dtype=None):
     return t.data_ptr()
 
 
+def _expect(t, shape, name):
+    """t must have exactly this shape (None: t is absent and may be None)."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+
+
+def _expect_rows(t, lead, last, name):
+    """t holds prod(lead) rows of `last` elements: any shape whose trailing
+    dimension is `last` (when given) and whose size is prod(lead) * last."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    n = 1
+    for x in lead:
+        n *= int(x)
+    want = n * (1 if last is None else int(last))
+    if t.numel() != want or (last is not None and (t.dim() == 0 or t.shape[-1] != last)):
+        tail = "" if last is None else f" with last dimension {last}"
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want} elements{tail}")
+
+
+def _ndim(t, n, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions (got shape {tuple(t.shape)})")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -136,11 +173,22 @@ def dsa_block_scores(kind, q, k_or_kmin, kmax, block, workspace, scores, stream=
     POOLED_HEAD: the same inputs -> scores [B,Hq,nb,nb] (one per query head).
     PAGE_BOUND: q [B,Hq,D], kmin/kmax [B,Hkv,nP,D] -> scores [B,Hkv,nP]."""
     if kind in (DSA_SCORE_POOLED, DSA_SCORE_POOLED_HEAD):
+        _ndim(q, 4, "q")
+        _ndim(k_or_kmin, 4, "k")
         B, Hq, n, D = q.shape
         Hkv = k_or_kmin.shape[1]
+        _expect(k_or_kmin, (B, Hkv, n, D), "k")
+        nb = -(-n // block) if block > 0 else 0
+        units = Hkv if kind == DSA_SCORE_POOLED else Hq
+        _expect_rows(scores, (B, units, nb), nb, "scores")
     else:
+        _ndim(q, 3, "q")
+        _ndim(k_or_kmin, 4, "kmin")
         B, Hq, D = q.shape
         Hkv, n = k_or_kmin.shape[1], k_or_kmin.shape[2]
+        _expect(k_or_kmin, (B, Hkv, n, D), "kmin")
+        _expect(kmax, (B, Hkv, n, D), "kmax")
+        _expect_rows(scores, (B, Hkv), n, "scores")
     ws_ptr = _ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().dsa_block_scores(kind, _dtype_code(q), _ptr(q, "q"), _ptr(k_or_kmin, "k"),
@@ -151,18 +199,49 @@ def dsa_block_scores(kind, q, k_or_kmin, kmax, block, workspace, scores, stream=
 
 def dsa_topk_select(scores, k, n_local, causal, idx, count, stream=None):
     """scores [..., n_q, n_k] float32 -> idx [..., n_q, k+n_local], count [..., n_q] int32."""
+    if scores.dim() < 2:
+        raise ValueError(f"scores must have at least 2 dimensions (got {tuple(scores.shape)})")
     n_q, n_k = scores.shape[-2], scores.shape[-1]
-    rows = scores.numel() // (n_q * n_k)
+    rows = scores.numel() // max(1, n_q * n_k)
+    _expect_rows(idx, (rows, n_q), k + n_local, "idx")
+    _expect_rows(count, (rows, n_q), None, "count")
     st = load().dsa_topk_select(_ptr(scores, "scores", torch.float32), rows, n_q, n_k, k, n_local,
                                 int(bool(causal)), _ptr(idx, "idx", torch.int32),
                                 _ptr(count, "count", torch.int32), _stream(stream))
     _check(st, "dsa_topk_select")
 
 
-def dsa_sparse_attn_prefill(q, k, v, idx, count, block, window, scale, out, lse=None, stream=None):
+def _check_attn(q, k, v, out, lse):
+    """q, out [B,Hq,S,D]; k, v [B,Hkv,S,D]; lse [B,Hq,S]."""
+    _ndim(q, 4, "q")
+    _ndim(k, 4, "k")
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
-    width = idx.shape[-1] if idx is not None else 0
+    _expect(k, (B, Hkv, S, D), "k")
+    _expect(v, (B, Hkv, S, D), "v")
+    _expect(out, (B, Hq, S, D), "out")
+    _expect(lse, (B, Hq, S), "lse")
+    return B, Hq, Hkv, S, D
+
+
+def _check_lists(idx, count, units, n_rows, name="idx"):
+    """idx [*units, n_rows, width] and count [*units, n_rows]; returns width."""
+    if idx is None and count is None:
+        return 0
+    if idx is None or count is None:
+        raise ValueError("idx and count must be given together")
+    if idx.dim() < 1:
+        raise ValueError(f"{name} must have a last (list) dimension")
+    width = idx.shape[-1]
+    _expect(idx, (*units, n_rows, width), name)
+    _expect(count, (*units, n_rows), "count")
+    return width
+
+
+def dsa_sparse_attn_prefill(q, k, v, idx, count, block, window, scale, out, lse=None, stream=None):
+    B, Hq, Hkv, S, D = _check_attn(q, k, v, out, lse)
+    nb = -(-S // block) if block > 0 else 0
+    width = _check_lists(idx, count, (B, Hkv), nb)
     st = load().dsa_sparse_attn_prefill(
         _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S, D,
         _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), width, block, window,
@@ -176,8 +255,13 @@ def dsa_sparse_attn_prefill_backward_workspace_size(B, Hq, Hkv, S, D, block) -> 
 
 def dsa_sparse_attn_prefill_backward(q, k, v, out, lse, dout, idx, count, block, scale, workspace,
                                      dq, dk, dv, stream=None):
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, S, D = _check_attn(q, k, v, out, lse)
+    for t, name in ((dout, "dout"), (dq, "dq")):
+        _expect(t, (B, Hq, S, D), name)
+    for t, name in ((dk, "dk"), (dv, "dv")):
+        _expect(t, (B, Hkv, S, D), name)
+    nb = -(-S // block) if block > 0 else 0
+    _check_lists(idx, count, (B, Hkv), nb)
     st = load().dsa_sparse_attn_prefill_backward(
         _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype),
         _ptr(out, "out", q.dtype), _ptr(lse, "lse", torch.float32), _ptr(dout, "dout", q.dtype),
@@ -190,8 +274,12 @@ def dsa_sparse_attn_prefill_backward(q, k, v, out, lse, dout, idx, count, block,
 
 def dsa_sparse_attn_prefill_ex(q, k, v, idx, count, block, sel_heads, key_bias, scale, out,
                                lse=None, stream=None):
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, S, D = _check_attn(q, k, v, out, lse)
+    nb = -(-S // block) if block > 0 else 0
+    if sel_heads < 1 or Hq % sel_heads:
+        raise ValueError(f"sel_heads ({sel_heads}) must divide Hq ({Hq})")
+    _check_lists(idx, count, (B, Hq // sel_heads), nb)
+    _expect(key_bias, (B, Hkv, S), "key_bias")
     st = load().dsa_sparse_attn_prefill_ex(
         _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S, D,
         _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), idx.shape[-1], block,
@@ -202,7 +290,13 @@ def dsa_sparse_attn_prefill_ex(q, k, v, idx, count, block, sel_heads, key_bias, 
 
 def dsa_dma_weights(v, proj, gain, block, weights, block_scores=None, stream=None):
     """v [B,Hkv,S,D] -> weights [B,Hkv,S] (and block_scores [B,Hkv,nb,nb])."""
+    _ndim(v, 4, "v")
     B, Hkv, S, D = v.shape
+    nb = -(-S // block) if block > 0 else 0
+    _expect(proj, (Hkv, D), "proj")
+    _expect(gain, (Hkv,), "gain")
+    _expect(weights, (B, Hkv, S), "weights")
+    _expect(block_scores, (B, Hkv, nb, nb), "block_scores")
     st = load().dsa_dma_weights(_dtype_code(v), _ptr(v, "v"), B, Hkv, S, D,
                                 _ptr(proj, "proj", torch.float32), _ptr(gain, "gain", torch.float32),
                                 block, _ptr(weights, "weights", torch.float32),
@@ -213,8 +307,18 @@ def dsa_dma_weights(v, proj, gain, block, weights, block_scores=None, stream=Non
 def dsa_paged_append(k_new, v_new, page_table, seq_len, k_pool, v_pool, kmin, kmax, stream=None):
     """k_new, v_new [B,Hkv,D]; pools [n_pool,Hkv,page,D]; kmin/kmax [n_pool,Hkv,D];
     page_table [B,max_pages] int32; seq_len [B] int32 (incremented)."""
+    _ndim(k_new, 3, "k_new")
+    _ndim(k_pool, 4, "k_pool")
+    _ndim(page_table, 2, "page_table")
     B, Hkv, D = k_new.shape
     n_pool, _, page, _ = k_pool.shape
+    _expect(v_new, (B, Hkv, D), "v_new")
+    _expect(k_pool, (n_pool, Hkv, page, D), "k_pool")
+    _expect(v_pool, (n_pool, Hkv, page, D), "v_pool")
+    _expect(kmin, (n_pool, Hkv, D), "kmin")
+    _expect(kmax, (n_pool, Hkv, D), "kmax")
+    _expect(page_table, (B, page_table.shape[1]), "page_table")
+    _expect(seq_len, (B,), "seq_len")
     st = load().dsa_paged_append(
         _dtype_code(k_new), _ptr(k_new, "k_new"), _ptr(v_new, "v_new", k_new.dtype), B, Hkv, D, page,
         page_table.shape[1], _ptr(page_table, "page_table", torch.int32),
@@ -226,8 +330,16 @@ def dsa_paged_append(k_new, v_new, page_table, seq_len, k_pool, v_pool, kmin, km
 
 def dsa_paged_page_scores(q, kmin, kmax, page, page_table, seq_len, scores, stream=None):
     """q [B,Hq,D]; kmin/kmax [n_pool,Hkv,D] -> scores [B,Hkv,max_pages]."""
+    _ndim(q, 3, "q")
+    _ndim(kmin, 3, "kmin")
+    _ndim(page_table, 2, "page_table")
     B, Hq, D = q.shape
     n_pool, Hkv, _ = kmin.shape
+    _expect(kmin, (n_pool, Hkv, D), "kmin")
+    _expect(kmax, (n_pool, Hkv, D), "kmax")
+    _expect(page_table, (B, page_table.shape[1]), "page_table")
+    _expect(seq_len, (B,), "seq_len")
+    _expect_rows(scores, (B, Hkv), page_table.shape[1], "scores")
     st = load().dsa_paged_page_scores(
         _dtype_code(q), _ptr(q, "q"), _ptr(kmin, "kmin", q.dtype), _ptr(kmax, "kmax", q.dtype), B, Hq,
         Hkv, D, page, page_table.shape[1], _ptr(page_table, "page_table", torch.int32),
@@ -238,8 +350,18 @@ def dsa_paged_page_scores(q, kmin, kmax, page, page_table, seq_len, scores, stre
 
 def dsa_paged_decode(q, k_pool, v_pool, page_table, seq_len, idx, count, scale, workspace, out,
                      stream=None):
+    _ndim(q, 3, "q")
+    _ndim(k_pool, 4, "k_pool")
+    _ndim(page_table, 2, "page_table")
     B, Hq, D = q.shape
     n_pool, Hkv, page, _ = k_pool.shape
+    _expect(k_pool, (n_pool, Hkv, page, D), "k_pool")
+    _expect(v_pool, (n_pool, Hkv, page, D), "v_pool")
+    _expect(page_table, (B, page_table.shape[1]), "page_table")
+    _expect(seq_len, (B,), "seq_len")
+    _expect_rows(idx, (B, Hkv), idx.shape[-1], "idx")
+    _expect_rows(count, (B, Hkv), None, "count")
+    _expect(out, (B, Hq, D), "out")
     st = load().dsa_paged_decode(
         _dtype_code(q), _ptr(q, "q"), _ptr(k_pool, "k_pool", q.dtype), _ptr(v_pool, "v_pool", q.dtype),
         B, Hq, Hkv, D, page, page_table.shape[1], _ptr(page_table, "page_table", torch.int32),
@@ -250,7 +372,11 @@ def dsa_paged_decode(q, k_pool, v_pool, page_table, seq_len, idx, count, scale, 
 
 
 def dsa_page_minmax(k, page, kmin, kmax, stream=None):
+    _ndim(k, 4, "k")
     B, Hkv, L, D = k.shape
+    n_pages = L // page if page > 0 else 0
+    _expect_rows(kmin, (B, Hkv, n_pages), D, "kmin")
+    _expect_rows(kmax, (B, Hkv, n_pages), D, "kmax")
     st = load().dsa_page_minmax(_dtype_code(k), _ptr(k, "k"), B, Hkv, L, D, page,
                                 _ptr(kmin, "kmin", k.dtype), _ptr(kmax, "kmax", k.dtype),
                                 _stream(stream))
@@ -263,8 +389,15 @@ def dsa_sparse_attn_decode_workspace_size(B, Hq, Hkv, idx_width, page, D) -> int
 
 def dsa_sparse_attn_decode(q, k_cache, v_cache, idx, count, page, scale, workspace, out,
                            stream=None):
+    _ndim(q, 3, "q")
+    _ndim(k_cache, 4, "k_cache")
     B, Hq, D = q.shape
     Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _expect(k_cache, (B, Hkv, L, D), "k_cache")
+    _expect(v_cache, (B, Hkv, L, D), "v_cache")
+    _expect_rows(idx, (B, Hkv), idx.shape[-1], "idx")
+    _expect_rows(count, (B, Hkv), None, "count")
+    _expect(out, (B, Hq, D), "out")
     st = load().dsa_sparse_attn_decode(
         _dtype_code(q), _ptr(q, "q"), _ptr(k_cache, "k_cache", q.dtype),
         _ptr(v_cache, "v_cache", q.dtype), B, Hq, Hkv, L, D, _ptr(idx, "idx", torch.int32),
@@ -275,7 +408,12 @@ def dsa_sparse_attn_decode(q, k_cache, v_cache, idx, count, page, scale, workspa
 
 
 def dsa_nsa_compress(k, v, length, stride, ck, cv, stream=None):
+    _ndim(k, 4, "k")
     B, Hkv, S, D = k.shape
+    n_cmp = (S - length) // stride + 1 if length >= 1 and stride >= 1 and S >= length else 0
+    _expect(v, (B, Hkv, S, D), "v")
+    _expect(ck, (B, Hkv, n_cmp, D), "ck")
+    _expect(cv, (B, Hkv, n_cmp, D), "cv")
     st = load().dsa_nsa_compress(_dtype_code(k), _ptr(k, "k"), _ptr(v, "v", k.dtype), B, Hkv, S, D,
                                  length, stride, _ptr(ck, "ck", k.dtype), _ptr(cv, "cv", k.dtype),
                                  _stream(stream))
@@ -284,8 +422,17 @@ def dsa_nsa_compress(k, v, length, stride, ck, cv, stream=None):
 
 def dsa_nsa_cmp_attn(q, ck, cv, length, stride, sel_block, scale, out, lse, block_scores=None,
                      stream=None):
+    _ndim(q, 4, "q")
+    _ndim(ck, 4, "ck")
     B, Hq, S, D = q.shape
     Hkv = ck.shape[1]
+    n_cmp = (S - length) // stride + 1 if length >= 1 and stride >= 1 and S >= length else 0
+    nb = -(-S // sel_block) if sel_block > 0 else 0
+    _expect(ck, (B, Hkv, n_cmp, D), "ck")
+    _expect(cv, (B, Hkv, n_cmp, D), "cv")
+    _expect(out, (B, Hq, S, D), "out")
+    _expect(lse, (B, Hq, S), "lse")
+    _expect(block_scores, (B, Hkv, nb, nb), "block_scores")
     st = load().dsa_nsa_cmp_attn(
         _dtype_code(q), _ptr(q, "q"), _ptr(ck, "ck", q.dtype), _ptr(cv, "cv", q.dtype), B, Hq, Hkv,
         S, D, length, stride, sel_block, float(scale), _ptr(out, "out", q.dtype),
@@ -296,8 +443,15 @@ def dsa_nsa_cmp_attn(q, ck, cv, length, stride, sel_block, scale, out, lse, bloc
 
 def dsa_nsa_cmp_token_scores(q, ck, lse, length, stride, sel_block, scale, scores, stream=None):
     """Per-token selection scores [B,Hkv,S,nb] from the compressed branch's lse."""
+    _ndim(q, 4, "q")
+    _ndim(ck, 4, "ck")
     B, Hq, S, D = q.shape
     Hkv = ck.shape[1]
+    n_cmp = (S - length) // stride + 1 if length >= 1 and stride >= 1 and S >= length else 0
+    nb = -(-S // sel_block) if sel_block > 0 else 0
+    _expect(ck, (B, Hkv, n_cmp, D), "ck")
+    _expect(lse, (B, Hq, S), "lse")
+    _expect(scores, (B, Hkv, S, nb), "scores")
     st = load().dsa_nsa_cmp_token_scores(
         _dtype_code(q), _ptr(q, "q"), _ptr(ck, "ck", q.dtype), _ptr(lse, "lse", torch.float32), B,
         Hq, Hkv, S, D, length, stride, sel_block, float(scale),
@@ -308,8 +462,12 @@ def dsa_nsa_cmp_token_scores(q, ck, lse, length, stride, sel_block, scale, score
 def dsa_topk_select_tokens(scores, k, n_local, block, idx, count, stream=None):
     """scores [..., S, n_k] float32 (one row per token) -> idx [..., S, k+n_local],
     count [..., S] int32; token t's candidates are blocks 0 .. t // block - n_local."""
+    if scores.dim() < 2:
+        raise ValueError(f"scores must have at least 2 dimensions (got {tuple(scores.shape)})")
     S, n_k = scores.shape[-2], scores.shape[-1]
-    rows = scores.numel() // (S * n_k)
+    rows = scores.numel() // max(1, S * n_k)
+    _expect_rows(idx, (rows, S), k + n_local, "idx")
+    _expect_rows(count, (rows, S), None, "count")
     st = load().dsa_topk_select_tokens(_ptr(scores, "scores", torch.float32), rows, S, n_k, k,
                                        n_local, block, _ptr(idx, "idx", torch.int32),
                                        _ptr(count, "count", torch.int32), _stream(stream))
@@ -318,8 +476,8 @@ def dsa_topk_select_tokens(scores, k, n_local, block, idx, count, stream=None):
 
 def dsa_sparse_attn_tokens(q, k, v, idx, count, block, scale, out, lse=None, stream=None):
     """Selected branch with per-token lists idx [B,Hkv,S,W], count [B,Hkv,S]."""
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, S, D = _check_attn(q, k, v, out, lse)
+    _check_lists(idx, count, (B, Hkv), S)
     st = load().dsa_sparse_attn_tokens(
         _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S,
         D, _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), idx.shape[-1], block,
@@ -329,8 +487,10 @@ def dsa_sparse_attn_tokens(q, k, v, idx, count, block, scale, out, lse=None, str
 
 def dsa_nsa_window_combine(q, k, v, window, scale, o_cmp, o_sel, gate_logits, out, stream=None):
     """Sliding branch with the gated combine in its epilogue (o_win stays on chip)."""
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, S, D = _check_attn(q, k, v, out, None)
+    _expect(o_cmp, (B, Hq, S, D), "o_cmp")
+    _expect(o_sel, (B, Hq, S, D), "o_sel")
+    _expect(gate_logits, (B, S, Hq, 3), "gate_logits")
     st = load().dsa_nsa_window_combine(
         _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S,
         D, window, float(scale), _ptr(o_cmp, "o_cmp", q.dtype), _ptr(o_sel, "o_sel", q.dtype),
@@ -339,7 +499,11 @@ def dsa_nsa_window_combine(q, k, v, window, scale, o_cmp, o_sel, gate_logits, ou
 
 
 def dsa_nsa_combine(o_cmp, o_sel, o_win, gate_logits, out, stream=None):
+    _ndim(o_cmp, 4, "o_cmp")
     B, Hq, S, D = o_cmp.shape
+    for t, name in ((o_sel, "o_sel"), (o_win, "o_win"), (out, "out")):
+        _expect(t, (B, Hq, S, D), name)
+    _expect(gate_logits, (B, S, Hq, 3), "gate_logits")
     st = load().dsa_nsa_combine(_dtype_code(o_cmp), _ptr(o_cmp, "o_cmp"),
                                 _ptr(o_sel, "o_sel", o_cmp.dtype), _ptr(o_win, "o_win", o_cmp.dtype),
                                 _ptr(gate_logits, "gate_logits", torch.float32), B, Hq, S, D,

@@ -73,6 +73,17 @@ int check_block(int block, const char* what) {
 // row indices: keep every row count below 2^31
 bool rows_fit(long long a, long long b, long long c) { return a * b * c < (1ll << 31); }
 
+// The attention kernels address one KV group's query rows [G, S, D] and its
+// keys [S, D] through buffer descriptors with 32-bit byte ranges and 32-bit
+// element offsets: a group's G*S*D elements must stay below 2^31.
+int check_group_extent(long long G, long long S, long long D, const char* dim) {
+  REQUIRE(G * S * D < (1ll << 31), DSA_E_UNSUPPORTED,
+          "one KV group's rows (%lld * %s * D = %lld elements) must stay below 2^31, the range of "
+          "the kernels' 32-bit buffer offsets",
+          G, dim, G * S * D);
+  return DSA_OK;
+}
+
 #define TRY(x)                     \
   do {                             \
     const int _st = (x);           \
@@ -194,6 +205,7 @@ static int prefill_impl(int dtype, const void* q, const void* k, const void* v, 
   TRY(check_block(block, "block"));
   REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);
@@ -305,6 +317,7 @@ int dsa_sparse_attn_prefill_backward(int dtype, const void* q, const void* k, co
   TRY(check_block(block, "block"));
   REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   REQUIRE(idx_width >= 1, DSA_E_ARG, "idx_width must be >= 1 (got %d)", idx_width);
   const long long nb = (S + block - 1) / block;
@@ -369,6 +382,7 @@ int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const 
           L, page);
   REQUIRE(idx_width >= 1 && idx_width <= L / page, DSA_E_ARG,
           "idx_width must be in [1, L/page] (got %d)", idx_width);
+  TRY(check_group_extent(1, L, D, "L"));
   REQUIRE(B * Hkv <= 65535, DSA_E_UNSUPPORTED, "B*Hkv must be at most 65535");
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   REQUIRE_PTR(q);
@@ -500,6 +514,7 @@ int dsa_nsa_cmp_token_scores(int dtype, const void* q, const void* ck, const flo
           stride);
   REQUIRE(S >= len, DSA_E_ARG, "S (%d) must be >= len (%d)", S, len);
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   REQUIRE(Hq / Hkv <= 16, DSA_E_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
           Hq / Hkv);
@@ -533,6 +548,7 @@ int dsa_sparse_attn_tokens(int dtype, const void* q, const void* k, const void* 
   REQUIRE(idx_width >= 1 && idx_width <= 64, DSA_E_UNSUPPORTED,
           "idx_width must be in [1, 64] (got %d)", idx_width);
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
   REQUIRE(rows_fit(B * Hkv, S, idx_width), DSA_E_ARG, "B*Hkv*S*idx_width too large");
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   REQUIRE_PTR(q);
@@ -579,6 +595,7 @@ int dsa_nsa_cmp_attn(int dtype, const void* q, const void* ck, const void* cv, i
   REQUIRE(S >= len, DSA_E_ARG, "S (%d) must be >= len (%d)", S, len);
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
   const int n_cmp = (S - len) / stride + 1;
   REQUIRE(n_cmp <= 8192, DSA_E_UNSUPPORTED, "at most 8192 summaries (got %d)", n_cmp);
   REQUIRE_PTR(q);
@@ -625,6 +642,7 @@ int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* 
   REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
   REQUIRE(window >= 1, DSA_E_ARG, "window must be >= 1 (got %d)", window);
   REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
   REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
   REQUIRE_PTR(q);
   REQUIRE_PTR(k);

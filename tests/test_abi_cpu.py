@@ -267,3 +267,44 @@ def test_window_combine_validation():
     assert f(*a) == L.DSA_E_UNSUPPORTED                            # G = 2: fewer than 256 rows
     a = list(args); a[9] = 9000
     assert f(*a) == L.DSA_E_UNSUPPORTED                            # window too long
+
+
+def test_offsets_beyond_32_bits_are_rejected():
+    """Kernels address one KV group's rows with 32-bit buffer offsets: a
+    group of G * S * D >= 2^31 elements is refused before any launch, in
+    every attention call and in decode (L * D).  (Every call here fails
+    validation, so the fake pointers never reach a kernel.)"""
+    lib = L.load()
+    S = 1 << 20                                   # 16 heads per group * 2^20 * 128 = 2^31
+    f = lib.dsa_sparse_attn_prefill
+    assert f(1, FAKE, FAKE, FAKE, 1, 32, 2, S, 128, FAKE, FAKE, 24, 64, 0, 0.1, FAKE, None,
+             None) == L.DSA_E_UNSUPPORTED
+    assert "2^31" in _err()
+    assert lib.dsa_nsa_window_combine(1, FAKE, FAKE, FAKE, 1, 32, 2, S, 128, 512, 0.1, FAKE, FAKE,
+                                      FAKE, FAKE, None) == L.DSA_E_UNSUPPORTED
+    assert lib.dsa_nsa_cmp_attn(1, FAKE, FAKE, FAKE, 1, 32, 2, S, 128, 32, 16, 64, 0.1, FAKE,
+                                FAKE, None, None) == L.DSA_E_UNSUPPORTED
+    L_ = 1 << 24                                  # 2^24 * 128 = 2^31
+    ws = lib.dsa_sparse_attn_decode_workspace_size(1, 8, 8, 102, 64, 128)
+    assert lib.dsa_sparse_attn_decode(1, FAKE, FAKE, FAKE, 1, 8, 8, L_, 128, FAKE, FAKE, 102, 64,
+                                      0.1, FAKE, ws, FAKE, None) == L.DSA_E_UNSUPPORTED
+    assert "2^31" in _err()
+
+
+def test_bad_layouts_are_rejected():
+    """Sizes that do not describe a valid dense layout fail validation: a
+    cache length that is not a whole number of pages, a page list wider than
+    the cache, summaries longer than the sequence, misaligned buffers."""
+    lib = L.load()
+    ws = lib.dsa_sparse_attn_decode_workspace_size(1, 8, 8, 4, 64, 128)
+    dec = lib.dsa_sparse_attn_decode
+    assert dec(1, FAKE, FAKE, FAKE, 1, 8, 8, 1000, 128, FAKE, FAKE, 4, 64, 0.1, FAKE, ws, FAKE,
+               None) == L.DSA_E_ARG                                # L % page != 0
+    assert dec(1, FAKE, FAKE, FAKE, 1, 8, 8, 256, 128, FAKE, FAKE, 5, 64, 0.1, FAKE, ws, FAKE,
+               None) == L.DSA_E_ARG                                # 5 pages of a 4-page cache
+    assert dec(1, FAKE, MISALIGNED, FAKE, 1, 8, 8, 256, 128, FAKE, FAKE, 4, 64, 0.1, FAKE, ws,
+               FAKE, None) == L.DSA_E_ARG
+    assert "aligned" in _err()
+    assert lib.dsa_page_minmax(1, FAKE, 1, 8, 1000, 128, 64, FAKE, FAKE, None) == L.DSA_E_ARG
+    assert lib.dsa_nsa_compress(1, FAKE, FAKE, 1, 4, 31, 128, 32, 16, FAKE, FAKE,
+                                None) == L.DSA_E_ARG               # S < len
