@@ -29,30 +29,14 @@
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
-// Query rows per workgroup = DSA_ATTN_NW waves x 32 x DSA_ATTN_QT.
-#ifndef DSA_ATTN_NW
-#define DSA_ATTN_NW 8
-#endif
-#ifndef DSA_ATTN_QT
-#define DSA_ATTN_QT 1
-#endif
-// Wave priority while issuing matrix instructions (0 = no change): a wave
-// in its MFMA phase wins issue over a wave doing softmax on the same SIMD.
-#ifndef DSA_ATTN_PRIO
-#define DSA_ATTN_PRIO 1
-#endif
-// D = 128: persistent workgroups (one per CU slot) walk the work items.
-#ifndef DSA_ATTN_PERSIST
-#define DSA_ATTN_PERSIST 1
-#endif
-// D = 128 epilogue: output rows staged through LDS for whole-row stores.
-#ifndef DSA_ATTN_OSTAGE
-#define DSA_ATTN_OSTAGE 1
-#endif
-// Minimum waves per SIMD the register allocation must allow.
-#ifndef DSA_ATTN_WAVES_PER_EU
+// Generic bf16 kernel: query rows per workgroup = kAttnWaves waves x 32.
+constexpr int kAttnWaves = 8;
+// Wave priority while issuing matrix instructions: a wave in its MFMA phase
+// wins issue over a wave doing softmax on the same SIMD.
+constexpr int kMfmaPrio = 1;
+// Minimum waves per SIMD the register allocation of the 8-wave kernels
+// must allow.
 #define DSA_ATTN_WAVES_PER_EU 2
-#endif
 
 namespace dsa {
 namespace {
@@ -312,7 +296,7 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
       for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][qt][r] = 0.f;
-    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
@@ -376,7 +360,7 @@ void k_attn_bf16(AttnArgs a, int wg_per_qb, int nqb,
       l[qt] += ls;
     }
 
-    __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+    __builtin_amdgcn_s_setprio(kMfmaPrio);
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
 #pragma unroll
@@ -483,15 +467,14 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   __shared__ int ucount;
   // epilogue: each wave's 32 output rows, 16-byte chunks XOR-swizzled by
   // row, and their log-sum-exp values
-  __shared__ __attribute__((aligned(16))) uint8_t ostage[DSA_ATTN_OSTAGE ? NW : 1][32 * D * 2];
-  __shared__ float lstage[DSA_ATTN_OSTAGE ? NW : 1][32];
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[NW][32 * D * 2];
+  __shared__ float lstage[NW][32];
 
   // Contiguous work per XCD keeps a group's K/V in that XCD's L2.  The
   // compressed branch is the exception: its work grows with the query block
   // (a contiguous range would give some XCDs only the longest blocks) and its
   // summaries are small, so its workgroups stay in dispatch order, dealt
   // round-robin over the XCDs.
-#if DSA_ATTN_PERSIST
   // Persistent workgroups: one per slot of the chip; workgroup j of XCD x
   // takes items x * per_xcd + j, + nwg, ... of that XCD's range.  The
   // compressed branch is launched with one workgroup per item (w_step =
@@ -501,10 +484,6 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd * per_xcd + slot;
   const int w_end = a.mode == MODE_CMP ? total : min(total, (xcd + 1) * per_xcd);
   const int w_step = a.mode == MODE_CMP ? int(gridDim.x) : nwg;
-#else
-  const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd_work_id(per_xcd);
-  const int w_end = min(total, w_first + 1), w_step = 1;
-#endif
   if (w_first >= w_end) return;
 
   // (sequence, selection unit): SH query heads sharing one index list and
@@ -874,7 +853,6 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   int p_b = 0, p_u = 0, p_sub = 0, p_t0 = 0;
   uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
   auto flush = [&]() __attribute__((always_inline)) {
-#if DSA_ATTN_OSTAGE
     // the wave's 32 rows: consecutive positions of one head (the launcher
     // sends blocks that are not a multiple of 32 rows elsewhere); four whole
     // 256-byte rows per store, marked streaming (nothing here reads them
@@ -896,7 +874,6 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
       if (a.lse && ln < 32 && tr0 + ln < a.S)
         a.lse[(size_t(p_b) * a.Hq + p_u * SH + hr) * a.S + tr0 + ln] = lstage[wave][ln];
     }
-#endif
   };
 
   if (prefetch_list) fetch_list(w_first);
@@ -934,11 +911,11 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
       }
       const bool mine = !UNION || (((n < 64 ? sel_lo : sel_hi) >> (n & 63)) & 1);   // wave-uniform
       if (mine) {
-        __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+        __builtin_amdgcn_s_setprio(kMfmaPrio);
         qk(n & 1);
         __builtin_amdgcn_s_setprio(0);
         softmax(n);
-        __builtin_amdgcn_s_setprio(DSA_ATTN_PRIO);
+        __builtin_amdgcn_s_setprio(kMfmaPrio);
         pv(n & 1);
         __builtin_amdgcn_s_setprio(0);
       }
@@ -957,62 +934,50 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
     const float lse_v = lt > 0.f ? (m + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
     const size_t orow = ((size_t(e_b) * a.Hq + e_row_h) * a.S + e_row_t) * D;
     uint16_t* dst = op + orow;
-    if (a.gate_z != nullptr || !DSA_ATTN_OSTAGE) {
-      if (a.gate_z != nullptr) {
-        if (e_row_ok) {
-          // gated combine with the other two branches' outputs (this branch
-          // in float32, the others as stored), rounded once
-          const float* z = a.gate_z + ((size_t(e_b) * a.S + e_row_t) * a.Hq + e_row_h) * 3;
-          const float g1 = 1.f / (1.f + __expf(-z[0]));
-          const float g2 = 1.f / (1.f + __expf(-z[1]));
-          const float g3 = inv / (1.f + __expf(-z[2]));
-          const uint16_t* p1 = static_cast<const uint16_t*>(a.gate_o1) + orow;
-          const uint16_t* p2 = static_cast<const uint16_t*>(a.gate_o2) + orow;
-          // a half row's loads before its stores: the stores may alias them
-          // as far as the compiler knows, so interleaving would serialise
-          // every load
+    if (a.gate_z != nullptr) {
+      if (e_row_ok) {
+        // gated combine with the other two branches' outputs (this branch
+        // in float32, the others as stored), rounded once
+        const float* z = a.gate_z + ((size_t(e_b) * a.S + e_row_t) * a.Hq + e_row_h) * 3;
+        const float g1 = 1.f / (1.f + __expf(-z[0]));
+        const float g2 = 1.f / (1.f + __expf(-z[1]));
+        const float g3 = inv / (1.f + __expf(-z[2]));
+        const uint16_t* p1 = static_cast<const uint16_t*>(a.gate_o1) + orow;
+        const uint16_t* p2 = static_cast<const uint16_t*>(a.gate_o2) + orow;
+        // a half row's loads before its stores: the stores may alias them
+        // as far as the compiler knows, so interleaving would serialise
+        // every load
 #pragma unroll
-          for (int d2 = 0; d2 < D / 64; ++d2) {
-            u32x2 w1[2][4], w2[2][4];
+        for (int d2 = 0; d2 < D / 64; ++d2) {
+          u32x2 w1[2][4], w2[2][4];
 #pragma unroll
-            for (int dh = 0; dh < 2; ++dh)
+          for (int dh = 0; dh < 2; ++dh)
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int off = (2 * d2 + dh) * 32 + rr * 8 + half * 4;
-                w1[dh][rr] = *reinterpret_cast<const u32x2*>(p1 + off);
-                w2[dh][rr] = *reinterpret_cast<const u32x2*>(p2 + off);
+            for (int rr = 0; rr < 4; ++rr) {
+              const int off = (2 * d2 + dh) * 32 + rr * 8 + half * 4;
+              w1[dh][rr] = *reinterpret_cast<const u32x2*>(p1 + off);
+              w2[dh][rr] = *reinterpret_cast<const u32x2*>(p2 + off);
+            }
+#pragma unroll
+          for (int dh = 0; dh < 2; ++dh)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int dt = 2 * d2 + dh;
+              u32x2 pk;
+#pragma unroll
+              for (int x = 0; x < 2; ++x) {
+                const float lo = g1 * bf16lo(w1[dh][rr][x]) + g2 * bf16lo(w2[dh][rr][x]) + g3 * o[dt][rr * 4 + 2 * x];
+                const float hi = g1 * bf16hi(w1[dh][rr][x]) + g2 * bf16hi(w2[dh][rr][x]) + g3 * o[dt][rr * 4 + 2 * x + 1];
+                pk[x] = pack_bf16x2(lo, hi);
               }
-#pragma unroll
-            for (int dh = 0; dh < 2; ++dh)
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const int dt = 2 * d2 + dh;
-                u32x2 pk;
-#pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                  const float lo = g1 * bf16lo(w1[dh][rr][x]) + g2 * bf16lo(w2[dh][rr][x]) + g3 * o[dt][rr * 4 + 2 * x];
-                  const float hi = g1 * bf16hi(w1[dh][rr][x]) + g2 * bf16hi(w2[dh][rr][x]) + g3 * o[dt][rr * 4 + 2 * x + 1];
-                  pk[x] = pack_bf16x2(lo, hi);
-                }
-                *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
-              }
-          }
+              *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
+            }
         }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            u32x2 pk;
-            pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
-            pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
-            if (e_row_ok) *reinterpret_cast<u32x2*>(dst + dt * 32 + rr * 8 + half * 4) = pk;
-          }
       }
       if (a.lse && half == 0 && e_row_ok) a.lse[(size_t(e_b) * a.Hq + e_row_h) * a.S + e_row_t] = lse_v;
     }
     begin(w_next);
-    if (a.gate_z == nullptr && DSA_ATTN_OSTAGE) {
+    if (a.gate_z == nullptr) {
       // A lane holds 8-byte pieces of its own row, so direct stores would
       // touch 32 rows per instruction.  The wave's 32 rows go to LDS (16-byte
       // chunks XOR-swizzled by row) and leave as whole rows in flush().
@@ -1132,26 +1097,18 @@ namespace {
 // per-query-head lists through the union kernel: 64-token blocks, the
 // group's heads filling whole workgroups, every union within the lane table
 bool uses_d128_union(const AttnArgs& a) {
-#if defined(DSA_ATTN_LEGACY) || !DSA_ATTN_PERSIST
-  return false;
-#else
   constexpr int ROWS = d128::NW * 32;
   const int G = a.Hq / a.Hkv;
   const int heads_per_wg = ROWS / 64;
   return a.dtype == 1 && a.D == 128 && a.mode == MODE_INDEX && a.block == 64 && a.sel_heads == 1 &&
          G > 1 && (G * 64) % ROWS == 0 && a.key_bias == nullptr && a.gate_z == nullptr &&
          heads_per_wg * a.idx_width <= d128::kMaxTiles && (a.S + 63) / 64 <= 256 * 32;
-#endif
 }
 
 bool uses_d128(const AttnArgs& a) {
-#ifdef DSA_ATTN_LEGACY
-  return false;
-#else
   const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
   return a.dtype == 1 && a.D == 128 && !kt32 && a.block % 32 == 0 && a.sel_heads * a.block >= 256 &&
          attn_max_tiles(a, 64) <= d128::kMaxTiles;
-#endif
 }
 }  // namespace
 
@@ -1174,14 +1131,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   }
   // key tile = 64 keys unless index-mode blocks are 32 tokens long
   const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
-#ifdef DSA_ATTN_KT128
-  if (a.D == 128 && a.mode == MODE_INDEX && a.block % 128 == 0)
-    return run_bf16<128, 128, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
-#endif
   // a selection unit with fewer rows than an eight-wave workgroup (per-head
   // selection) runs the generic kernel with as many waves as it has rows
   const int unit_rows = a.sel_heads * a.block;
-#ifndef DSA_ATTN_LEGACY
   if (uses_d128_union(a)) {
     constexpr int ROWS = d128::NW * 32;
     const int wg_per_qb = ((a.Hq / a.Hkv) * a.block + ROWS - 1) / ROWS;
@@ -1191,7 +1143,6 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     k_attn_bf16_d128<false, true><<<grid, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();
   }
-#endif
   if (unit_rows < 256) {
     const int nw = unit_rows <= 64 ? 2 : 4;
     if (a.D == 128)
@@ -1200,32 +1151,24 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     return kt32 ? (nw == 2 ? run_bf16<64, 32, 1, 2>(a, s) : run_bf16<64, 32, 1, 4>(a, s))
                 : (nw == 2 ? run_bf16<64, 64, 1, 2>(a, s) : run_bf16<64, 64, 1, 4>(a, s));
   }
-#ifndef DSA_ATTN_LEGACY
   if (uses_d128(a)) {
     constexpr int ROWS = d128::NW * 32;
     const int wg_per_qb = (a.sel_heads * a.block + ROWS - 1) / ROWS;
     const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
-#if DSA_ATTN_PERSIST
     // one resident workgroup per CU (registers allow two waves per SIMD); the
     // compressed branch, whose items differ in length, keeps one workgroup
     // per item so that the dispatcher balances them
     const int grid = a.mode == MODE_CMP ? total : kNumXcd * min(per_xcd, kAttnSlotsPerXcd);
-#else
-    const int grid = per_xcd * kNumXcd;
-#endif
     if (a.key_bias)
       k_attn_bf16_d128<true><<<grid, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     else
       k_attn_bf16_d128<false><<<grid, d128::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();
   }
-#endif
   if (a.D == 128)
-    return kt32 ? run_bf16<128, 32, DSA_ATTN_QT, DSA_ATTN_NW>(a, s)
-                : run_bf16<128, 64, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
-  return kt32 ? run_bf16<64, 32, DSA_ATTN_QT, DSA_ATTN_NW>(a, s)
-              : run_bf16<64, 64, DSA_ATTN_QT, DSA_ATTN_NW>(a, s);
+    return kt32 ? run_bf16<128, 32, 1, kAttnWaves>(a, s) : run_bf16<128, 64, 1, kAttnWaves>(a, s);
+  return kt32 ? run_bf16<64, 32, 1, kAttnWaves>(a, s) : run_bf16<64, 64, 1, kAttnWaves>(a, s);
 }
 
 }  // namespace dsa

@@ -12,8 +12,14 @@
  *   [SF]  The Sparse Frontier retelling, techwalker.com/2025/0429/3165971.shtml
  *
  * Conventions shared by every call
- *   - Tensors are dense and row-major with the last dimension contiguous;
- *     shapes are given in brackets.  bf16 tensors hold IEEE bfloat16 bits.
+ *   - Tensors are passed as bare pointers to dense row-major buffers whose
+ *     shapes are given in brackets; there are no strides.  Dense layouts
+ *     keep every block of keys (every page) one contiguous run ([NSA] §04:
+ *     selected blocks must be read contiguously), which the kernels' block
+ *     staging relies on; a caller holding strided views makes them dense
+ *     first.  The sizes passed are validated; the buffers' extents are the
+ *     caller's contract (the Python binding checks every tensor's shape).
+ *     bf16 tensors hold IEEE bfloat16 bits.
  *   - dtype is DSA_F32 or DSA_BF16 and applies to q, k, v and outputs of the
  *     same role; scores, log-sum-exp and gate logits are always float32;
  *     index and count tensors are int32.
@@ -280,7 +286,9 @@ int dsa_paged_decode(int dtype, const void* q, const void* k_pool, const void* v
  * Compressed keys / values for the coarse branch ([NSA] §03 "compressed
  * attention": a quick scan of summaries of the history).
  * ck, cv [B,Hkv,n_cmp,D] with n_cmp = (S-len)/stride + 1:
- * ck[c] = mean(K[c*stride .. c*stride+len-1]) (float32 sum, rounded once).
+ * ck[c] = mean(K[c*stride .. c*stride+len-1]): float64 sum, divided by len
+ * and rounded once to bf16 (nearest, ties to even), so a summary is the
+ * exactly rounded mean of its keys (of its values for cv).
  */
 int dsa_nsa_compress(int dtype, const void* k, const void* v, int B, int Hkv, int S, int D,
                      int len, int stride, void* ck, void* cv, void* stream);
