@@ -3,17 +3,22 @@
 
 Headline (the JSON line's `value`): tokens/s of the whole prefill path —
 pooled block scores, top-k + window selection, block-sparse attention — on
-the bf16 16K workload (B=1, 32 query / 8 KV heads, D=128, S=16384, block 64,
-top-16 blocks + 512-token window), inputs resident in HBM.  The line also
-carries the attention kernel's roofline (effective FLOPs on selected blocks
-against the bf16 MFMA peak), the decode path's HBM rate on the 128K-page
-workload, the long-prefill and three-branch workloads, the backward of the
-headline attention, the per-query-head selection and value-driven mask
-variants, decode over a paged pool with variable lengths, and the CPU oracle
-timed on a bounded sample of the headline workload.
+the largest prefill workload that fits one GPU, the bf16 64K mixture
+workload (B=1, 32 query / 8 KV heads, D=128, S=65536, block 128, top-32
+blocks + 1024-token window, keys from an 8-cluster mixture), inputs resident
+in HBM.  `roofline` is its attention kernel: effective FLOPs on selected
+blocks over the kernel's average launch time (HIP events on the launch
+stream) against the bf16 MFMA peak, with HBM traffic from committed counter
+summaries while the kernel source is unchanged.  The line also carries the
+16K prefill workload, the decode path's HBM rate on the 128K-page workload
+(with its own roofline block and a plain read stream as the achievable
+ceiling), the three-branch workload, the backward of the 16K attention, the
+per-query-head selection and value-driven mask variants, decode over a
+paged pool with variable lengths, and the CPU oracle timed on a bounded
+sample of the headline workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--only prefill|decode|long|nsa|nsa_tokens|backward|per_head|dma|paged]
+                    [--only prefill|prefill16k|decode|nsa|nsa_tokens|backward|per_head|dma|paged]
                     [--copy-calibration]
 """
 from __future__ import annotations
@@ -34,30 +39,42 @@ METRIC = "sparse-attn prefill tokens/s + effective TFLOP/s; decode HBM GB/s (1 G
 
 
 ATTN_KERNEL = "k_attn_bf16_d128"
-ATTN_SOURCE = os.path.join(ROOT, "dynamic_block_sparse_head_amd", "csrc", "k_attn.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_bf16_d128_prefill16k_traffic.txt")
+CSRC = os.path.join(ROOT, "dynamic_block_sparse_head_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+ATTN_TRAFFIC = (os.path.join(PROFILES, "k_attn_bf16_d128_prefill64k_traffic.txt"),
+                os.path.join(CSRC, "k_attn.hip"))
+ATTN16K_TRAFFIC = (os.path.join(PROFILES, "k_attn_bf16_d128_prefill16k_traffic.txt"),
+                   os.path.join(CSRC, "k_attn.hip"))
+DECODE_TRAFFIC = (os.path.join(PROFILES, "k_decode_split_decode128k_traffic.txt"),
+                  os.path.join(CSRC, "k_decode.hip"))
 
 
-def _measured_traffic():
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read
-    for a plain copy of known size), or None when the summary is missing or
-    was taken on a different version of the kernel source."""
+def _measured_traffic(spec, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by what the same counters read for a
+    plain copy of known size), or None when the summary is missing or was
+    taken on a different version of the kernel source."""
     import hashlib
+    path, source = spec
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
-                    key, val = line.split(":", 1)
-                    kv[key.strip()] = val.strip()
-        with open(ATTN_SOURCE, "rb") as f:
+                    k, val = line.split(":", 1)
+                    kv[k.strip()] = val.strip().split()[0]
+        with open(source, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
         if kv.get("source_sha256") != sha:
             return None
-        return int(float(kv["hbm_bytes_per_launch"]))
-    except (OSError, KeyError, ValueError):
+        return int(float(kv[key]))
+    except (OSError, KeyError, ValueError, IndexError):
         return None
+
+
+def _progress(msg):
+    """One line per finished stage on stderr (stdout carries only the JSON line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def _timed(fn, iters, torch):
@@ -88,64 +105,75 @@ def _timed_each(fn, iters, torch):
     return t[len(t) // 2], t[0], t[-1]
 
 
-def bench_prefill(args, torch):
-    from dynamic_block_sparse_head_amd import configs, inputs
+def bench_prefill(cfg, steps, warmup, torch):
+    """One prefill workload: the whole step (scores + selection + attention)
+    timed back to back over `steps` steps, the same step replayed as a HIP
+    graph, and each kernel alone (back-to-back average and per-call median,
+    min, max of the attention).  Effective FLOPs count every selected block
+    as a full tile: 4 D block^2 per (query head, selected key block)."""
+    from dynamic_block_sparse_head_amd import inputs
     from dynamic_block_sparse_head_amd.pipeline import GraphedStep, PrefillPlan
 
-    c = configs.PREFILL_16K
+    c = cfg
     x = inputs.prefill_inputs(c, seed=0, device="cuda")
     q, k, v = x["q"], x["k"], x["v"]
     plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         plan.run(q, k, v)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ms_step = _timed(lambda: plan.run(q, k, v), args.steps, torch)
+    ms_step = _timed(lambda: plan.run(q, k, v), steps, torch)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # the same step replayed as one HIP graph, for reference (the launches
-    # are not what separates the kernels: the gaps stay)
-    step = GraphedStep(lambda: plan.run(q, k, v), warmup=args.warmup)
-    ms_graph = _timed(step, args.steps, torch)
+    step = GraphedStep(lambda: plan.run(q, k, v), warmup=max(1, warmup))
+    ms_graph = _timed(step, steps, torch)
     torch.cuda.synchronize()
-    # the kernels one by one, same inputs (outputs rewritten identically)
-    reps = max(args.steps, 10)
+    reps = max(steps, 10)
     ms_scores = _timed(lambda: plan.score(q, k), reps, torch)
     ms_topk = _timed(plan.select, reps, torch)
     ms_attn = _timed(lambda: plan.attend(q, k, v), reps, torch)
     attn_each = _timed_each(lambda: plan.attend(q, k, v), max(reps, 20), torch)
-    count = plan.count.to(torch.int64)
-    sel = int(count.sum().item())                      # (group, query block, key block) triples
-    flops = 4.0 * c.D * c.block * c.block * c.G * sel  # each selected block as a full tile
-    tokens = c.B * c.S
-    return {
-        "cfg": c, "ms_step": ms_step, "wall_s": wall, "ms_scores": ms_scores, "ms_topk": ms_topk,
-        "ms_attn": ms_attn, "ms_graph": ms_graph, "selected_block_pairs": sel, "effective_flops": flops,
-        "attn_each": attn_each,
-        "tokens_per_step": tokens,
-    }
-
-
-def bench_long_prefill(torch, iters=5):
-    from dynamic_block_sparse_head_amd import configs, inputs
-    from dynamic_block_sparse_head_amd.pipeline import PrefillPlan
-
-    c = configs.PREFILL_64K
-    x = inputs.prefill_inputs(c, seed=0, device="cuda")
-    q, k, v = x["q"], x["k"], x["v"]
-    plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
-    plan.run(q, k, v)
-    ms_step = _timed(lambda: plan.run(q, k, v), iters, torch)
-    ms_attn = _timed(lambda: plan.attend(q, k, v), iters, torch)
-    sel = int(plan.count.to(torch.int64).sum().item())
+    sel = int(plan.count.to(torch.int64).sum().item())  # (group, query block, key block) triples
     flops = 4.0 * c.D * c.block * c.block * c.G * sel
-    del x, q, k, v, plan
-    return {"workload": f"{c.name}: B=1 Hq=32 Hkv=8 S=65536 D=128 block=128 top-32 + window 1024, "
-                        "8-cluster keys",
-            "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.S / (ms_step * 1e-3), 1),
-            "attn_ms": round(ms_attn, 4),
-            "attn_effective_tflops": round(flops / (ms_attn * 1e-3) / 1e12, 2),
-            "attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del x, q, k, v, plan, step
+    torch.cuda.empty_cache()
+    return {"cfg": c, "ms_step": ms_step, "ms_scores": ms_scores, "ms_topk": ms_topk,
+            "ms_attn": ms_attn, "ms_graph": ms_graph, "selected_block_pairs": sel,
+            "effective_flops": flops, "attn_each": attn_each, "tokens_per_step": c.B * c.S}
+
+
+def _workload(c):
+    keys = f", {c.n_clusters}-cluster keys" if c.keys == "mixture" else ""
+    return (f"{c.name}: B={c.B} Hq={c.Hq} Hkv={c.Hkv} S={c.S} D={c.D} block={c.block} "
+            f"top-{c.topk} + window {c.window}{keys} (scores + selection + attention)")
+
+
+def _roofline(r, traffic_spec):
+    tflops = r["effective_flops"] / (r["ms_attn"] * 1e-3) / 1e12
+    med = r["attn_each"][0]
+    return {"bound": "mfma", "kernel": ATTN_KERNEL,
+            "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": _measured_traffic(traffic_spec),
+            "flops_per_launch": r["effective_flops"],
+            "avg_launch_ms": round(r["ms_attn"], 4),
+            "per_call_ms_median_min_max": [round(x, 4) for x in r["attn_each"]],
+            "frac_at_per_call_median": round(r["effective_flops"] / (med * 1e-3) / 1e12
+                                             / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def _prefill_detail(r):
+    c = r["cfg"]
+    tflops = r["effective_flops"] / (r["ms_attn"] * 1e-3) / 1e12
+    return {"workload": _workload(c),
+            "ms_per_step": round(r["ms_step"], 4),
+            "tokens_per_s": round(r["tokens_per_step"] / (r["ms_step"] * 1e-3), 1),
+            "step_ms_graph_replay": round(r["ms_graph"], 4),
+            "scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
+            "attn_ms": round(r["ms_attn"], 4),
+            "attn_ms_per_call_median_min_max": [round(x, 4) for x in r["attn_each"]],
+            "attn_tokens_per_s": round(c.S / (r["ms_attn"] * 1e-3), 1),
+            "selected_block_pairs": r["selected_block_pairs"],
+            "attn_effective_tflops": round(tflops, 2),
+            "attn_frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def bench_decode(torch, iters=20, n_query_sets=4):
@@ -194,7 +222,13 @@ def bench_decode(torch, iters=20, n_query_sets=4):
         e[1].record(s)
         e[1].synchronize()
         t_graph += e[0].elapsed_time(e[1])
-    # reference: a plain device copy of 1 GiB (read + write) on the same GPU
+    # yardsticks: the library's plain read stream over the 1 GiB buffer (the
+    # achievable read rate), and a plain device copy of 512 MiB (read + write)
+    from dynamic_block_sparse_head_amd import binding as L
+    sink = torch.zeros(L.load().dsa_read_stream_sink_words(), dtype=torch.int32, device="cuda")
+    L.dsa_read_stream(flush, sink)
+    read_ms = _timed(lambda: L.dsa_read_stream(flush, sink), 5, torch)
+    read_gbs = flush.numel() * 4 / (read_ms * 1e-3) / 1e9
     src = flush[: (1 << 27)]
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -212,15 +246,23 @@ def bench_decode(torch, iters=20, n_query_sets=4):
     gbs = sel_bytes / (ms_attn * 1e-3) / 1e9
     copy_gbs = 2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9
     ms_graph = t_graph / iters
-    del x, qs, plan, flush, src, dst, step, q_in
+    del x, qs, plan, flush, src, dst, step, q_in, sink
+    torch.cuda.empty_cache()
     return {"workload": f"{c.name}: B=16 L=131072 page=64 Hq=32 Hkv=8 D=128, top {c.topk} of "
                         f"{c.n_pages} pages; LLC swept by a 1 GiB read between steps",
+            "roofline": {"bound": "hbm", "kernel": "k_decode_split + k_decode_merge",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": _measured_traffic(DECODE_TRAFFIC, "fetch_bytes_per_dispatch"),
+                         "bytes_per_launch": sel_bytes, "avg_launch_ms": round(ms_attn, 4),
+                         "frac_of_read_stream": round(gbs / read_gbs, 4)},
             "ms_per_step": round(ms_step, 4), "tokens_per_s": round(c.B / (ms_step * 1e-3), 1),
             "ms_per_step_graph_replay": round(ms_graph, 4),
             "attn_ms": round(ms_attn, 4), "selected_bytes": sel_bytes,
             "attn_hbm_gbs": round(gbs, 1), "attn_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "step_gbs_incl_metadata": round((sel_bytes + meta_bytes) / (ms_step * 1e-3) / 1e9, 1),
             "full_cache_bytes": cache_bytes,
+            "read_stream_gbs": round(read_gbs, 1),
             "device_copy_gbs": round(copy_gbs, 1),
             "page_metadata_build_ms": round(t_meta, 3)}
 
@@ -472,11 +514,22 @@ def bench_nsa_tokens(torch, iters=5):
             "selected_attn_unshared_kv_gb": round(kv_unshared / 1e9, 2)}
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(budget_s=20.0):
     """The oracle, untouched, on a bounded sample of the headline workload:
-    pooled scores for every block, then selection and attention (all 32 heads)
-    for query blocks spread over the sequence until the time budget is used."""
-    import numpy as np
+    pooled scores and selection for every query block, then attention (all
+    32 heads) for query blocks spread over the sequence until the time
+    budget is used; the whole workload's time is extrapolated per block."""
     import torch
 
     from dynamic_block_sparse_head_amd import configs, inputs
@@ -487,7 +540,7 @@ def cpu_baseline(budget_s=20.0):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    c = configs.PREFILL_16K
+    c = configs.PREFILL_64K
     x = inputs.prefill_inputs(c, seed=0, device="cpu")
     t0 = time.perf_counter()
     q = x["q"].to(torch.float64).numpy()
@@ -496,12 +549,13 @@ def cpu_baseline(budget_s=20.0):
     s = Op.block_scores_pooled(q, k, c.block)
     idx, cnt = Op.select_blocks(s, c.topk, c.n_local, causal=True)
     t_sel = time.perf_counter() - t0
-    order = list(range(c.n_blocks - 1, -1, -7)) + list(range(c.n_blocks - 2, -1, -7))
-    done = 0
+    order = list(range(c.n_blocks - 1, -1, -13)) + list(range(c.n_blocks - 7, -1, -13))
+    done, flops = 0, 0.0
     t1 = time.perf_counter()
     for i in order:
         Op.sparse_attention(q, k, v, idx, cnt, c.block, c.scale, q_blocks=[i])
         done += 1
+        flops += 4.0 * c.D * c.block * c.block * c.G * float(cnt[0, :, i].sum())
         if time.perf_counter() - t1 > budget_s:
             break
     t_attn = time.perf_counter() - t1
@@ -509,9 +563,12 @@ def cpu_baseline(budget_s=20.0):
     est_total = t_sel + per_block * c.n_blocks          # the whole workload at this rate
     return {"value": round(c.S / est_total, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "oracle_attn_gflops": round(flops / t_attn / 1e9, 2),
             "sample": (f"{c.name}: float64 numpy oracle; scores + selection for all {c.n_blocks} "
                        f"query blocks ({t_sel:.1f} s), attention for {done} of {c.n_blocks} query "
-                       f"blocks (all 32 heads, {t_attn:.1f} s); tokens/s = S / (selection time + "
+                       f"blocks spread over the sequence (all 32 heads, {t_attn:.1f} s, "
+                       f"{flops / 1e12:.2f} effective TFLOP); tokens/s = S / (selection time + "
                        f"per-block attention time x {c.n_blocks}); BLAS threads {threads}, "
                        f"host cpus {len(os.sched_getaffinity(0))}")}
 
@@ -532,8 +589,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "nsa", "nsa_tokens", "backward",
-                                       "per_head", "dma", "paged"], default=None)
+    ap.add_argument("--only", choices=["prefill", "prefill16k", "decode", "nsa", "nsa_tokens",
+                                       "backward", "per_head", "dma", "paged"], default=None)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -556,9 +613,9 @@ def main():
 
     extra = {}
     if args.only in (None, "prefill"):
-        r = bench_prefill(args, torch)
+        from dynamic_block_sparse_head_amd import configs
+        r = bench_prefill(configs.PREFILL_64K, args.steps, args.warmup, torch)
         c = r["cfg"]
-        tflops = r["effective_flops"] / (r["ms_attn"] * 1e-3) / 1e12
         line = {
             "metric": METRIC,
             "value": round(r["tokens_per_step"] / (r["ms_step"] * 1e-3), 1),
@@ -567,44 +624,31 @@ def main():
             "ms_per_step": round(r["ms_step"], 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"{c.name}: B=1 Hq=32 Hkv=8 S=16384 D=128 block=64 top-16 + "
-                                   "window 512 (scores + selection + attention)",
-                       "global_batch": c.B, "seq_len": c.S, "parallelism": "single GPU"},
-            "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL,
-                         "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": _measured_traffic(),
-                         "flops_per_launch": r["effective_flops"],
-                         "avg_launch_ms": round(r["ms_attn"], 4)},
-            "prefill": {"step_ms_graph_replay": round(r["ms_graph"], 4),
-                        "scores_ms": round(r["ms_scores"], 4), "topk_ms": round(r["ms_topk"], 4),
-                        "attn_ms": round(r["ms_attn"], 4),
-                        "attn_ms_per_call_median_min_max": [round(x, 4) for x in r["attn_each"]],
-                        "attn_tokens_per_s": round(c.S / (r["ms_attn"] * 1e-3), 1),
-                        "selected_block_pairs": r["selected_block_pairs"],
-                        "effective_tflops": round(tflops, 2)},
+            "config": {"workload": _workload(c), "global_batch": c.B, "seq_len": c.S,
+                       "parallelism": "single GPU"},
+            "roofline": _roofline(r, ATTN_TRAFFIC),
+            "prefill_64k": _prefill_detail(r),
         }
     else:
         line = {"metric": METRIC, "n_gpus": 1}
-    if args.only in (None, "decode"):
-        extra["decode"] = bench_decode(torch)
-    if args.only in (None, "long"):
-        extra["long_prefill"] = bench_long_prefill(torch)
-    if args.only in (None, "nsa"):
-        extra["nsa"] = bench_nsa(torch)
-    if args.only in (None, "nsa_tokens"):
-        extra["nsa_per_token"] = bench_nsa_tokens(torch)
-    if args.only in (None, "backward"):
-        extra["backward"] = bench_backward(torch)
-    if args.only in (None, "per_head"):
-        extra["per_head_selection"] = bench_per_head(torch)
-    if args.only in (None, "dma"):
-        extra["dma_mask"] = bench_dma(torch)
-    if args.only in (None, "paged"):
-        extra["paged_decode"] = bench_paged(torch)
+    if args.only in (None, "prefill16k"):
+        from dynamic_block_sparse_head_amd import configs
+        r16 = bench_prefill(configs.PREFILL_16K, args.steps, args.warmup, torch)
+        extra["prefill_16k"] = {**_prefill_detail(r16), "roofline": _roofline(r16, ATTN16K_TRAFFIC)}
+    legs = [("decode", "decode", bench_decode), ("nsa", "nsa", bench_nsa),
+            ("nsa_tokens", "nsa_per_token", bench_nsa_tokens),
+            ("backward", "backward", bench_backward),
+            ("per_head", "per_head_selection", bench_per_head), ("dma", "dma_mask", bench_dma),
+            ("paged", "paged_decode", bench_paged)]
+    _progress("prefill legs done")
+    for only, key, fn in legs:
+        if args.only in (None, only):
+            extra[key] = fn(torch)
+            _progress(f"{key} done")
     line.update(extra)
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         line["cpu_baseline"] = cpu_baseline()
+        _progress("cpu baseline done")
     print(json.dumps(line))
 
 

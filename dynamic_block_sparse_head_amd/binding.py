@@ -64,6 +64,8 @@ SIGNATURES = {
                                + [_c_float, _vp, _vp, _vp, _vp, _vp]),
     "dsa_sparse_attn_tokens": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
                                + [_c_int] * 2 + [_c_float, _vp, _vp, _vp]),
+    "dsa_read_stream_sink_words": (_c_size, []),
+    "dsa_read_stream": (_c_int, [_vp, _c_size, _vp, _c_size, _vp]),
 }
 
 _lib = None
@@ -509,3 +511,16 @@ def dsa_nsa_combine(o_cmp, o_sel, o_win, gate_logits, out, stream=None):
                                 _ptr(gate_logits, "gate_logits", torch.float32), B, Hq, S, D,
                                 _ptr(out, "out", o_cmp.dtype), _stream(stream))
     _check(st, "dsa_nsa_combine")
+
+
+def dsa_read_stream(src, sink, stream=None):
+    """Read every byte of src once (measurement helper); sink [>= sink words]
+    int32 receives one XOR word per workgroup."""
+    if not isinstance(src, torch.Tensor) or not isinstance(sink, torch.Tensor):
+        raise TypeError("src and sink must be torch.Tensors")
+    need = load().dsa_read_stream_sink_words()
+    if sink.numel() < need:
+        raise ValueError(f"sink has shape {tuple(sink.shape)}, expected at least {need} elements")
+    st = load().dsa_read_stream(_ptr(src, "src"), src.numel() * src.element_size(),
+                                _ptr(sink, "sink", torch.int32), sink.numel(), _stream(stream))
+    _check(st, "dsa_read_stream")

@@ -24,7 +24,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
 SOURCES = ["dsa_abi.cpp", "k_scores.hip", "k_topk.hip", "k_attn.hip", "k_decode.hip", "k_nsa.hip", "k_tok.hip",
-           "k_bwd.hip", "k_dma.hip"]
+           "k_bwd.hip", "k_dma.hip", "k_stream.hip"]
 
 
 def _compile(src: str) -> str:

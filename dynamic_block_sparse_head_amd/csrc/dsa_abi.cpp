@@ -698,4 +698,20 @@ int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void*
                     "dsa_nsa_combine");
 }
 
+size_t dsa_read_stream_sink_words(void) { return 2048; }
+
+int dsa_read_stream(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                    void* stream) {
+  g_err.clear();
+  REQUIRE_PTR(src);
+  REQUIRE(sink != nullptr, DSA_E_ARG, "sink must not be NULL");
+  REQUIRE(bytes >= 16 && bytes % 16 == 0, DSA_E_ARG,
+          "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  REQUIRE(sink_words >= dsa_read_stream_sink_words(), DSA_E_WORKSPACE,
+          "sink needs %zu words (got %zu)", dsa_read_stream_sink_words(), sink_words);
+  return hip_status(dsa::launch_read_stream(src, bytes, sink, int(dsa_read_stream_sink_words()),
+                                            static_cast<hipStream_t>(stream)),
+                    "dsa_read_stream");
+}
+
 }  // extern "C"

@@ -143,6 +143,11 @@ hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s);
 // needs Hq/Hkv <= 16 and (sel_block + len - 2) / stride <= 31
 hipError_t launch_cmp_token_scores(const CmpScoreArgs& a, hipStream_t s);
 
+// XOR of every 32-bit word of src [bytes / 4] folded into sink [n_wg], one
+// word per workgroup (bytes a multiple of 16).
+hipError_t launch_read_stream(const void* src, size_t bytes, uint32_t* sink, int n_wg,
+                              hipStream_t s);
+
 hipError_t launch_nsa_combine(const void* o1, const void* o2, const void* o3, const float* z,
                               int B, int Hq, int S, int D, void* out, hipStream_t s);
 

@@ -373,6 +373,20 @@ int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* 
                            const void* o_sel, const float* gate_logits, void* out,
                            void* stream);
 
+/*
+ * Measurement helper, not a step of the method: reads src [bytes] (device,
+ * 16-byte aligned, bytes a positive multiple of 16) once with 16-byte
+ * loads, eight in flight per lane, and writes sink[w] = XOR of the 32-bit
+ * words workgroup w read, for w < dsa_read_stream_sink_words() (the other
+ * sink words are untouched).  The XOR of all sink words is the XOR of every
+ * word of src.  Its rate is the achievable HBM read bandwidth that the
+ * memory-bound decode calls ([SF] §四: read only the selected pages) are
+ * compared with.  Errors: DSA_E_ARG (pointers, size), DSA_E_WORKSPACE (sink
+ * too small).
+ */
+size_t dsa_read_stream_sink_words(void);
+int dsa_read_stream(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 26
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -308,3 +308,14 @@ def test_bad_layouts_are_rejected():
     assert lib.dsa_page_minmax(1, FAKE, 1, 8, 1000, 128, 64, FAKE, FAKE, None) == L.DSA_E_ARG
     assert lib.dsa_nsa_compress(1, FAKE, FAKE, 1, 4, 31, 128, 32, 16, FAKE, FAKE,
                                 None) == L.DSA_E_ARG               # S < len
+
+
+def test_read_stream_validation():
+    lib = L.load()
+    n = lib.dsa_read_stream_sink_words()
+    assert n >= 256
+    assert lib.dsa_read_stream(FAKE, 0, FAKE, n, None) == L.DSA_E_ARG
+    assert lib.dsa_read_stream(FAKE, 24, FAKE, n, None) == L.DSA_E_ARG      # not 16-byte chunks
+    assert lib.dsa_read_stream(MISALIGNED, 32, FAKE, n, None) == L.DSA_E_ARG
+    assert lib.dsa_read_stream(FAKE, 32, None, n, None) == L.DSA_E_ARG
+    assert lib.dsa_read_stream(FAKE, 32, FAKE, n - 1, None) == L.DSA_E_WORKSPACE

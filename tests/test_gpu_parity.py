@@ -336,3 +336,19 @@ def test_decode_repeated_calls_identical():
         outs.append(plan.out.clone())
     _sync()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (64 << 20) + 16 * 37])
+def test_read_stream_reads_every_word(nbytes):
+    """The read-stream yardstick touches every word once: the XOR of its
+    per-workgroup words equals the XOR of the buffer."""
+    g = torch.Generator().manual_seed(nbytes)
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    n = L.load().dsa_read_stream_sink_words()
+    sink = torch.zeros(n + 5, dtype=torch.int32, device=DEV)
+    L.dsa_read_stream(src.to(DEV), sink)
+    _sync()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy()[:n].view(np.uint32))
+    want = np.bitwise_xor.reduce(src.numpy().view(np.uint32))
+    assert got == want
+    assert (sink.cpu().numpy()[n:] == 0).all()
