@@ -64,6 +64,8 @@ SIGNATURES = {
                                + [_c_float, _vp, _vp, _vp, _vp, _vp]),
     "dsa_sparse_attn_tokens": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
                                + [_c_int] * 2 + [_c_float, _vp, _vp, _vp]),
+    "dsa_sparse_attn_decode_noalloc": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                                       + [_c_int] * 2 + [_c_float, _vp, _vp]),
     "dsa_read_stream_sink_words": (_c_size, []),
     "dsa_read_stream": (_c_int, [_vp, _c_size, _vp, _c_size, _vp]),
 }
@@ -407,6 +409,27 @@ def dsa_sparse_attn_decode(q, k_cache, v_cache, idx, count, page, scale, workspa
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _ptr(out, "out", q.dtype), _stream(stream))
     _check(st, "dsa_sparse_attn_decode")
+
+
+def dsa_sparse_attn_decode_noalloc(q, k_cache, v_cache, idx, count, page, scale, out,
+                                   stream=None):
+    """dsa_sparse_attn_decode with the library's per-device scratch in place
+    of a workspace (allocates nothing; overlapping calls on one GPU race)."""
+    _ndim(q, 3, "q")
+    _ndim(k_cache, 4, "k_cache")
+    B, Hq, D = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    _expect(k_cache, (B, Hkv, L, D), "k_cache")
+    _expect(v_cache, (B, Hkv, L, D), "v_cache")
+    _expect_rows(idx, (B, Hkv), idx.shape[-1], "idx")
+    _expect_rows(count, (B, Hkv), None, "count")
+    _expect(out, (B, Hq, D), "out")
+    st = load().dsa_sparse_attn_decode_noalloc(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k_cache, "k_cache", q.dtype),
+        _ptr(v_cache, "v_cache", q.dtype), B, Hq, Hkv, L, D, _ptr(idx, "idx", torch.int32),
+        _ptr(count, "count", torch.int32), idx.shape[-1], page, float(scale),
+        _ptr(out, "out", q.dtype), _stream(stream))
+    _check(st, "dsa_sparse_attn_decode_noalloc")
 
 
 def dsa_nsa_compress(k, v, length, stride, ck, cv, stream=None):

@@ -365,11 +365,15 @@ size_t dsa_sparse_attn_decode_workspace_size(int B, int Hq, int Hkv, int idx_wid
   return dsa::decode_workspace_bytes(B, Hq, Hkv, idx_width, page, D);
 }
 
-int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
-                           int B, int Hq, int Hkv, int L, int D, const int32_t* idx,
-                           const int32_t* count, int idx_width, int page, float scale,
-                           void* workspace, size_t workspace_bytes, void* out, void* stream) {
-  g_err.clear();
+static_assert(dsa::kDecodeScratchBytes == DSA_DECODE_NOALLOC_SCRATCH_BYTES,
+              "the header and the kernels must agree on the decode scratch size");
+
+// Validation shared by the two decode calls; workspace == nullptr selects
+// the library's per-device scratch (dsa_sparse_attn_decode_noalloc).
+static int decode_impl(int dtype, const void* q, const void* k_cache, const void* v_cache, int B,
+                       int Hq, int Hkv, int L, int D, const int32_t* idx, const int32_t* count,
+                       int idx_width, int page, float scale, void* workspace,
+                       size_t workspace_bytes, bool noalloc, void* out, void* stream) {
   TRY(check_dtype(dtype, false));
   TRY(check_heads(B, Hq, Hkv));
   TRY(check_dim(D));
@@ -391,13 +395,40 @@ int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const 
   REQUIRE_PTR(out);
   REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
   const size_t need = dsa::decode_workspace_bytes(B, Hq, Hkv, idx_width, page, D);
-  REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
-          "decode needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
-  REQUIRE_PTR(workspace);
+  if (noalloc) {
+    REQUIRE(need <= DSA_DECODE_NOALLOC_SCRATCH_BYTES, DSA_E_WORKSPACE,
+            "this decode needs %zu bytes of partial results, more than the %zu-byte scratch of "
+            "dsa_sparse_attn_decode_noalloc (use dsa_sparse_attn_decode with a workspace)",
+            need, size_t(DSA_DECODE_NOALLOC_SCRATCH_BYTES));
+    const hipError_t e = dsa::decode_scratch(&workspace);
+    if (e != hipSuccess) return hip_status(e, "dsa_sparse_attn_decode_noalloc: scratch lookup");
+  } else {
+    REQUIRE(workspace != nullptr && workspace_bytes >= need, DSA_E_WORKSPACE,
+            "decode needs a workspace of %zu bytes (got %zu)", need, workspace_bytes);
+    REQUIRE_PTR(workspace);
+  }
   dsa::DecodeArgs a{q,  k_cache, v_cache, idx,   count, B, Hq, Hkv, L, D, idx_width, page,
                     scale, static_cast<float*>(workspace), out};
   return hip_status(dsa::launch_decode(a, static_cast<hipStream_t>(stream)),
-                    "dsa_sparse_attn_decode");
+                    noalloc ? "dsa_sparse_attn_decode_noalloc" : "dsa_sparse_attn_decode");
+}
+
+int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const void* v_cache,
+                           int B, int Hq, int Hkv, int L, int D, const int32_t* idx,
+                           const int32_t* count, int idx_width, int page, float scale,
+                           void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  g_err.clear();
+  return decode_impl(dtype, q, k_cache, v_cache, B, Hq, Hkv, L, D, idx, count, idx_width, page,
+                     scale, workspace, workspace_bytes, false, out, stream);
+}
+
+int dsa_sparse_attn_decode_noalloc(int dtype, const void* q, const void* k_cache,
+                                   const void* v_cache, int B, int Hq, int Hkv, int L, int D,
+                                   const int32_t* idx, const int32_t* count, int idx_width,
+                                   int page, float scale, void* out, void* stream) {
+  g_err.clear();
+  return decode_impl(dtype, q, k_cache, v_cache, B, Hq, Hkv, L, D, idx, count, idx_width, page,
+                     scale, nullptr, 0, true, out, stream);
 }
 
 // shared checks of the paged-cache calls

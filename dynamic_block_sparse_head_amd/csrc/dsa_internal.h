@@ -122,6 +122,10 @@ struct DecodeArgs {
 };
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int idx_width, int page, int D);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Size of the per-device scratch array of the non-allocating decode, and
+// its address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_paged_append(const void* k_new, const void* v_new, int B, int Hkv, int D,
                                int page, int max_pages, const int32_t* page_table,
                                int32_t* seq_len, int n_pool, void* k_pool, void* v_pool,

@@ -10,11 +10,19 @@
 // computes, for the group's G query heads, the chunk's running max, exp-sum
 // and unnormalised weighted value sum.  A merge kernel combines the chunks
 // of each (sequence, head) in chunk order (deterministic, no atomics).
+#include <mutex>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
 namespace dsa {
 namespace {
+
+// Partial results of dsa_sparse_attn_decode_noalloc: one copy per GPU, held
+// until the process ends.  Host code never names it directly (on the host
+// the name is only a stand-in for the symbol): decode_scratch() looks up
+// each device's address once and kernels receive that address.
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
 
 constexpr int kThreads = 256;
 constexpr int kMaxTok = 512;   // tokens per workgroup: 8 pages of 64, 4 of 128, ...
@@ -384,6 +392,25 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int idx_width, int page, i
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   return a.D == 128 ? run_d<128>(a, s) : run_d<64>(a, s);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dsa

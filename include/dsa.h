@@ -239,6 +239,26 @@ int dsa_sparse_attn_decode(int dtype, const void* q, const void* k_cache, const 
                            void* out, void* stream);
 
 /*
+ * dsa_sparse_attn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and results, with the partial
+ * results kept in a scratch array of DSA_DECODE_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends (its
+ * address is looked up on a device's first call).  Nothing is allocated or
+ * freed by the call.  A decode whose partial results exceed the scratch
+ * (more than dsa_sparse_attn_decode_workspace_size() would ask for) returns
+ * DSA_E_WORKSPACE.  Every partial result read in a call is written earlier
+ * in the same call, so the scratch needs no clearing; but all calls on one
+ * GPU share it, so calls that overlap in time on one GPU (different streams
+ * or threads) race and must be serialised by the caller.
+ */
+#define DSA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dsa_sparse_attn_decode_noalloc(int dtype, const void* q, const void* k_cache,
+                                   const void* v_cache, int B, int Hq, int Hkv, int L, int D,
+                                   const int32_t* idx, const int32_t* count, int idx_width,
+                                   int page, float scale, void* out, void* stream);
+
+/*
  * Paged KV cache for serving ([SF] §二-§四: the whole cache is kept and a
  * decode step reads only the pages it selects; here the cache of a whole
  * batch lives in one pool of pages).

@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -319,3 +319,28 @@ def test_read_stream_validation():
     assert lib.dsa_read_stream(MISALIGNED, 32, FAKE, n, None) == L.DSA_E_ARG
     assert lib.dsa_read_stream(FAKE, 32, None, n, None) == L.DSA_E_ARG
     assert lib.dsa_read_stream(FAKE, 32, FAKE, n - 1, None) == L.DSA_E_WORKSPACE
+
+
+def test_decode_noalloc_validation():
+    """The non-allocating decode validates like the workspace call and
+    refuses a decode whose partial results exceed its scratch, before it
+    touches the GPU."""
+    lib = L.load()
+    f = lib.dsa_sparse_attn_decode_noalloc
+    args = [1, FAKE, FAKE, FAKE, 16, 32, 8, 131072, 128, FAKE, FAKE, 102, 64, 0.1, FAKE, None]
+    limit = 16 << 20
+    assert lib.dsa_sparse_attn_decode_workspace_size(16, 32, 8, 102, 64, 128) <= limit
+    big = list(args); big[4] = 128                                  # 8x the batch
+    assert lib.dsa_sparse_attn_decode_workspace_size(128, 32, 8, 102, 64, 128) > limit
+    assert f(*big) == L.DSA_E_WORKSPACE
+    assert "scratch" in _err()
+    a = list(args); a[0] = 0
+    assert f(*a) == L.DSA_E_UNSUPPORTED                             # float32
+    a = list(args); a[12] = 96
+    assert f(*a) == L.DSA_E_UNSUPPORTED                             # page 96
+    a = list(args); a[11] = 5000
+    assert f(*a) == L.DSA_E_ARG                                     # more pages than the cache
+    a = list(args); a[9] = None
+    assert f(*a) == L.DSA_E_ARG                                     # no page lists
+    a = list(args); a[14] = MISALIGNED
+    assert f(*a) == L.DSA_E_ARG
