@@ -23,13 +23,17 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
          # packed fp32 VALU forms are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
+# k_attn.hip: matrix-core results stay in ordinary vector registers, where
+# the softmax reads them; otherwise the compiler puts the generic bf16 kernels'
+# scores in accumulation registers and copies each one out before use.
+FILE_FLAGS = {"k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 SOURCES = ["dsa_abi.cpp", "k_scores.hip", "k_topk.hip", "k_attn.hip", "k_decode.hip", "k_nsa.hip", "k_tok.hip",
            "k_bwd.hip", "k_dma.hip", "k_stream.hip"]
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

@@ -1008,6 +1008,400 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
   }
 }
 
+// -------------------------- bf16, D = 128, software-pipelined within each wave
+// The tiles, LDS layouts and MFMA shapes of k_attn_bf16_d128 (eight waves of
+// 32 query rows, two waves per SIMD), with each wave's softmax moved into
+// the shadow of its own matrix products.  Measured on gfx950: a wave that
+// issues its own products keeps the matrix core busy while it runs a few
+// independent vector instructions between them, and two such waves per SIMD
+// do better still; a wave whose vector work waits for its own products (the
+// plain order Q.K, softmax, P.V) leaves the other wave to fill the gaps,
+// which it does poorly.  So:
+//  * keys advance in steps of 32 (the two halves of a 64-key LDS tile);
+//  * step g issues P.V of step g-2 and Q.K of step g on the matrix core and,
+//    between those products, the softmax of step g-1 (scores and
+//    probabilities are double-buffered by step parity);
+//  * P.V trails Q.K by two steps, i.e. one 64-key tile: tile n's keys and
+//    tile n-1's values are read while tile n+1's keys and tile n's values
+//    stream into the other buffers by direct-to-LDS loads; one barrier per
+//    tile;
+//  * the softmax's common path takes no maximum: probabilities are taken
+//    against the row's current reference and summed in float32; a step in
+//    which some lane's 16-key partial sum exceeds 2^8 (or whose row has no
+//    reference yet) takes the slow path, which moves the reference as the
+//    other kernels do and redoes that step's probabilities.
+namespace w2 {
+constexpr int D = 128, KT = 64, NW = 8, NT = NW * 64, ROWS = NW * 32;
+constexpr int KCH = d128::KCH, VCH = d128::VCH, KBYTES = d128::KBYTES, VBYTES = d128::VBYTES;
+constexpr int kMaxTiles = 128;
+// a lane's partial sum of one step above this (or not a number) sends the
+// step through the slow path
+constexpr float kSumLimit = 256.0f;
+}  // namespace w2
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at dst + 16 l (dst uniform across the wave).  Issued from inline assembly so
+// the compiler does not wait for these loads before unrelated LDS reads; the
+// kernel waits for them itself (vmcnt) before the barrier that publishes a
+// tile.  The instruction writes no register.
+__device__ __forceinline__ void lds_load16(const void* src, void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+__global__ __launch_bounds__(w2::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
+  using namespace w2;
+  // K and V double-buffered; after an item's last step the same bytes stage
+  // its output rows (32 x 256 B per wave)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KBYTES + 2 * VBYTES];
+  __shared__ float lstage[NW][32];
+  static_assert(2 * KBYTES + 2 * VBYTES >= NW * 32 * D * 2, "output staging fits the tile buffers");
+  uint8_t* const kbase = smem;
+  uint8_t* const vbase = smem + 2 * KBYTES;
+
+  // persistent workgroups (one per CU); the compressed branch runs one
+  // workgroup per item, dealt round-robin (its items differ in length)
+  const int nwg = int(gridDim.x) / kNumXcd;
+  const int xcd = int(blockIdx.x) % kNumXcd, slot = int(blockIdx.x) / kNumXcd;
+  const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd * per_xcd + slot;
+  const int w_end = a.mode == MODE_CMP ? total : min(total, (xcd + 1) * per_xcd);
+  const int w_step = a.mode == MODE_CMP ? int(gridDim.x) : nwg;
+
+  const int SH = a.sel_heads, U = a.Hq / SH;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const float c = a.scale * kLog2e;
+  const uint32_t k_rd = (col & 15) * KCH + (col >> 4) * 256 + half * 16;
+  const uint32_t v_rd = ((lane & 15) >> 2) * VCH + half * 256 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8;
+  // direct-to-LDS staging: wave w moves K chunks 2w, 2w+1 (chunk j holds keys
+  // j, j+16, j+32, j+48) and V chunks 2w, 2w+1 (chunk j holds keys
+  // 16 (j/4) + 4 q + j%4, q = 0..3); lane l carries row l/16 of a chunk,
+  // bytes 16 (l%16) .. 16 (l%16) + 15 of its key
+  const int lq = lane >> 4, lc = lane & 15;
+
+  // per item
+  int ntiles = 0, key0_w0 = 0, key0_w1 = 0;
+  int row_lo = 0, row_hi = -1, blk_lo = 0, blk_hi = -1;
+  bf16x8 qf[D / 16];
+  floatx16 o[D / 32];
+  floatx16 s[2];       // S^T of a 32-key step, by step parity
+  bf16x8 pb[2][2];     // its probabilities as the P.V operand, by step parity
+  float m = 0.f, l = 0.f, lsum = 0.f, alpha = 1.f;
+  bool rescale = false;
+  const uint16_t* kg = nullptr;
+  const uint16_t* vg = nullptr;
+
+  auto key0_of = [&](int n) __attribute__((always_inline)) -> int {
+    const int lo = __builtin_amdgcn_readlane(key0_w0, n & 63);
+    const int hi = __builtin_amdgcn_readlane(key0_w1, n & 63);
+    return n < 64 ? lo : hi;
+  };
+  auto kbuf = [&](int n) __attribute__((always_inline)) -> uint8_t* { return kbase + (n & 1) * KBYTES; };
+  auto vbuf = [&](int n) __attribute__((always_inline)) -> uint8_t* { return vbase + (n & 1) * VBYTES; };
+  // keys of tile nk and values of tile nv into their buffers (nk or nv < 0:
+  // none); rows outside the keys read the nearest key (keys past the end are
+  // masked for every row, and a list entry outside the sequence cannot send
+  // a load outside the buffer)
+  auto dma = [&](int nk, int nv) __attribute__((always_inline)) {
+    if (nk >= 0) {
+      const int key0 = key0_of(nk);
+      const bool clip = key0 < 0 || key0 + KT > a.Skv;   // uniform
+      uint8_t* kd = kbuf(nk);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * wave + jj;
+        int key = key0 + 16 * lq + j;
+        if (clip) key = min(max(key, 0), a.Skv - 1);
+        lds_load16(kg + size_t(key) * D + lc * 8, kd + j * KCH);
+      }
+    }
+    if (nv >= 0) {
+      const int key0 = key0_of(nv);
+      const bool clip = key0 < 0 || key0 + KT > a.Skv;
+      uint8_t* vd = vbuf(nv);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * wave + jj;
+        int key = key0 + 16 * (j >> 2) + 4 * lq + (j & 3);
+        if (clip) key = min(max(key, 0), a.Skv - 1);
+        lds_load16(vg + size_t(key) * D + lc * 8, vd + j * VCH);
+      }
+    }
+  };
+  auto wait_loads = [&]() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // probabilities of the step in s[P] against reference mu into pb[P];
+  // lsum = this lane's float32 sum of them (the slow path's recomputation)
+  auto probs = [&](auto P, float mu) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = fast_exp2(fmaf(s[p][kk * 8 + e], c, -mu));
+        acc[e & 3] += x;
+        pb[p][kk][e] = static_cast<__bf16>(x);
+      }
+    lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+
+  // One step, in explicit issue order: NPV products of P.V (step gpv, operand
+  // pb[parity of gpv]) and NQK of Q.K (step gqk, into s[parity of gqk]) on
+  // the matrix core, each product's operand read from LDS two products
+  // ahead, and after each product one sixteenth of the common-path softmax
+  // of the step in s[PS] against the current reference (when SM): score e's
+  // probability and its contribution to the row sum, and every second score
+  // the bf16 pair.  The scheduling barriers keep this order.
+  auto body = [&](auto NPV, auto NQK, auto SM, auto PS, int gpv, int gqk) __attribute__((always_inline)) {
+    constexpr int npv = decltype(NPV)::value, nqk = decltype(NQK)::value;
+    constexpr bool sm = decltype(SM)::value;
+    constexpr int ps = decltype(PS)::value;   // parity of the softmax step
+    constexpr int pp = ps ^ 1;                // parity of the P.V and Q.K steps
+    constexpr int N = npv + nqk;
+    constexpr int NI = N > 16 ? N : 16;
+    const uint8_t* vp = vbuf(gpv >> 1) + (gpv & 1) * 2 * 4352 + v_rd;
+    const uint8_t* kp = kbuf(gqk >> 1) + (gqk & 1) * 512 + k_rd;
+    (void)vp;
+    (void)kp;
+    auto read_op = [&](auto I) __attribute__((always_inline)) -> bf16x8 {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i < npv) {
+        constexpr int kk = i / 4, dt = i % 4;
+        const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DSA_LDS_BF16X4(vp + kk * 4352 + dt * 64));
+        const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(DSA_LDS_BF16X4(vp + kk * 4352 + 512 + dt * 64));
+        return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else {
+        constexpr int ks = i - npv;
+        return *reinterpret_cast<const bf16x8*>(kp + ks * 32);
+      }
+    };
+    const float nmu = -m;
+    float pe[16];
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 op[3];
+    if constexpr (N > 0) op[0] = read_op(std::integral_constant<int, 0>{});
+    if constexpr (N > 1) op[1] = read_op(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    auto one = [&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if constexpr (i + 2 < N) op[(i + 2) % 3] = read_op(std::integral_constant<int, i + 2>{});
+      if constexpr (i < npv) {
+        constexpr int kk = i / 4, dt = i % 4;
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pb[pp][kk], o[dt], 0, 0, 0);
+      } else if constexpr (i < N) {
+        constexpr int ks = i - npv;
+        s[pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qf[ks], ks == 0 ? floatx16{} : s[pp], 0, 0, 0);
+      }
+      if constexpr (sm && i < 16) {
+        pe[i] = fast_exp2(fmaf(s[ps][i], c, nmu));
+        acc[i % 4] += pe[i];
+        if constexpr (i % 2 == 1) {
+          pb[ps][i / 8][(i % 8) - 1] = static_cast<__bf16>(pe[i - 1]);
+          pb[ps][i / 8][i % 8] = static_cast<__bf16>(pe[i]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    [&]<int... Is>(std::integer_sequence<int, Is...>) __attribute__((always_inline)) {
+      (one(std::integral_constant<int, Is>{}), ...);
+    }(std::make_integer_sequence<int, NI>{});
+    if constexpr (sm) lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+  // after the common-path softmax of the step in s[PS]: the slow path where
+  // needed, then the row sum
+  auto finish = [&](auto PS) __attribute__((always_inline)) {
+    if (__any(!(lsum <= kSumLimit))) {   // wave-uniform, rare
+      asm volatile("");
+      constexpr int p = decltype(PS)::value;
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[p][e]);
+      const float mt = half_max(mx) * c;
+      const bool grow = mt > m + kLazyRescale;
+      if (__any(grow)) {
+        const float a_ = grow ? fast_exp2(m - mt) : 1.f;   // 0 when there was no reference
+        m = grow ? mt : m;
+        l *= a_;
+        alpha *= a_;
+        rescale = true;
+      }
+      probs(PS, m == -__builtin_inff() ? 0.f : m);
+    }
+    l += lsum;
+  };
+  // keys of step g (in s[P]) outside the row's visible interval -> -inf
+  // (steps that cut the block's visible region only)
+  auto mask = [&](auto P, int g) __attribute__((always_inline)) {
+    constexpr int p = decltype(P)::value;
+    const int key0 = key0_of(g >> 1) + (g & 1) * 32;
+    if (key0 < blk_lo || key0 + 31 > blk_hi) {   // wave-uniform
+      asm volatile("");
+      const int lo = row_lo - key0, hi = row_hi - key0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int off = (e >> 2) * 8 + (e & 3);
+        s[p][e] = (off < lo || off > hi) ? -__builtin_inff() : s[p][e];
+      }
+    }
+  };
+  auto apply_rescale = [&]() __attribute__((always_inline)) {
+    if (rescale) {   // wave-uniform
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+      alpha = 1.f;
+      rescale = false;
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I8 = std::integral_constant<int, 8>;
+  using T = std::true_type;
+  using F = std::false_type;
+
+  // step g: P.V of step g-2 (when PV), Q.K of step g (when QK), softmax of
+  // step g-1 (when SM); G is g's parity.  Even steps start a tile: they issue
+  // the loads of the next tile's keys and this tile's values; odd steps that
+  // computed Q.K end it with the barrier that publishes those loads.
+  auto step = [&](auto PV, auto QK, auto SM, auto G, int g) __attribute__((always_inline)) {
+    constexpr bool pv = decltype(PV)::value, qk = decltype(QK)::value, sm = decltype(SM)::value;
+    constexpr int gp = decltype(G)::value;
+    using PS = std::integral_constant<int, gp ^ 1>;   // parity of step g-1
+    using NP = std::integral_constant<int, pv ? 8 : 0>;
+    using NQ = std::integral_constant<int, qk ? 8 : 0>;
+    if constexpr (qk && gp == 0) {
+      const int n = g >> 1;
+      dma(n + 1 < ntiles ? n + 1 : -1, n);
+    }
+    if constexpr (sm) mask(PS{}, g - 1);
+    if constexpr (pv) apply_rescale();
+    body(NP{}, NQ{}, std::integral_constant<bool, sm>{}, PS{}, g - 2, g);
+    if constexpr (sm) finish(PS{});
+    if constexpr (qk && gp == 1) {
+      wait_loads();
+      __syncthreads();
+    }
+  };
+
+  for (int w = w_first; w < w_end; w += w_step) {
+    const int sub = w % wg_per_qb;
+    const int rest = w / wg_per_qb;
+    const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
+    const int bu = rest / nqb;
+    const int b = bu / U, u = bu % U;
+    const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
+    const int t0 = i * a.block;
+    const int t1 = min(a.S, t0 + a.block) - 1;
+    kg = static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D;
+    vg = static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D;
+
+    // this lane's query row; rows past the unit or the sequence compute on
+    // zeros and are not stored
+    {
+      const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+          static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(u) * SH) * a.S * D,
+          uint32_t(SH) * a.S * D * 2);
+      const int r = sub * ROWS + wave * 32 + col;
+      const int hh = r / a.block;
+      const int row_t = t0 + r % a.block;
+      const bool row_ok = hh < SH && row_t < a.S;
+      row_range(a, row_t, row_lo, row_hi);
+      row_lo -= half * 4;
+      row_hi -= half * 4;
+      const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + half * 8) * 2) : 0x80000000u;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, ks * 32, 0));
+      int dummy;
+      row_range(a, t1, blk_lo, dummy);
+      row_range(a, t0, dummy, blk_hi);
+    }
+    if (a.mode == MODE_INDEX) {
+      const size_t lrow = size_t(bu) * nqb + i;
+      const int32_t* lst = a.idx + lrow * a.idx_width;
+      const int tpb = a.block / KT;
+      ntiles = max(0, min(a.count[lrow], a.idx_width)) * tpb;
+      key0_w0 = lane < ntiles ? lst[lane / tpb] * a.block + (lane % tpb) * KT : 0;
+      key0_w1 = lane + 64 < ntiles ? lst[(lane + 64) / tpb] * a.block + ((lane + 64) % tpb) * KT : 0;
+    } else {
+      TileSpec ts;
+      ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
+      key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
+      key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
+    }
+    m = -__builtin_inff();
+    l = 0.f;
+    alpha = 1.f;
+    rescale = false;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = floatx16{};
+
+    __syncthreads();   // the previous item's output staging is read out
+    if (ntiles > 0) dma(0, -1);
+    wait_loads();
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the query rows too
+    __syncthreads();
+
+    if (ntiles > 0) {
+      step(F{}, T{}, F{}, I0{}, 0);
+      step(F{}, T{}, T{}, I1{}, 1);
+      for (int n = 1; n < ntiles; ++n) {
+        step(T{}, T{}, T{}, I0{}, 2 * n);
+        step(T{}, T{}, T{}, I1{}, 2 * n + 1);
+      }
+      step(T{}, F{}, T{}, I0{}, 2 * ntiles);
+      step(T{}, F{}, F{}, I1{}, 2 * ntiles + 1);
+    }
+    __syncthreads();   // every wave is done with the tile buffers
+
+    // epilogue: the wave's 32 rows through LDS, then whole rows out
+    uint8_t* stg = smem + wave * (32 * D * 2);
+    {
+      const float lt = half_sum(l);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float mu = m == -__builtin_inff() ? 0.f : m;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+          pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
+        }
+      if (half == 0) lstage[wave][col] = lt > 0.f ? (mu + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    {
+      // the wave's 32 rows are consecutive positions of one head (blocks are
+      // a multiple of 32 rows)
+      const int rw = sub * ROWS + wave * 32;
+      const int hr = rw / a.block;
+      const int tr0 = t0 + rw % a.block;
+      if (hr < SH) {
+        uint16_t* wb = static_cast<uint16_t*>(a.out) + ((size_t(b) * a.Hq + u * SH + hr) * a.S + tr0) * D;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int R = 4 * j + lq;
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(stg + R * 256 + ((lc ^ (R & 15)) << 4));
+          if (tr0 + R < a.S) __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(wb + R * D + lc * 8));
+        }
+        if (a.lse && lane < 32 && tr0 + lane < a.S)
+          a.lse[(size_t(b) * a.Hq + u * SH + hr) * a.S + tr0 + lane] = lstage[wave][lane];
+      }
+    }
+  }
+}
+
 // ----------------------------------------------------------------- float32
 template <int D>
 __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
@@ -1105,6 +1499,13 @@ bool uses_d128_union(const AttnArgs& a) {
          heads_per_wg * a.idx_width <= d128::kMaxTiles && (a.S + 63) / 64 <= 256 * 32;
 }
 
+// the software-pipelined kernel: 64-token blocks (key tiles of whole blocks,
+// each wave's 32 rows inside one head), whole workgroups of rows
+bool uses_pipe(const AttnArgs& a) {
+  return a.dtype == 1 && a.D == 128 && a.block % 64 == 0 && a.sel_heads * a.block >= 256 &&
+         a.key_bias == nullptr && a.gate_z == nullptr && attn_max_tiles(a, 64) <= w2::kMaxTiles;
+}
+
 bool uses_d128(const AttnArgs& a) {
   const bool kt32 = (a.mode == MODE_INDEX && a.block % 64 != 0);
   return a.dtype == 1 && a.D == 128 && !kt32 && a.block % 32 == 0 && a.sel_heads * a.block >= 256 &&
@@ -1150,6 +1551,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                   : (nw == 2 ? run_bf16<128, 64, 1, 2>(a, s) : run_bf16<128, 64, 1, 4>(a, s));
     return kt32 ? (nw == 2 ? run_bf16<64, 32, 1, 2>(a, s) : run_bf16<64, 32, 1, 4>(a, s))
                 : (nw == 2 ? run_bf16<64, 64, 1, 2>(a, s) : run_bf16<64, 64, 1, 4>(a, s));
+  }
+  if (uses_pipe(a)) {
+    constexpr int ROWS = w2::ROWS;
+    const int wg_per_qb = (a.sel_heads * a.block + ROWS - 1) / ROWS;
+    const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
+    const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
+    const int grid = a.mode == MODE_CMP ? total : kNumXcd * min(per_xcd, kAttnSlotsPerXcd);
+    k_attn_bf16_d128_pipe<<<grid, w2::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    return hipGetLastError();
   }
   if (uses_d128(a)) {
     constexpr int ROWS = d128::NW * 32;
