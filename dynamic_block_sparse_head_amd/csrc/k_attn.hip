@@ -1048,6 +1048,12 @@ __device__ __forceinline__ void lds_load16(const void* src, void* dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
+// the same from a wave-uniform base plus a per-lane 32-bit byte offset: no
+// vector address arithmetic
+__device__ __forceinline__ void lds_load16_base(const void* base, uint32_t off, void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0) : "memory", "m0");
+}
 
 __global__ __launch_bounds__(w2::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
@@ -1080,6 +1086,11 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   // 16 (j/4) + 4 q + j%4, q = 0..3); lane l carries row l/16 of a chunk,
   // bytes 16 (l%16) .. 16 (l%16) + 15 of its key
   const int lq = lane >> 4, lc = lane & 15;
+  // byte offsets of this lane's 16 bytes within a whole tile, per chunk
+  const uint32_t k_off0 = uint32_t((16 * lq + 2 * wave) * D * 2 + lc * 16);
+  const uint32_t k_off1 = k_off0 + D * 2;
+  const uint32_t v_off0 = uint32_t((16 * ((2 * wave) >> 2) + 4 * lq + ((2 * wave) & 3)) * D * 2 + lc * 16);
+  const uint32_t v_off1 = v_off0 + D * 2;   // chunk 2w+1: the next key of the same quad
 
   // per item
   int ntiles = 0, key0_w0 = 0, key0_w1 = 0;
@@ -1087,7 +1098,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   bf16x8 qf[D / 16];
   floatx16 o[D / 32];
   floatx16 s[2];       // S^T of a 32-key step, by step parity
-  bf16x8 pb[2][2];     // its probabilities as the P.V operand, by step parity
+  u32x4 pb[2][2];      // its probabilities (bf16 pairs) as the P.V operand, by step parity
   float m = 0.f, l = 0.f, lsum = 0.f, alpha = 1.f;
   bool rescale = false;
   const uint16_t* kg = nullptr;
@@ -1104,30 +1115,60 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   // none); rows outside the keys read the nearest key (keys past the end are
   // masked for every row, and a list entry outside the sequence cannot send
   // a load outside the buffer)
-  auto dma = [&](int nk, int nv) __attribute__((always_inline)) {
-    if (nk >= 0) {
+  // One tile's loads for this wave: K chunks 2w, 2w+1 of tile nk and V
+  // chunks 2w, 2w+1 of tile nv (nk or nv < 0: none), each from a
+  // wave-uniform base plus a per-lane byte offset.  A tile that starts before
+  // the sequence or reaches past its end reads clamped rows instead (through
+  // offsets from the group's first row): keys past the end are masked for
+  // every row, and a list entry outside the sequence cannot send a load
+  // outside the buffer.
+  struct TileLoads {
+    const uint16_t* kb;
+    const uint16_t* vb;
+    uint32_t ko0, ko1, vo0, vo1;
+    uint8_t* kd;
+    uint8_t* vd;
+    bool k, v;
+  };
+  auto plan = [&](int nk, int nv) __attribute__((always_inline)) -> TileLoads {
+    TileLoads r;
+    r.k = nk >= 0;
+    r.v = nv >= 0;
+    r.kd = kbuf(nk) + (2 * wave) * KCH;
+    r.vd = vbuf(nv) + (2 * wave) * VCH;
+    r.kb = kg;
+    r.vb = vg;
+    r.ko0 = k_off0;
+    r.ko1 = k_off1;
+    r.vo0 = v_off0;
+    r.vo1 = v_off1;
+    if (r.k) {
       const int key0 = key0_of(nk);
-      const bool clip = key0 < 0 || key0 + KT > a.Skv;   // uniform
-      uint8_t* kd = kbuf(nk);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * wave + jj;
-        int key = key0 + 16 * lq + j;
-        if (clip) key = min(max(key, 0), a.Skv - 1);
-        lds_load16(kg + size_t(key) * D + lc * 8, kd + j * KCH);
+      if (key0 >= 0 && key0 + KT <= a.Skv) {   // uniform: the whole tile inside
+        r.kb = kg + size_t(key0) * D;
+      } else {
+        r.ko0 = uint32_t(min(max(key0 + 16 * lq + 2 * wave, 0), a.Skv - 1) * D * 2 + lc * 16);
+        r.ko1 = uint32_t(min(max(key0 + 16 * lq + 2 * wave + 1, 0), a.Skv - 1) * D * 2 + lc * 16);
       }
     }
-    if (nv >= 0) {
+    if (r.v) {
       const int key0 = key0_of(nv);
-      const bool clip = key0 < 0 || key0 + KT > a.Skv;
-      uint8_t* vd = vbuf(nv);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * wave + jj;
-        int key = key0 + 16 * (j >> 2) + 4 * lq + (j & 3);
-        if (clip) key = min(max(key, 0), a.Skv - 1);
-        lds_load16(vg + size_t(key) * D + lc * 8, vd + j * VCH);
+      if (key0 >= 0 && key0 + KT <= a.Skv) {
+        r.vb = vg + size_t(key0) * D;
+      } else {
+        const int k0 = key0 + 16 * ((2 * wave) >> 2) + 4 * lq + ((2 * wave) & 3);
+        r.vo0 = uint32_t(min(max(k0, 0), a.Skv - 1) * D * 2 + lc * 16);
+        r.vo1 = uint32_t(min(max(k0 + 1, 0), a.Skv - 1) * D * 2 + lc * 16);
       }
+    }
+    return r;
+  };
+  // load q (0..3: K chunk 2w, 2w+1, V chunk 2w, 2w+1) of a planned tile
+  auto issue = [&](const TileLoads& r, int q) __attribute__((always_inline)) {
+    if (q < 2) {
+      if (r.k) lds_load16_base(r.kb, q ? r.ko1 : r.ko0, r.kd + q * KCH);
+    } else {
+      if (r.v) lds_load16_base(r.vb, q == 3 ? r.vo1 : r.vo0, r.vd + (q - 2) * VCH);
     }
   };
   auto wait_loads = [&]() __attribute__((always_inline)) {
@@ -1139,13 +1180,15 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   auto probs = [&](auto P, float mu) __attribute__((always_inline)) {
     constexpr int p = decltype(P)::value;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float pe[8];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = fast_exp2(fmaf(s[p][kk * 8 + e], c, -mu));
         acc[e & 3] += x;
-        pb[p][kk][e] = static_cast<__bf16>(x);
+        pe[e] = x;
+        if (e & 1) pb[p][kk][e >> 1] = pack_bf16x2(pe[e - 1], x);
       }
     lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
@@ -1155,9 +1198,11 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   // the matrix core, each product's operand read from LDS two products
   // ahead, and after each product one sixteenth of the common-path softmax
   // of the step in s[PS] against the current reference (when SM): score e's
-  // probability and its contribution to the row sum, and every second score
-  // the bf16 pair.  The scheduling barriers keep this order.
-  auto body = [&](auto NPV, auto NQK, auto SM, auto PS, int gpv, int gqk) __attribute__((always_inline)) {
+  // probability, score e-1's contribution to the row sum and, every second
+  // score, the bf16 pair of scores e-2 and e-1 (one score behind, so that no
+  // instruction waits for the exponential just issued).  The scheduling
+  // barriers keep this order.
+  auto body = [&](auto NPV, auto NQK, auto SM, auto PS, int gpv, int gqk, auto&& after) __attribute__((always_inline)) {
     constexpr int npv = decltype(NPV)::value, nqk = decltype(NQK)::value;
     constexpr bool sm = decltype(SM)::value;
     constexpr int ps = decltype(PS)::value;   // parity of the softmax step
@@ -1182,35 +1227,46 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     };
     const float nmu = -m;
     float pe[16];
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float acc[4];
     bf16x8 op[3];
     if constexpr (N > 0) op[0] = read_op(std::integral_constant<int, 0>{});
     if constexpr (N > 1) op[1] = read_op(std::integral_constant<int, 1>{});
     __builtin_amdgcn_sched_barrier(0);
+    // score j into the row sum; after an odd j, the bf16 pair (j-1, j)
+    auto sum_pair = [&](auto J) __attribute__((always_inline)) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < 4) acc[j] = pe[j];
+      else acc[j % 4] += pe[j];
+      if constexpr (j % 2 == 1) {
+        uint32_t w = pack_bf16x2(pe[j - 1], pe[j]);
+        asm volatile("" : "+v"(w));   // converted here, in the products' shadow
+        pb[ps][j / 8][(j % 8) / 2] = w;
+      }
+    };
     auto one = [&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       if constexpr (i + 2 < N) op[(i + 2) % 3] = read_op(std::integral_constant<int, i + 2>{});
       if constexpr (i < npv) {
         constexpr int kk = i / 4, dt = i % 4;
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], pb[pp][kk], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], __builtin_bit_cast(bf16x8, pb[pp][kk]), o[dt], 0, 0, 0);
       } else if constexpr (i < N) {
         constexpr int ks = i - npv;
         s[pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qf[ks], ks == 0 ? floatx16{} : s[pp], 0, 0, 0);
       }
+      after(I);
       if constexpr (sm && i < 16) {
         pe[i] = fast_exp2(fmaf(s[ps][i], c, nmu));
-        acc[i % 4] += pe[i];
-        if constexpr (i % 2 == 1) {
-          pb[ps][i / 8][(i % 8) - 1] = static_cast<__bf16>(pe[i - 1]);
-          pb[ps][i / 8][i % 8] = static_cast<__bf16>(pe[i]);
-        }
+        if constexpr (i >= 1) sum_pair(std::integral_constant<int, i - 1>{});
       }
       __builtin_amdgcn_sched_barrier(0);
     };
     [&]<int... Is>(std::integer_sequence<int, Is...>) __attribute__((always_inline)) {
       (one(std::integral_constant<int, Is>{}), ...);
     }(std::make_integer_sequence<int, NI>{});
-    if constexpr (sm) lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if constexpr (sm) {
+      sum_pair(std::integral_constant<int, 15>{});
+      lsum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
   };
   // after the common-path softmax of the step in s[PS]: the slow path where
   // needed, then the row sum
@@ -1276,13 +1332,21 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     using PS = std::integral_constant<int, gp ^ 1>;   // parity of step g-1
     using NP = std::integral_constant<int, pv ? 8 : 0>;
     using NQ = std::integral_constant<int, qk ? 8 : 0>;
+    // even steps start the loads of the next tile's keys and this tile's
+    // values (issued together: spreading them over the products measured
+    // slower)
     if constexpr (qk && gp == 0) {
       const int n = g >> 1;
-      dma(n + 1 < ntiles ? n + 1 : -1, n);
+      const TileLoads tl = plan(n + 1 < ntiles ? n + 1 : -1, n);
+      issue(tl, 0);
+      issue(tl, 1);
+      issue(tl, 2);
+      issue(tl, 3);
     }
+    auto after = [&](auto) __attribute__((always_inline)) {};
     if constexpr (sm) mask(PS{}, g - 1);
     if constexpr (pv) apply_rescale();
-    body(NP{}, NQ{}, std::integral_constant<bool, sm>{}, PS{}, g - 2, g);
+    body(NP{}, NQ{}, std::integral_constant<bool, sm>{}, PS{}, g - 2, g, after);
     if constexpr (sm) finish(PS{});
     if constexpr (qk && gp == 1) {
       wait_loads();
@@ -1344,7 +1408,11 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = floatx16{};
 
     __syncthreads();   // the previous item's output staging is read out
-    if (ntiles > 0) dma(0, -1);
+    if (ntiles > 0) {
+      const TileLoads t0l = plan(0, -1);
+      issue(t0l, 0);
+      issue(t0l, 1);
+    }
     wait_loads();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the query rows too
     __syncthreads();
