@@ -1039,20 +1039,20 @@ constexpr int kMaxTiles = 128;
 constexpr float kSumLimit = 256.0f;
 }  // namespace w2
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at dst + 16 l (dst uniform across the wave).  Issued from inline assembly so
-// the compiler does not wait for these loads before unrelated LDS reads; the
-// kernel waits for them itself (vmcnt) before the barrier that publishes a
-// tile.  The instruction writes no register.
-__device__ __forceinline__ void lds_load16(const void* src, void* dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-}
-// the same from a wave-uniform base plus a per-lane 32-bit byte offset: no
-// vector address arithmetic
+// 16 bytes per lane from global memory straight into LDS: from a wave-uniform
+// base plus a per-lane 32-bit byte offset (no vector address arithmetic), and
+// lane l's bytes land at dst + 16 l (dst uniform across the wave).  Issued
+// from inline assembly so the compiler does not wait for these loads before
+// unrelated LDS reads; the kernel waits for them itself (vmcnt) before the
+// barrier that publishes a tile.  The instruction writes no register.
 __device__ __forceinline__ void lds_load16_base(const void* base, uint32_t off, void* dst) {
+  // (the builtin returns a signed int: widen each half as unsigned)
+  const uint64_t b = uint64_t(uintptr_t(base));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)));
+  const uint64_t sb = uint64_t(hi) << 32 | uint64_t(lo);
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0) : "memory", "m0");
 }
 
 __global__ __launch_bounds__(w2::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1111,10 +1111,6 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   };
   auto kbuf = [&](int n) __attribute__((always_inline)) -> uint8_t* { return kbase + (n & 1) * KBYTES; };
   auto vbuf = [&](int n) __attribute__((always_inline)) -> uint8_t* { return vbase + (n & 1) * VBYTES; };
-  // keys of tile nk and values of tile nv into their buffers (nk or nv < 0:
-  // none); rows outside the keys read the nearest key (keys past the end are
-  // masked for every row, and a list entry outside the sequence cannot send
-  // a load outside the buffer)
   // One tile's loads for this wave: K chunks 2w, 2w+1 of tile nk and V
   // chunks 2w, 2w+1 of tile nv (nk or nv < 0: none), each from a
   // wave-uniform base plus a per-lane byte offset.  A tile that starts before
@@ -1318,7 +1314,6 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I8 = std::integral_constant<int, 8>;
   using T = std::true_type;
   using F = std::false_type;
 
