@@ -729,7 +729,7 @@ int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void*
                     "dsa_nsa_combine");
 }
 
-size_t dsa_read_stream_sink_words(void) { return 2048; }
+size_t dsa_read_stream_sink_words(void) { return 512; }   // two workgroups per CU
 
 int dsa_read_stream(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
                     void* stream) {

@@ -396,7 +396,8 @@ int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* 
 /*
  * Measurement helper, not a step of the method: reads src [bytes] (device,
  * 16-byte aligned, bytes a positive multiple of 16) once with 16-byte
- * loads, eight in flight per lane, and writes sink[w] = XOR of the 32-bit
+ * streaming loads, each workgroup taking whole 16 KiB runs (four loads in
+ * flight per lane), and writes sink[w] = XOR of the 32-bit
  * words workgroup w read, for w < dsa_read_stream_sink_words() (the other
  * sink words are untouched).  The XOR of all sink words is the XOR of every
  * word of src.  Its rate is the achievable HBM read bandwidth that the

@@ -95,7 +95,7 @@ def test_scores_and_decode_validation():
     assert lib.dsa_block_scores(5, 1, FAKE, FAKE, None, 1, 32, 8, 16384, 128, 64, FAKE, need,
                                 FAKE, None) == L.DSA_E_ARG       # unknown kind
     ws = lib.dsa_sparse_attn_decode_workspace_size(16, 32, 8, 102, 64, 128)
-    assert ws == 16 * 32 * 12 * 130 * 4      # 12 chunks of 8-9 pages fill three rounds of 512
+    assert ws == 16 * 32 * 6 * 130 * 4       # 6 chunks of 17 pages: one round of 768 workgroups
     dec = lib.dsa_sparse_attn_decode
     args = [1, FAKE, FAKE, FAKE, 16, 32, 8, 131072, 128, FAKE, FAKE, 102, 64, 0.1, FAKE, ws, FAKE,
             None]
