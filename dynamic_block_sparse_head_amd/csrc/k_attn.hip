@@ -1046,8 +1046,8 @@ constexpr float kSumLimit = 256.0f;
 // unrelated LDS reads; the kernel waits for them itself (vmcnt) before the
 // barrier that publishes a tile.  The instruction writes no register.
 __device__ __forceinline__ void lds_load16_base(const void* base, uint32_t off, void* dst) {
-  // (the builtin returns a signed int: widen each half as unsigned)
   const uint64_t b = uint64_t(uintptr_t(base));
+  // (the builtin returns a signed int: widen each half as unsigned)
   const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)));
   const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)));
   const uint64_t sb = uint64_t(hi) << 32 | uint64_t(lo);
@@ -1058,11 +1058,12 @@ __device__ __forceinline__ void lds_load16_base(const void* base, uint32_t off, 
 __global__ __launch_bounds__(w2::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
   using namespace w2;
-  // K and V double-buffered; after an item's last step the same bytes stage
-  // its output rows (32 x 256 B per wave)
+  // K and V double-buffered; each wave stages its output rows (32 x 256 B)
+  // in a region of its own, so the next item's first tile can load while
+  // this item's output is still being written out
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KBYTES + 2 * VBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[NW][32 * D * 2];
   __shared__ float lstage[NW][32];
-  static_assert(2 * KBYTES + 2 * VBYTES >= NW * 32 * D * 2, "output staging fits the tile buffers");
   uint8_t* const kbase = smem;
   uint8_t* const vbase = smem + 2 * KBYTES;
 
@@ -1349,14 +1350,40 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     }
   };
 
-  for (int w = w_first; w < w_end; w += w_step) {
-    const int sub = w % wg_per_qb;
+  // item coordinates
+  int sub = 0, b = 0, u = 0, t0 = 0;
+  auto item_lane = [&]() __attribute__((always_inline)) -> int {
+    int x = lane;
+    asm volatile("" : "+v"(x));   // keeps list loads on the vector path
+    return x;
+  };
+  // index mode: the next item's count and list entries lane, lane + 64,
+  // requested while the running item computes
+  int nx_cnt = 0, nx_e0 = 0, nx_e1 = 0;
+  auto fetch_list = [&](int w) __attribute__((always_inline)) {
+    if (a.mode == MODE_INDEX) {
+      const int rest = w / wg_per_qb;
+      const size_t lrow = size_t(rest / nqb) * nqb + (nqb - 1 - rest % nqb);
+      const int32_t* lst = a.idx + lrow * a.idx_width;
+      const int ln = item_lane();
+      nx_cnt = a.count[lrow + (ln & 0x40000000)];   // (ln < 2^30: the entry itself)
+      nx_e0 = ln < a.idx_width ? lst[ln] : 0;
+      nx_e1 = ln + 64 < a.idx_width ? lst[ln + 64] : 0;
+    }
+  };
+  // begin(w): coordinates of item w, its query rows (registers), its key
+  // tiles and the loads of its first tile's keys; in index mode the list
+  // comes from fetch_list(w), issued earlier
+  auto begin = [&](int w) __attribute__((always_inline)) {
+    w = __builtin_amdgcn_readfirstlane(w);
+    sub = w % wg_per_qb;
     const int rest = w / wg_per_qb;
     const int i = nqb - 1 - rest % nqb;   // later query blocks see more keys: start them first
     const int bu = rest / nqb;
-    const int b = bu / U, u = bu % U;
-    const int bg = b * a.Hkv + (u * SH) / (a.Hq / a.Hkv);
-    const int t0 = i * a.block;
+    b = bu / U;
+    u = bu % U;
+    const int bg = __builtin_amdgcn_readfirstlane(b * a.Hkv + (u * SH) / (a.Hq / a.Hkv));
+    t0 = i * a.block;
     const int t1 = min(a.S, t0 + a.block) - 1;
     kg = static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D;
     vg = static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D;
@@ -1383,18 +1410,70 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       row_range(a, t0, dummy, blk_hi);
     }
     if (a.mode == MODE_INDEX) {
-      const size_t lrow = size_t(bu) * nqb + i;
-      const int32_t* lst = a.idx + lrow * a.idx_width;
+      // tile n is part n % tpb of listed block n / tpb (entries past the
+      // count are never used)
       const int tpb = a.block / KT;
-      ntiles = max(0, min(a.count[lrow], a.idx_width)) * tpb;
-      key0_w0 = lane < ntiles ? lst[lane / tpb] * a.block + (lane % tpb) * KT : 0;
-      key0_w1 = lane + 64 < ntiles ? lst[(lane + 64) / tpb] * a.block + ((lane + 64) % tpb) * KT : 0;
+      // (every lane loaded the same count)
+      ntiles = max(0, min(__builtin_amdgcn_readfirstlane(nx_cnt), a.idx_width)) * tpb;
+      auto key0 = [&](int n) -> int {
+        const int e = n / tpb;
+        const int v0 = __shfl(nx_e0, e & 63), v1 = __shfl(nx_e1, e & 63);
+        return (e < 64 ? v0 : v1) * a.block + (n % tpb) * KT;
+      };
+      const int ln = item_lane();
+      const int k0 = key0(ln), k1 = key0(ln + 64);
+      key0_w0 = ln < ntiles ? k0 : 0;
+      key0_w1 = ln + 64 < ntiles ? k1 : 0;
     } else {
       TileSpec ts;
       ntiles = make_tiles(a, bu, i, t0, t1, KT, ts);
       key0_w0 = lane < ntiles ? tile_key0(ts, lane) : 0;
       key0_w1 = lane + 64 < ntiles ? tile_key0(ts, lane + 64) : 0;
     }
+    if (ntiles > 0) {
+      const TileLoads t0l = plan(0, -1);
+      issue(t0l, 0);
+      issue(t0l, 1);
+    }
+  };
+
+  // the staged output of the previous item leaves: the wave's 32 rows are
+  // consecutive positions of one head (blocks are a multiple of 32 rows),
+  // whole 256-byte rows per store, streaming (nothing here reads them back)
+  bool pend = false;   // uniform
+  int p_b = 0, p_u = 0, p_sub = 0, p_t0 = 0;
+  auto flush = [&]() __attribute__((always_inline)) {
+    const uint8_t* stg = &ostage[wave][0];
+    const int rw = p_sub * ROWS + wave * 32;
+    const int hr = rw / a.block;
+    const int tr0 = p_t0 + rw % a.block;
+    if (hr < SH) {
+      uint16_t* wb = static_cast<uint16_t*>(a.out) + ((size_t(p_b) * a.Hq + p_u * SH + hr) * a.S + tr0) * D;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int R = 4 * j + lq;
+        const u32x4 v4 = *reinterpret_cast<const u32x4*>(stg + R * 256 + ((lc ^ (R & 15)) << 4));
+        if (tr0 + R < a.S) __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(wb + R * D + lc * 8));
+      }
+      if (a.lse && lane < 32 && tr0 + lane < a.S)
+        a.lse[(size_t(p_b) * a.Hq + p_u * SH + hr) * a.S + tr0 + lane] = lstage[wave][lane];
+    }
+  };
+
+  // Per item: wait for its query rows and first keys, write out the
+  // previous item's staged output, request the next item's list, run the
+  // tile loop; then request the next item's query rows and first keys
+  // before staging this item's output, so that those loads run under the
+  // staging and the stores.
+  if (w_first < w_end) {
+    fetch_list(w_first);
+    begin(w_first);
+  }
+  for (int w = w_first; w < w_end; w += w_step) {
+    // the next item, or this one again after the last (those loads are
+    // never used; running begin() unconditionally keeps one version of its
+    // registers)
+    const int w_next = w + w_step < w_end ? w + w_step : w;   // uniform
     m = -__builtin_inff();
     l = 0.f;
     alpha = 1.f;
@@ -1402,15 +1481,14 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) o[dt] = floatx16{};
 
-    __syncthreads();   // the previous item's output staging is read out
-    if (ntiles > 0) {
-      const TileLoads t0l = plan(0, -1);
-      issue(t0l, 0);
-      issue(t0l, 1);
-    }
     wait_loads();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the query rows too
     __syncthreads();
+    if (pend) {
+      flush();
+      pend = false;
+    }
+    fetch_list(w_next);
 
     if (ntiles > 0) {
       step(F{}, T{}, F{}, I0{}, 0);
@@ -1424,44 +1502,36 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     }
     __syncthreads();   // every wave is done with the tile buffers
 
-    // epilogue: the wave's 32 rows through LDS, then whole rows out
-    uint8_t* stg = smem + wave * (32 * D * 2);
-    {
-      const float lt = half_sum(l);
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const float mu = m == -__builtin_inff() ? 0.f : m;
+    const float lt = half_sum(l);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float mu = m == -__builtin_inff() ? 0.f : m;
+    const float lse_v = lt > 0.f ? (mu + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
+    p_b = b;
+    p_u = u;
+    p_sub = sub;
+    p_t0 = t0;
+    begin(w_next);
+
+    // the wave's 32 rows into its staging region, 16-byte chunks
+    // XOR-swizzled by row
+    uint8_t* stg = &ostage[wave][0];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
-          pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
-        }
-      if (half == 0) lstage[wave][col] = lt > 0.f ? (mu + __builtin_log2f(lt)) * kLn2 : -__builtin_inff();
-    }
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+        pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
+      }
+    if (half == 0) lstage[wave][col] = lse_v;
+    pend = true;
+  }
+  if (pend) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    {
-      // the wave's 32 rows are consecutive positions of one head (blocks are
-      // a multiple of 32 rows)
-      const int rw = sub * ROWS + wave * 32;
-      const int hr = rw / a.block;
-      const int tr0 = t0 + rw % a.block;
-      if (hr < SH) {
-        uint16_t* wb = static_cast<uint16_t*>(a.out) + ((size_t(b) * a.Hq + u * SH + hr) * a.S + tr0) * D;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int R = 4 * j + lq;
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(stg + R * 256 + ((lc ^ (R & 15)) << 4));
-          if (tr0 + R < a.S) __builtin_nontemporal_store(v4, reinterpret_cast<u32x4*>(wb + R * D + lc * 8));
-        }
-        if (a.lse && lane < 32 && tr0 + lane < a.S)
-          a.lse[(size_t(b) * a.Hq + u * SH + hr) * a.S + tr0 + lane] = lstage[wave][lane];
-      }
-    }
+    flush();
   }
 }
 
