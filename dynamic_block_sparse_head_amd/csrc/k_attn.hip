@@ -1515,15 +1515,57 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     // the wave's 32 rows into its staging region, 16-byte chunks
     // XOR-swizzled by row
     uint8_t* stg = &ostage[wave][0];
+    if (a.gate_z == nullptr) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
-        pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
+        for (int rr = 0; rr < 4; ++rr) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+          pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
+        }
+    } else {
+      // gated combine with the other two branches' outputs: sigmoid(z0) o1 +
+      // sigmoid(z1) o2 + sigmoid(z2) (this branch, float32), rounded once.
+      // The lane's pieces of both rows are all loaded before any is used.
+      const int r = p_sub * ROWS + wave * 32 + col;
+      const int hh = r / a.block;
+      const int row_t = p_t0 + r % a.block;
+      const bool ok = hh < SH && row_t < a.S;
+      const int h = p_u * SH + (ok ? hh : 0);
+      const size_t orow = ((size_t(p_b) * a.Hq + h) * a.S + (ok ? row_t : 0)) * D;
+      float g1 = 0.f, g2 = 0.f, g3 = 0.f;
+      u32x2 w1[D / 32][4], w2[D / 32][4];
+      const uint16_t* p1 = static_cast<const uint16_t*>(a.gate_o1) + orow;
+      const uint16_t* p2 = static_cast<const uint16_t*>(a.gate_o2) + orow;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          w1[dt][rr] = ok ? *reinterpret_cast<const u32x2*>(p1 + dt * 32 + rr * 8 + half * 4) : u32x2{0u, 0u};
+          w2[dt][rr] = ok ? *reinterpret_cast<const u32x2*>(p2 + dt * 32 + rr * 8 + half * 4) : u32x2{0u, 0u};
+        }
+      if (ok) {
+        const float* z = a.gate_z + ((size_t(p_b) * a.S + row_t) * a.Hq + h) * 3;
+        g1 = 1.f / (1.f + __expf(-z[0]));
+        g2 = 1.f / (1.f + __expf(-z[1]));
+        g3 = inv / (1.f + __expf(-z[2]));
       }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          u32x2 pk;
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const float lo = g1 * bf16lo(w1[dt][rr][x]) + g2 * bf16lo(w2[dt][rr][x]) + g3 * o[dt][rr * 4 + 2 * x];
+            const float hi = g1 * bf16hi(w1[dt][rr][x]) + g2 * bf16hi(w2[dt][rr][x]) + g3 * o[dt][rr * 4 + 2 * x + 1];
+            pk[x] = pack_bf16x2(lo, hi);
+          }
+          *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
+        }
+    }
     if (half == 0) lstage[wave][col] = lse_v;
     pend = true;
   }
@@ -1636,7 +1678,8 @@ bool uses_d128_union(const AttnArgs& a) {
 // each wave's 32 rows inside one head), whole workgroups of rows
 bool uses_pipe(const AttnArgs& a) {
   return a.dtype == 1 && a.D == 128 && a.block % 64 == 0 && a.sel_heads * a.block >= 256 &&
-         a.key_bias == nullptr && a.gate_z == nullptr && attn_max_tiles(a, 64) <= w2::kMaxTiles;
+         a.key_bias == nullptr && (a.gate_z == nullptr || a.mode == MODE_WINDOW) &&
+         attn_max_tiles(a, 64) <= w2::kMaxTiles;
 }
 
 bool uses_d128(const AttnArgs& a) {
