@@ -38,12 +38,12 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 METRIC = "sparse-attn prefill tokens/s + effective TFLOP/s; decode HBM GB/s (1 GPU)"
 
 
-ATTN_KERNEL = "k_attn_bf16_d128"
+ATTN_KERNEL = "k_attn_bf16_d128_pipe"
 CSRC = os.path.join(ROOT, "dynamic_block_sparse_head_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-ATTN_TRAFFIC = (os.path.join(PROFILES, "k_attn_bf16_d128_prefill64k_traffic.txt"),
+ATTN_TRAFFIC = (os.path.join(PROFILES, "k_attn_bf16_d128_pipe_prefill64k_traffic.txt"),
                 os.path.join(CSRC, "k_attn.hip"))
-ATTN16K_TRAFFIC = (os.path.join(PROFILES, "k_attn_bf16_d128_prefill16k_traffic.txt"),
+ATTN16K_TRAFFIC = (os.path.join(PROFILES, "k_attn_bf16_d128_pipe_prefill16k_traffic.txt"),
                    os.path.join(CSRC, "k_attn.hip"))
 DECODE_TRAFFIC = (os.path.join(PROFILES, "k_decode_split_decode128k_traffic.txt"),
                   os.path.join(CSRC, "k_decode.hip"))
