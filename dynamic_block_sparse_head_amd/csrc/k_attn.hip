@@ -714,7 +714,7 @@ void k_attn_bf16_d128(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total
       const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
           static_cast<const uint16_t*>(a.q) + (size_t(b) * a.Hq + size_t(u) * SH) * a.S * D,
           uint32_t(SH) * a.S * D * 2);
-      const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + (ln >> 5) * 8) * 2) : 0x80000000u;
+      const uint32_t qoff = row_ok ? uint32_t((hh * a.S + row_t) * D + (ln >> 5) * 8) * 2u : 0x80000000u;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, ks * 32, 0));
@@ -1055,6 +1055,11 @@ __device__ __forceinline__ void lds_load16_base(const void* base, uint32_t off, 
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0) : "memory", "m0");
 }
 
+// BIAS: every key carries an additive logit term (key_bias, per KV head and
+// key; the value-driven mask): a tile's terms, divided by the softmax scale,
+// sit in LDS beside its keys and enter each step's first Q.K product as its
+// accumulator, so the scores come out with the term added.
+template <bool BIAS>
 __global__ __launch_bounds__(w2::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int total) {
   using namespace w2;
@@ -1064,6 +1069,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * KBYTES + 2 * VBYTES];
   __shared__ __attribute__((aligned(16))) uint8_t ostage[NW][32 * D * 2];
   __shared__ float lstage[NW][32];
+  __shared__ __attribute__((aligned(16))) float kbias[2][BIAS ? KT : 4];   // key_bias / scale, by K buffer
   uint8_t* const kbase = smem;
   uint8_t* const vbase = smem + 2 * KBYTES;
 
@@ -1109,6 +1115,26 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     const int lo = __builtin_amdgcn_readlane(key0_w0, n & 63);
     const int hi = __builtin_amdgcn_readlane(key0_w1, n & 63);
     return n < 64 ? lo : hi;
+  };
+  // BIAS: the item's key terms (a descriptor over the group's keys; reads
+  // past the sequence return zeros) and the next tile's four terms per lane
+  // of wave 0, lanes 0..15, on their way to LDS
+  __amdgpu_buffer_rsrc_t brs = make_rsrc(a.q, 0u);
+  u32x4 stb = {0u, 0u, 0u, 0u};
+  const float inv_scale = 1.f / a.scale;
+  auto bias_load = [&](int n) __attribute__((always_inline)) {
+    if constexpr (BIAS)
+      if (wave == 0 && lane < KT / 4)
+        stb = __builtin_amdgcn_raw_buffer_load_b128(brs, uint32_t(lane * 16), uint32_t(key0_of(n)) * 4u, 0);
+  };
+  auto bias_store = [&](int n) __attribute__((always_inline)) {
+    if constexpr (BIAS)
+      if (wave == 0 && lane < KT / 4) {
+        floatx4 bv = __builtin_bit_cast(floatx4, stb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] *= inv_scale;
+        *reinterpret_cast<floatx4*>(&kbias[n & 1][lane * 4]) = bv;
+      }
   };
   auto kbuf = [&](int n) __attribute__((always_inline)) -> uint8_t* { return kbase + (n & 1) * KBYTES; };
   auto vbuf = [&](int n) __attribute__((always_inline)) -> uint8_t* { return vbase + (n & 1) * VBYTES; };
@@ -1226,8 +1252,24 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     float pe[16];
     float acc[4];
     bf16x8 op[3];
+    // BIAS: the step's key terms, the first Q.K product's accumulator (read
+    // with that product's operand); keys of accumulator element e are
+    // 8 (e / 4) + 4 half + e % 4 of the step's 32
+    floatx16 binit = {};
+    auto read_bias = [&]() __attribute__((always_inline)) {
+      if constexpr (BIAS) {
+        const float* kb = &kbias[(gqk >> 1) & 1][(gqk & 1) * 32 + half * 4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const floatx4 b4 = *reinterpret_cast<const floatx4*>(kb + 8 * j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) binit[4 * j + e] = b4[e];
+        }
+      }
+    };
     if constexpr (N > 0) op[0] = read_op(std::integral_constant<int, 0>{});
     if constexpr (N > 1) op[1] = read_op(std::integral_constant<int, 1>{});
+    if constexpr (nqk > 0 && npv < 2) read_bias();
     __builtin_amdgcn_sched_barrier(0);
     // score j into the row sum; after an odd j, the bf16 pair (j-1, j)
     auto sum_pair = [&](auto J) __attribute__((always_inline)) {
@@ -1243,12 +1285,13 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     auto one = [&](auto I) __attribute__((always_inline)) {
       constexpr int i = decltype(I)::value;
       if constexpr (i + 2 < N) op[(i + 2) % 3] = read_op(std::integral_constant<int, i + 2>{});
+      if constexpr (nqk > 0 && npv >= 2 && i + 2 == npv) read_bias();
       if constexpr (i < npv) {
         constexpr int kk = i / 4, dt = i % 4;
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], __builtin_bit_cast(bf16x8, pb[pp][kk]), o[dt], 0, 0, 0);
       } else if constexpr (i < N) {
         constexpr int ks = i - npv;
-        s[pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qf[ks], ks == 0 ? floatx16{} : s[pp], 0, 0, 0);
+        s[pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[i % 3], qf[ks], ks == 0 ? binit : s[pp], 0, 0, 0);
       }
       after(I);
       if constexpr (sm && i < 16) {
@@ -1338,6 +1381,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       issue(tl, 1);
       issue(tl, 2);
       issue(tl, 3);
+      if (n + 1 < ntiles) bias_load(n + 1);
     }
     auto after = [&](auto) __attribute__((always_inline)) {};
     if constexpr (sm) mask(PS{}, g - 1);
@@ -1345,6 +1389,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     body(NP{}, NQ{}, std::integral_constant<bool, sm>{}, PS{}, g - 2, g, after);
     if constexpr (sm) finish(PS{});
     if constexpr (qk && gp == 1) {
+      if (BIAS && (g >> 1) + 1 < ntiles) bias_store((g >> 1) + 1);
       wait_loads();
       __syncthreads();
     }
@@ -1387,6 +1432,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     const int t1 = min(a.S, t0 + a.block) - 1;
     kg = static_cast<const uint16_t*>(a.k) + size_t(bg) * a.Skv * D;
     vg = static_cast<const uint16_t*>(a.v) + size_t(bg) * a.Skv * D;
+    if constexpr (BIAS) brs = make_rsrc(a.key_bias + size_t(bg) * a.Skv, uint32_t(a.Skv) * 4u);
 
     // this lane's query row; rows past the unit or the sequence compute on
     // zeros and are not stored
@@ -1401,7 +1447,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       row_range(a, row_t, row_lo, row_hi);
       row_lo -= half * 4;
       row_hi -= half * 4;
-      const uint32_t qoff = row_ok ? uint32_t(((hh * a.S + row_t) * D + half * 8) * 2) : 0x80000000u;
+      const uint32_t qoff = row_ok ? uint32_t((hh * a.S + row_t) * D + half * 8) * 2u : 0x80000000u;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
         qf[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, ks * 32, 0));
@@ -1434,6 +1480,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       const TileLoads t0l = plan(0, -1);
       issue(t0l, 0);
       issue(t0l, 1);
+      bias_load(0);
     }
   };
 
@@ -1483,6 +1530,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
 
     wait_loads();
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the query rows too
+    if (ntiles > 0) bias_store(0);
     __syncthreads();
     if (pend) {
       flush();
@@ -1678,8 +1726,7 @@ bool uses_d128_union(const AttnArgs& a) {
 // each wave's 32 rows inside one head), whole workgroups of rows
 bool uses_pipe(const AttnArgs& a) {
   return a.dtype == 1 && a.D == 128 && a.block % 64 == 0 && a.sel_heads * a.block >= 256 &&
-         a.key_bias == nullptr && (a.gate_z == nullptr || a.mode == MODE_WINDOW) &&
-         attn_max_tiles(a, 64) <= w2::kMaxTiles;
+         (a.gate_z == nullptr || a.mode == MODE_WINDOW) && attn_max_tiles(a, 64) <= w2::kMaxTiles;
 }
 
 bool uses_d128(const AttnArgs& a) {
@@ -1734,7 +1781,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int total = a.B * (a.Hq / a.sel_heads) * nqb * wg_per_qb;
     const int per_xcd = (total + kNumXcd - 1) / kNumXcd;
     const int grid = a.mode == MODE_CMP ? total : kNumXcd * min(per_xcd, kAttnSlotsPerXcd);
-    k_attn_bf16_d128_pipe<<<grid, w2::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    if (a.key_bias)
+      k_attn_bf16_d128_pipe<true><<<grid, w2::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
+    else
+      k_attn_bf16_d128_pipe<false><<<grid, w2::NT, 0, s>>>(a, wg_per_qb, nqb, per_xcd, total);
     return hipGetLastError();
   }
   if (uses_d128(a)) {
