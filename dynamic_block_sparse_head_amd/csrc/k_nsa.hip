@@ -51,19 +51,35 @@ __global__ __launch_bounds__(256) void k_compress(const uint16_t* __restrict__ k
   *reinterpret_cast<u32x4*>(dst) = o;
 }
 
-constexpr int kNW = 4;      // waves per workgroup
-constexpr int kQT = 2;      // 32-row tiles per wave
-constexpr int kRows = kNW * 32 * kQT;
+// x of lane l % 32 plus x of lane 32 + l % 32, on every lane
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-// grid (B*Hkv*nqb); dynamic LDS: colsum[kNW][n_cmp] floats (one row per wave,
-// so a wave adds its partial column sums without waiting for the others)
-template <int D>
-__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+constexpr int kNW = 4;      // waves per workgroup of the per-token kernel
+
+// Block-score kernel shape: NW waves of QT 32-row tiles each (the query
+// rows a workgroup holds at once: one chunk of its group's rows).
+constexpr int kBsNW = 8;
+constexpr int kBsQT = 1;
+
+// grid (B*Hkv*nqb), NW*64 threads; dynamic LDS: colsum[n_cmp] floats.
+// Every summary tile's per-wave column sums meet in a small exchange buffer;
+// one wave (rotating with the tile) adds them, in wave order, into colsum, so
+// the reduction order is fixed.
+template <int D, int NW, int QT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4 / QT, 4 / QT)))
 void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
+  constexpr int ROWS = NW * 32 * QT;                         // rows per chunk
   constexpr int CSTR = D + 8;
   constexpr int CPR = D / 8;                                  // 16-byte chunks per summary
-  constexpr int CPT = (32 * CPR + kNW * 64 - 1) / (kNW * 64); // chunks per thread per tile
+  constexpr int CPT = (32 * CPR + NW * 64 - 1) / (NW * 64);   // chunks per thread per tile
+  constexpr int NP = QT * D / 16;                             // products per wave per tile
+  constexpr int NE = QT * 16;                                 // scores per lane per tile
+  constexpr int EPS = (NE + NP - 1) / NP;                     // exponentials per product
   __shared__ __attribute__((aligned(16))) uint16_t c_lds[2][32 * CSTR];
+  __shared__ float xsum[2][NW][32];
   extern __shared__ float colsum[];
 
   // later query blocks see more summaries: start them first
@@ -76,8 +92,7 @@ void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
   const int col = lane & 31, half = lane >> 5;
   const float c = a.scale * kLog2e;
 
-  for (int x = threadIdx.x; x < kNW * a.n_cmp; x += kNW * 64) colsum[x] = 0.f;
-  float* my_colsum = colsum + wave * a.n_cmp;
+  for (int x = threadIdx.x; x < a.n_cmp; x += NW * 64) colsum[x] = 0.f;
 
   int c_hi = -1;
   if (t1 >= a.len - 1) c_hi = min(a.n_cmp - 1, (t1 - (a.len - 1)) / a.stride);
@@ -86,12 +101,12 @@ void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
                                                uint32_t(a.n_cmp) * D * 2);
   const uint16_t* qp = static_cast<const uint16_t*>(a.q);
 
-  // summary tile staging: global -> registers one tile ahead -> LDS
+  // summary tile staging: global -> registers two tiles ahead -> LDS
   u32x4 st[CPT];
   auto load = [&](int kt) {
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-      const int e = threadIdx.x + cc * kNW * 64;
+      const int e = threadIdx.x + cc * NW * 64;
       if (e < 32 * CPR)   // past n_cmp the buffer range check returns zeros
         st[cc] = __builtin_amdgcn_raw_buffer_load_b128(crs, uint32_t(((kt * 32 + e / CPR) * D + (e % CPR) * 8) * 2), 0, 0);
     }
@@ -99,24 +114,35 @@ void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
   auto store = [&](int buf) {
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc) {
-      const int e = threadIdx.x + cc * kNW * 64;
+      const int e = threadIdx.x + cc * NW * 64;
       if (e < 32 * CPR) *reinterpret_cast<u32x4*>(&c_lds[buf][(e / CPR) * CSTR + (e % CPR) * 8]) = st[cc];
+    }
+  };
+  // the column sums of tile kt (parked by every wave before the last
+  // barrier) into colsum, by wave kt % NW
+  auto flush = [&](int kt) __attribute__((always_inline)) {
+    const int cs = kt * 32 + col;
+    if (wave == kt % NW && half == 0 && cs < a.n_cmp) {
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) t += xsum[kt & 1][w2][col];
+      colsum[cs] += t;
     }
   };
 
   const int total_rows = G * sb;
-  const int nchunks = (total_rows + kRows - 1) / kRows;
+  const int nchunks = (total_rows + ROWS - 1) / ROWS;
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     // this wave's query rows, their Q operands and base-2 log-sum-exp.  A
     // 32-row tile lies in one head (sel_block is a multiple of 32), so the
     // token of accumulator row (rr/4)*8 + half*4 + rr%4 is tbase + (rr/4)*8
     // + rr%4: the visibility test needs no per-row table
-    bf16x8 qf[kQT][D / 16];
-    float lse2[kQT][16];
-    int tbase[kQT];
+    bf16x8 qf[QT][D / 16];
+    float lse2[QT][16];
+    int tbase[QT];
 #pragma unroll
-    for (int qt = 0; qt < kQT; ++qt) {
-      const int r = chunk * kRows + wave * 32 * kQT + qt * 32 + col;
+    for (int qt = 0; qt < QT; ++qt) {
+      const int r = chunk * ROWS + wave * 32 * QT + qt * 32 + col;
       const int hh = r / sb;
       const int t = t0 + r % sb;
       const bool ok = hh < G && t <= t1;
@@ -128,7 +154,7 @@ void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
         for (int e = 0; e < 8; ++e) qf[qt][ks][e] = ok ? v[e] : static_cast<__bf16>(0.0f);
       }
       // rows of the accumulator tile held by this lane: (rr/4)*8 + half*4 + rr%4
-      const int rbase = chunk * kRows + wave * 32 * kQT + qt * 32;
+      const int rbase = chunk * ROWS + wave * 32 * QT + qt * 32;
       tbase[qt] = t0 + rbase % sb + half * 4;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
@@ -142,57 +168,126 @@ void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
       }
     }
 
+    // Tiles whose summaries all end at or before the block's first token
+    // (every row sees them) form a prefix, tiles [0, nfull); they run as a
+    // software pipeline: while the exponentials of tile kt run, the products
+    // of tile kt + 1 are issued (in an order fixed by scheduling barriers)
+    // and tile kt + 2 is on its way from memory.  The remaining (diagonal)
+    // tiles, one or two per row chunk, run one at a time with the
+    // visibility test as the first product's accumulator (-inf where a row
+    // cannot see the summary, so the exponential of a hidden pair is 0 with
+    // no per-score select).
+    int nfull = 0;
+    if (t0 - a.len + 1 >= 0) {
+      const int m = (t0 - a.len + 1) / a.stride;   // summaries 0..m end at or before t0
+      nfull = m >= 31 ? min(nkt, (m - 31) / 32 + 1) : 0;
+    }
+    float pp[4];
+    auto park = [&](int kt) __attribute__((always_inline)) {
+      // lane holds summary kt*32+col for 16 rows of each row tile
+      const float part = sum_halves((pp[0] + pp[1]) + (pp[2] + pp[3]));
+      if (half == 0) xsum[kt & 1][wave][col] = part;
+    };
+    // exponentials of cur into pp; with NXT, the products of the tile in LDS
+    // buffer buf into nxt (zero accumulator) between them
+    auto step = [&](auto NXT, int buf, floatx16 (&cur)[QT], floatx16 (&nxt)[QT])
+        __attribute__((always_inline)) {
+      constexpr bool kNxt = decltype(NXT)::value;
+      const uint16_t* cl = &c_lds[buf][col * CSTR + half * 8];
+      bf16x8 cb[2];
+      if constexpr (kNxt) cb[0] = *reinterpret_cast<const bf16x8*>(cl);
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        if constexpr (kNxt) {
+          const int ks = j / QT, qt = j % QT;
+          if (qt == 0 && ks + 1 < D / 16) cb[(ks + 1) & 1] = *reinterpret_cast<const bf16x8*>(cl + (ks + 1) * 16);
+          nxt[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], cb[ks & 1], ks == 0 ? floatx16{} : nxt[qt],
+                                                             0, 0, 0);
+        }
+#pragma unroll
+        for (int e = EPS * j; e < EPS * j + EPS; ++e) {
+          if (e < NE) {
+            const int qt = e >> 4, rr = e & 15;
+            const float p = fast_exp2(fmaf(cur[qt][rr], c, -lse2[qt][rr]));
+            pp[rr & 3] = e < 4 ? p : pp[rr & 3] + p;   // four independent chains
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto products = [&](int buf, floatx16 (&acc)[QT], bool zero_init) __attribute__((always_inline)) {
+      const uint16_t* cl = &c_lds[buf][col * CSTR + half * 8];
+      if (zero_init) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) acc[qt] = floatx16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 cb = *reinterpret_cast<const bf16x8*>(cl + ks * 16);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], cb, acc[qt], 0, 0, 0);
+      }
+    };
+    // one pipelined full tile: NXT when tile kt + 1 is full too.  Buffer
+    // kt & 1 held tile kt, whose products every wave issued before the
+    // previous barrier, so tile kt + 2 goes there.
+    auto iter_full = [&](auto NXT, int kt, floatx16 (&cur)[QT], floatx16 (&nxt)[QT])
+        __attribute__((always_inline)) {
+      if (kt + 2 < nkt) load(kt + 2);
+      if (kt > 0) flush(kt - 1);
+      step(NXT, (kt + 1) & 1, cur, nxt);
+      park(kt);
+      if (kt + 2 < nkt) store(kt & 1);
+      __syncthreads();
+    };
+
+    floatx16 sa[QT], sb2[QT];
     if (nkt > 0) {
       load(0);
       store(0);
+      __syncthreads();
+      if (nfull > 0) products(0, sa, true);
+      if (nkt > 1) {
+        load(1);
+        store(1);
+      }
+      __syncthreads();   // tile 1 in LDS; every wave is done with tile 0's buffer
     }
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nkt) load(kt + 1);
-      floatx16 s[kQT];
+    int kt = 0;
+    for (; kt + 2 < nfull; kt += 2) {
+      iter_full(std::true_type{}, kt, sa, sb2);
+      iter_full(std::true_type{}, kt + 1, sb2, sa);
+    }
+    if (kt + 1 < nfull) {
+      iter_full(std::true_type{}, kt, sa, sb2);
+      iter_full(std::false_type{}, kt + 1, sb2, sa);
+    } else if (kt < nfull) {
+      iter_full(std::false_type{}, kt, sa, sb2);
+    }
+    for (kt = nfull; kt < nkt; ++kt) {
+      if (kt + 2 < nkt) load(kt + 2);
+      if (kt > 0) flush(kt - 1);
+      const int cend = (kt * 32 + col) * a.stride + a.len - 1;   // last token of this lane's summary
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 cb = *reinterpret_cast<const bf16x8*>(&c_lds[buf][col * CSTR + ks * 16 + half * 8]);
+      for (int qt = 0; qt < QT; ++qt) {
+        const int lim = tbase[qt] - cend;   // row visible iff its offset >= -lim
 #pragma unroll
-        for (int qt = 0; qt < kQT; ++qt)
-          s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qt][ks], cb, ks == 0 ? floatx16{} : s[qt], 0, 0, 0);
+        for (int rr = 0; rr < 16; ++rr)
+          sa[qt][rr] = ((rr >> 2) * 8 + (rr & 3) + lim >= 0) ? 0.f : -__builtin_inff();
       }
-      // lane holds summary kt*32+col for 16 rows of each row tile
-      const int cs = kt * 32 + col;
-      const int cend = cs * a.stride + a.len - 1;   // its last token
-      float pp[4] = {0.f, 0.f, 0.f, 0.f};   // independent chains
-      if ((kt * 32 + 31) * a.stride + a.len - 1 <= t0) {
-        // every summary of the tile ends before the block's first row: all
-        // rows of the block see all of them (rows outside it add 0)
-#pragma unroll
-        for (int qt = 0; qt < kQT; ++qt)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) pp[rr & 3] += fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
-      } else {
-#pragma unroll
-        for (int qt = 0; qt < kQT; ++qt) {
-          const int lim = tbase[qt] - cend;   // row visible iff its offset >= -lim
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) {
-            const float p = fast_exp2(fmaf(s[qt][rr], c, -lse2[qt][rr]));
-            pp[rr & 3] += ((rr >> 2) * 8 + (rr & 3) + lim >= 0) ? p : 0.f;
-          }
-        }
+      products(kt & 1, sa, false);
+      step(std::false_type{}, 0, sa, sb2);
+      park(kt);
+      if (kt + 2 < nkt) {
+        __syncthreads();   // every wave is done with tile kt's buffer
+        store(kt & 1);
       }
-      float part = (pp[0] + pp[1]) + (pp[2] + pp[3]);
-      part += __shfl_xor(part, 32);
-      if (half == 0 && cs < a.n_cmp) my_colsum[cs] += part;
-      if (kt + 1 < nkt) store(buf ^ 1);
       __syncthreads();
     }
-  }
-  __syncthreads();
-  for (int x = threadIdx.x; x < a.n_cmp; x += kNW * 64) {
-    float t = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < kNW; ++w2) t += colsum[w2 * a.n_cmp + x];
-    colsum[x] = t;   // row 0 now holds the block's column sums
+    // the last tile's sums (every wave parked them before the last barrier;
+    // the next chunk's first park comes after two more barriers)
+    if (nkt > 0) flush(nkt - 1);
   }
   __syncthreads();
 
@@ -200,7 +295,7 @@ void k_cmp_block_scores(CmpScoreArgs a, int nqb) {
   const int nb = (a.S + sb - 1) / sb;
   const float norm = 1.f / (float(t1 - t0 + 1) * float(G));
   float* out = a.scores + (size_t(bg) * nqb + i) * nb;
-  for (int j = threadIdx.x; j < nb; j += kNW * 64) {
+  for (int j = threadIdx.x; j < nb; j += NW * 64) {
     const int j0 = j * sb, j1 = j * sb + sb - 1;
     int c0 = (j0 - a.len + 1 + a.stride - 1);
     c0 = c0 <= 0 ? 0 : c0 / a.stride;
@@ -433,11 +528,11 @@ hipError_t launch_nsa_compress(const void* k, const void* v, int B, int Hkv, int
 
 hipError_t launch_cmp_block_scores(const CmpScoreArgs& a, hipStream_t s) {
   const int nqb = (a.S + a.sel_block - 1) / a.sel_block;
-  const size_t lds = size_t(kNW) * a.n_cmp * sizeof(float);
+  const size_t lds = size_t(a.n_cmp) * sizeof(float);
   if (a.D == 128)
-    k_cmp_block_scores<128><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
+    k_cmp_block_scores<128, kBsNW, kBsQT><<<a.B * a.Hkv * nqb, kBsNW * 64, lds, s>>>(a, nqb);
   else
-    k_cmp_block_scores<64><<<a.B * a.Hkv * nqb, kNW * 64, lds, s>>>(a, nqb);
+    k_cmp_block_scores<64, kBsNW, kBsQT><<<a.B * a.Hkv * nqb, kBsNW * 64, lds, s>>>(a, nqb);
   return hipGetLastError();
 }
 

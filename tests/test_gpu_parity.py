@@ -291,6 +291,19 @@ def test_nsa_pipeline_small():
     print(f"bit-exact index rows: {exact:.3f}")
 
 
+def test_nsa_pipeline_head_dim_64():
+    """Head dimension 64 (the block-score kernel's other instance) with a
+    ragged last block and two KV groups, end to end."""
+    c = replace(configs.NSA_32K, S=1500 + 37, Hq=8, Hkv=2, D=64)
+    x = inputs.nsa_inputs(c, seed=5, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV, fuse_combine=False)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    _sync()
+    exact = _nsa_end_to_end(c, x, plan)
+    print(f"bit-exact index rows: {exact:.3f}")
+
+
 @pytest.mark.parametrize("S,Hq,Hkv,window", [(2048 + 64, 16, 1, 512), (1000, 8, 2, 512),
                                               (777, 4, 1, 100)])
 def test_nsa_window_combine_fused(S, Hq, Hkv, window):
