@@ -173,8 +173,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
         const bool ok = e != ~size_t(0) && tok0 + tg < len;   // the row exists and is written
         const size_t off = ok ? e + tg * D + dc * 8 : 0;
         bt.base[u] = ok ? 1u : 0xffffffffu;
-        bt.k[u] = *reinterpret_cast<const u32x4*>(kpool + off);
-        bt.v[u] = *reinterpret_cast<const u32x4*>(vpool + off);
+        // streaming loads, as below (a buffer descriptor cannot span a pool
+        // of 4 GiB or more, so these are global loads)
+        bt.k[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kpool + off));
+        bt.v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vpool + off));
       } else {
         bt.base[u] = row_base(sl, u);
         // streaming loads (nt): the pages are read once per call; measured
