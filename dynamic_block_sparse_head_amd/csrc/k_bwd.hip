@@ -372,6 +372,16 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
+// As dma16, from a wave-uniform base plus a per-lane 32-bit byte offset
+// (the address lives in scalar registers; one vector register per lane).
+__device__ __forceinline__ void dma16_base(const void* base, uint32_t off, void* dst) {
+  const uint64_t b = uint64_t(uintptr_t(base));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b)));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(b >> 32)));
+  const uint64_t sb = uint64_t(hi) << 32 | uint64_t(lo);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(m0) : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* src, void* dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(uintptr_t(dst)));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
@@ -838,6 +848,246 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int 
     }
 }
 
+// dk, dv, D = 128, blocks of 64: eight waves in pairs.  For key tile kt and
+// row half rh, wave A (waves 0..3) computes S = Q K^T, P and dv^T += dO^T P;
+// wave B (waves 4..7) computes dP = dO V^T, dS = P (dP - D) with A's P
+// (float32, through LDS) and dk^T += Q^T dS.  Each wave holds one
+// accumulator set and one fixed operand (K or V rows), so two waves fit a
+// SIMD and one's softmax and operand reads run beside the other's products
+// (a single wave holding both sets keeps the matrix core about a quarter
+// busy).  Tiles, arithmetic and summation order are those of
+// k_bwd_dkdv_d128, so the results are identical.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
+  using namespace f128;
+  constexpr int BLK = 64, NKT = BLK / 32, NW = 8, NB = 3;
+  __shared__ __attribute__((aligned(1024))) uint8_t kv[2 * BLK * ROWB];   // K rows, then V rows
+  // a tile buffer: Q rows, dO rows, then the row terms (lse, D) of its rows
+  constexpr int QDB = 2 * 64 * ROWB + 2 * 64 * 4 + 512;   // (padded to a multiple of 1 KB)
+  __shared__ __attribute__((aligned(1024))) uint8_t qd[NB][QDB];
+  auto rt_of = [&](int buf) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(&qd[buf][2 * 64 * ROWB]);
+  };
+  // a pair's P: group q4 of lane l's 16 floats at [q4][l] (consecutive lanes
+  // in consecutive 16-byte slots: no bank conflicts)
+  __shared__ __attribute__((aligned(16))) floatx4 xp[NW / 2][4][64];
+  __shared__ int lst[kDkdvList];          // the inverted list (the launcher checks it fits)
+
+  const int w = xcd_work_id(per_xcd);
+  if (w >= total) return;
+  const int j = w % a.nqb, bg = w / a.nqb;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const bool role_b = wave >= NW / 2;     // uniform
+  const int pr = wave % (NW / 2);         // the pair: waves pr and pr + 4 share a SIMD
+  const int kt = pr % NKT, rh = pr / NKT;
+  const int col = lane & 31, half = lane >> 5;
+  const float c = a.scale * kLog2e;
+  const int kb0 = j * BLK;
+
+  floatx16 acc[D / 32];   // dv^T (A) or dk^T (B)
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] = 0.f;
+
+  const int key = kb0 + kt * 32 + col;          // this lane's key
+  const int32_t* inv = a.inv + (size_t(bg) * a.nqb + j) * a.nqb;
+  const int nsteps = a.inv_cnt[size_t(bg) * a.nqb + j] * G;
+
+  // tile n: query block inv[n / G], head n mod G, its 64 rows
+  struct Tile { int t0; size_t row0; };
+  auto tile_of = [&](int i, int n) __attribute__((always_inline)) -> Tile {
+    return Tile{i * BLK, (size_t(b) * a.Hq + g * G + n % G) * a.S};
+  };
+  const uint32_t dma_off = dma_lane_off(wave, lane);
+  auto stage = [&](const Tile& tl, uint8_t* dst) __attribute__((always_inline)) {
+    const int nv = a.S - tl.t0;
+    if (nv >= 64) {   // runs wave and wave + 8 of each array (see dma_rows64_full)
+      const uint8_t* qs = reinterpret_cast<const uint8_t*>(a.q + (tl.row0 + tl.t0) * D);
+      const uint8_t* ds = reinterpret_cast<const uint8_t*>(a.dout + (tl.row0 + tl.t0) * D);
+#pragma unroll
+      for (int jr = 0; jr < 16 / NW; ++jr) {
+        dma16_base(qs + jr * NW * 4 * ROWB, dma_off, dst + (wave + jr * NW) * 1024);
+        dma16_base(ds + jr * NW * 4 * ROWB, dma_off, dst + 64 * ROWB + (wave + jr * NW) * 1024);
+      }
+    } else {
+      dma_rows64(a.q + (tl.row0 + tl.t0) * D, nv, dst, wave, NW, lane);
+      dma_rows64(a.dout + (tl.row0 + tl.t0) * D, nv, dst + 64 * ROWB, wave, NW, lane);
+    }
+  };
+  // row terms of a tile (base-2 lse, then D), streamed by wave 0: one row
+  // per lane, rows past S read row S - 1 (their weights are masked)
+  auto stage_rt = [&](const Tile& tl, float* dst) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const size_t rr = tl.row0 + min(tl.t0 + lane, a.S - 1);
+      dma4(a.lse2 + rr, dst);
+      dma4(a.dt + rr, dst + 64);
+    }
+  };
+
+  const uint32_t lb = row_base(kt * 32 + col, half);       // K / V rows (B operand)
+  const uint32_t la = row_base(rh * 32 + col, half);       // Q / dO rows (A operand)
+  uint32_t lt0, lt8;
+  tr_bases(rh * 32, lane, lt0, lt8);                       // Q^T / dO^T (transposed A operand)
+  bf16x8 kvf[D / 16];   // A: this wave's K rows; B: its V rows
+
+  // One step: A requests its Q operands, B its dO operands, then the first
+  // product (S or dP) and, under it, the second product's transposed
+  // operands; A forms P and parks it; after the pair barrier A adds dO^T P
+  // into dv, B forms dS and adds Q^T dS into dk.
+  auto step = [&](int t0, const uint8_t* cur, const float* rtc) __attribute__((always_inline)) {
+    const uint8_t* rows = cur + (role_b ? 64 * ROWB : 0);
+    const uint8_t* trs = cur + (role_b ? 0 : 64 * ROWB);
+    // the per-lane operand addresses are formed here, each step, rather than
+    // kept live for every buffer across the loop
+    uint32_t la_ = la, lt0_ = lt0, lt8_ = lt8;
+    asm volatile("" : "+v"(la_), "+v"(lt0_), "+v"(lt8_));
+    bf16x8 ra[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) ra[ks] = rd_row(rows, la_, ks);
+    __builtin_amdgcn_sched_barrier(0);   // keep the requests ahead of the products
+    floatx16 x = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks], kvf[ks], x, 0, 0, 0);
+    // the second product's transposed operands (dO^T for A, Q^T for B),
+    // requested under the first
+    bf16x8 tr[2][D / 32];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) tr[ks2][dt] = rd_tr(trs, lt0_, lt8_, ks2, dt);
+    __builtin_amdgcn_sched_barrier(0);   // ... and ahead of the softmax arithmetic
+    bf16x8 op[2];   // the second product's B operand: P (A) or dS (B), bf16
+    if (!role_b) {
+      // every row of this half at or after every key of its tile, all inside
+      // the sequence: no masking
+      const int r_lo = t0 + rh * 32, k_hi = kb0 + kt * 32 + 31;
+      const bool full = k_hi <= r_lo && r_lo + 31 < a.S && k_hi < a.S;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int qr0 = rh * 32 + q4 * 8 + half * 4;
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(rtc + qr0);
+        floatx4 p4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = q4 * 4 + e;
+          float p;
+          if (full) {
+            p = fast_exp2(fmaf(x[rr], c, -l4[e]));
+          } else {
+            const int tt = t0 + qr0 + e;
+            const bool vis = key <= tt && key < a.S && tt < a.S;
+            p = vis ? fast_exp2(fmaf(x[rr], c, -l4[e])) : 0.f;
+          }
+          op[rr >> 3][rr & 7] = static_cast<__bf16>(p);
+          p4[e] = p;
+        }
+        xp[pr][q4][lane] = p4;
+      }
+    }
+    lds_barrier();   // the pair's P is parked
+    if (role_b) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int qr0 = rh * 32 + q4 * 8 + half * 4;
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(rtc + 64 + qr0);
+        const floatx4 p4 = xp[pr][q4][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = q4 * 4 + e;
+          // a hidden pair has P = 0, so its dS is 0 as well
+          op[rr >> 3][rr & 7] = static_cast<__bf16>(p4[e] * (x[rr] - d4[e]));
+        }
+      }
+    }
+    // the second product: dO^T P (A) or Q^T dS (B)
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[ks2][dt], op[ks2], acc[dt], 0, 0, 0);
+  };
+
+  if (nsteps > 0) {
+    const int nv = a.S - kb0;
+    dma_rows64(a.k + (size_t(bg) * a.S + kb0) * D, nv, kv, wave, NW, lane);
+    dma_rows64(a.v + (size_t(bg) * a.S + kb0) * D, nv, kv + BLK * ROWB, wave, NW, lane);
+    // NB buffers: tile n + 2 streams in while tile n is used.  The list sits
+    // in LDS, so finding a tile's rows costs no memory round trip; the row
+    // terms stream like the rows (direct-to-LDS, one float a lane).
+    const int ninv = nsteps / G;
+    for (int e = threadIdx.x; e < ninv; e += NW * 64) lst[e] = inv[e];
+    __syncthreads();
+    auto entry = [&](int n) __attribute__((always_inline)) { return lst[n / G]; };
+    constexpr int kOps = 4;   // direct-to-LDS row loads per wave and tile (16 runs each of Q, dO over 8 waves)
+    {
+      const Tile t = tile_of(entry(0), 0);
+      stage_rt(t, rt_of(0));
+      stage(t, qd[0]);
+    }
+    if (nsteps > 1) {
+      const Tile t = tile_of(entry(1), 1);
+      stage_rt(t, rt_of(1));
+      stage(t, qd[1]);
+    }
+    wait_vm<0>();
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kvf[ks] = rd_row(kv + (role_b ? BLK * ROWB : 0), lb, ks);
+    // one loop body (the buffer of tile n is n mod NB, kept as a rotating
+    // index), so the accumulators stay in one set of registers
+    int cb = 0;
+    for (int n = 0; n < nsteps; ++n) {
+      const int pbuf = cb == 0 ? NB - 1 : cb - 1;   // (n + NB - 1) mod NB
+      const bool pf = n + NB - 1 < nsteps;
+      if (pf) {
+        const Tile tp = tile_of(entry(n + NB - 1), n + NB - 1);
+        stage_rt(tp, rt_of(pbuf));
+        stage(tp, qd[pbuf]);
+      }
+      step(entry(n) * BLK, qd[cb], rt_of(cb));
+      // tile n + 1 has landed (each wave waits for its own loads); the row
+      // loads of tile n + 2, issued last, may still be in flight
+      if (pf) wait_vm<kOps>();
+      else wait_vm<0>();
+      lds_barrier();
+      cb = cb == NB - 1 ? 0 : cb + 1;
+    }
+  }
+
+  // the second row half's waves hand their sums to the first half's (the
+  // tile buffers are free: the last step ended with a barrier)
+  float* xs = reinterpret_cast<float*>(qd[role_b ? 1 : 0]) + kt * 64 * 64 + lane;
+  if (rh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xs[(dt * 16 + e) * 64] = acc[dt][e];
+  }
+  __syncthreads();
+  if (rh == 1) return;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[dt][e] += xs[(dt * 16 + e) * 64];
+
+  if (key >= a.S) return;
+  const float sc = role_b ? a.scale : 1.f;
+  uint16_t* dst = (role_b ? a.dk : a.dv) + (size_t(bg) * a.S + key) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[dt][r4 * 4 + 0] * sc, acc[dt][r4 * 4 + 1] * sc);
+      pk[1] = pack_bf16x2(acc[dt][r4 * 4 + 2] * sc, acc[dt][r4 * 4 + 3] * sc);
+      *reinterpret_cast<u32x2*>(dst + dt * 32 + r4 * 8 + half * 4) = pk;
+    }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 template <int BLK>
@@ -852,7 +1102,10 @@ hipError_t launch_d128(const BwdK& k, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int total_k = nbg * k.nqb;
   const int per_xcd_k = (total_k + kNumXcd - 1) / kNumXcd;
-  k_bwd_dkdv_d128<BLK><<<per_xcd_k * kNumXcd, 256, 0, s>>>(k, per_xcd_k, total_k);
+  if constexpr (BLK == 64)
+    k_bwd_dkdv_pair<<<per_xcd_k * kNumXcd, 512, 0, s>>>(k, per_xcd_k, total_k);
+  else
+    k_bwd_dkdv_d128<BLK><<<per_xcd_k * kNumXcd, 256, 0, s>>>(k, per_xcd_k, total_k);
   return hipGetLastError();
 }
 
