@@ -255,6 +255,25 @@ constexpr int kIters = 4;
 // PAGED: the summaries live in a pool [n_pool, Hkv, D]; logical page p of
 // sequence b reads pool page page_table[b][p], and pages at or past
 // ceil(seq_len[b] / page) (or naming no pool page) score -inf.
+// One float64 lane value moved by a DPP pattern (both halves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(u)), CTRL, 0xF, 0xF, false));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_update_dpp(0, int(uint32_t(u >> 32)), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(double, uint64_t(hi) << 32 | lo);
+}
+
+// Sum over the n (8 or 16) lanes of a page (a DPP row group, or half of
+// one); every lane gets the total.
+__device__ __forceinline__ double page_sum(double x, int n) {
+  x += dpp_f64<0xB1>(x);    // lane ^ 1
+  x += dpp_f64<0x4E>(x);    // lane ^ 2
+  x += dpp_f64<0x141>(x);   // half-row mirror: the other quad of the 8
+  if (n == 16) x += dpp_f64<0x140>(x);   // row mirror: the other 8 of the 16
+  return x;
+}
+
 template <int G, bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ kmin,
@@ -301,8 +320,9 @@ __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* _
           off = (size_t(bg) * nP + p) * D + sub * 8;
         }
         live[buf][t] = true;
-        rlo[buf][t] = *reinterpret_cast<const u32x4*>(kmin + off);
-        rhi[buf][t] = *reinterpret_cast<const u32x4*>(kmax + off);
+        // streaming loads: every bound is read once per call
+        rlo[buf][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmin + off));
+        rhi[buf][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kmax + off));
       }
     }
   };
@@ -323,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void k_page_scores_bf16(const uint16_t* _
           acc = __builtin_fma(double(lo), neg[e], acc);
         }
       }
-      for (int o = lpp / 2; o > 0; o /= 2) acc += __shfl_xor(acc, o);
+      acc = page_sum(acc, lpp);
       if (p < nP && sub == 0)
         scores[size_t(bg) * nP + p] = live[it & 1][t] ? float(acc) : -__builtin_inff();
     }
