@@ -62,6 +62,8 @@ SIGNATURES = {
     "dsa_topk_select_tokens": (_c_int, [_vp] + [_c_int] * 6 + [_vp, _vp, _vp]),
     "dsa_nsa_window_combine": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 6
                                + [_c_float, _vp, _vp, _vp, _vp, _vp]),
+    "dsa_nsa_select_window_combine": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
+                                      + [_c_int] * 3 + [_c_float, _vp, _vp, _vp, _vp]),
     "dsa_sparse_attn_tokens": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
                                + [_c_int] * 2 + [_c_float, _vp, _vp, _vp]),
     "dsa_sparse_attn_decode_noalloc": (_c_int, [_c_int, _vp, _vp, _vp] + [_c_int] * 5 + [_vp, _vp]
@@ -521,6 +523,23 @@ def dsa_nsa_window_combine(q, k, v, window, scale, o_cmp, o_sel, gate_logits, ou
         D, window, float(scale), _ptr(o_cmp, "o_cmp", q.dtype), _ptr(o_sel, "o_sel", q.dtype),
         _ptr(gate_logits, "gate_logits", torch.float32), _ptr(out, "out", q.dtype), _stream(stream))
     _check(st, "dsa_nsa_window_combine")
+
+
+def dsa_nsa_select_window_combine(q, k, v, idx, count, sel_block, window, scale, o_cmp,
+                                  gate_logits, out, stream=None):
+    """Selected and sliding branches and the gated combine in one pass over
+    each query block's rows (o_sel and o_win stay on chip)."""
+    B, Hq, Hkv, S, D = _check_attn(q, k, v, out, None)
+    nb = -(-S // sel_block) if sel_block > 0 else 0
+    width = _check_lists(idx, count, (B, Hkv), nb)
+    _expect(o_cmp, (B, Hq, S, D), "o_cmp")
+    _expect(gate_logits, (B, S, Hq, 3), "gate_logits")
+    st = load().dsa_nsa_select_window_combine(
+        _dtype_code(q), _ptr(q, "q"), _ptr(k, "k", q.dtype), _ptr(v, "v", q.dtype), B, Hq, Hkv, S,
+        D, _ptr(idx, "idx", torch.int32), _ptr(count, "count", torch.int32), width, sel_block,
+        window, float(scale), _ptr(o_cmp, "o_cmp", q.dtype),
+        _ptr(gate_logits, "gate_logits", torch.float32), _ptr(out, "out", q.dtype), _stream(stream))
+    _check(st, "dsa_nsa_select_window_combine")
 
 
 def dsa_nsa_combine(o_cmp, o_sel, o_win, gate_logits, out, stream=None):

@@ -711,6 +711,60 @@ int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* 
                     "dsa_nsa_window_combine");
 }
 
+int dsa_nsa_select_window_combine(int dtype, const void* q, const void* k, const void* v, int B,
+                                  int Hq, int Hkv, int S, int D, const int32_t* idx,
+                                  const int32_t* count, int idx_width, int sel_block, int window,
+                                  float scale, const void* o_cmp, const float* gate_logits,
+                                  void* out, void* stream) {
+  g_err.clear();
+  TRY(check_dtype(dtype, false));
+  TRY(check_heads(B, Hq, Hkv));
+  REQUIRE(D == 128, DSA_E_UNSUPPORTED, "the fused branches need D = 128 (got %d)", D);
+  TRY(check_block(sel_block, "sel_block"));
+  REQUIRE(S >= 1, DSA_E_ARG, "S must be >= 1 (got %d)", S);
+  REQUIRE(window >= 1, DSA_E_ARG, "window must be >= 1 (got %d)", window);
+  REQUIRE(idx_width >= 1, DSA_E_ARG, "idx_width must be >= 1 (got %d)", idx_width);
+  REQUIRE(rows_fit(B, Hq, S), DSA_E_ARG, "B*Hq*S too large");
+  TRY(check_group_extent(Hq / Hkv, S, D, "S"));
+  REQUIRE(scale > 0.f, DSA_E_ARG, "scale must be > 0");
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE(idx != nullptr && count != nullptr, DSA_E_ARG, "idx and count must not be NULL");
+  REQUIRE_PTR(o_cmp);
+  REQUIRE_PTR(gate_logits);
+  REQUIRE_PTR(out);
+  dsa::AttnArgs a{};
+  a.dtype = dtype;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.idx = idx;
+  a.count = count;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.Skv = S;
+  a.D = D;
+  a.block = sel_block;
+  a.idx_width = idx_width;
+  a.mode = dsa::MODE_INDEX;
+  a.cmp_len = 1;
+  a.cmp_stride = 1;
+  a.sel_heads = Hq / Hkv;
+  a.gate_o1 = o_cmp;
+  a.gate_z = gate_logits;
+  a.scale = scale;
+  a.then_window = window;
+  REQUIRE(dsa::attention_supported(a), DSA_E_UNSUPPORTED,
+          "the fused branches need blocks of 64k tokens, at least 256 rows per query block and "
+          "group, and idx_width * sel_block/64 + (window + sel_block)/64 + 2 <= 128");
+  return hip_status(dsa::launch_attention(a, static_cast<hipStream_t>(stream)),
+                    "dsa_nsa_select_window_combine");
+}
+
 int dsa_nsa_combine(int dtype, const void* o_cmp, const void* o_sel, const void* o_win,
                     const float* gate_logits, int B, int Hq, int S, int D, void* out,
                     void* stream) {

@@ -74,6 +74,11 @@ struct AttnArgs {
   const void* gate_o2;
   const float* gate_z;
   float scale;
+  // index mode (pipelined D = 128 kernel): after its listed blocks, every
+  // row also attends to the token window of this many keys ending at the row
+  // (a second softmax); with gate_z the epilogue combines the two, the
+  // listed blocks' output taking gate_o2's place.  0: no window pass.
+  int then_window;
 };
 // Whether some kernel serves this configuration (host-side check).
 bool attention_supported(const AttnArgs& a);

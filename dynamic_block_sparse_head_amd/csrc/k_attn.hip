@@ -1074,12 +1074,19 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   uint8_t* const vbase = smem + 2 * KBYTES;
 
   // persistent workgroups (one per CU): a contiguous range of items per XCD,
-  // or for the compressed branch (items differ in length) every grid-th item
+  // or for the compressed branch (items differ in length) every grid-th item.
+  // An XCD's range runs longest items first and is dealt out round by round,
+  // forward in even rounds and backward in odd ones, so that the workgroup
+  // that took a round's longest item takes the next round's shortest (the
+  // short items of the earliest query blocks then even out instead of
+  // piling onto the same workgroups).
   const int nwg = int(gridDim.x) / kNumXcd;
   const int xcd = int(blockIdx.x) % kNumXcd, slot = int(blockIdx.x) / kNumXcd;
-  const int w_first = a.mode == MODE_CMP ? int(blockIdx.x) : xcd * per_xcd + slot;
   const int w_end = a.mode == MODE_CMP ? total : min(total, (xcd + 1) * per_xcd);
-  const int w_step = a.mode == MODE_CMP ? int(gridDim.x) : nwg;
+  auto item_of = [&](int r) __attribute__((always_inline)) -> int {
+    if (a.mode == MODE_CMP) return int(blockIdx.x) + r * int(gridDim.x);
+    return xcd * per_xcd + r * nwg + ((r & 1) ? nwg - 1 - slot : slot);
+  };
 
   const int SH = a.sel_heads, U = a.Hq / SH;
   const int lane = threadIdx.x & 63;
@@ -1099,8 +1106,9 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   const uint32_t v_off0 = uint32_t((16 * ((2 * wave) >> 2) + 4 * lq + ((2 * wave) & 3)) * D * 2 + lc * 16);
   const uint32_t v_off1 = v_off0 + D * 2;   // chunk 2w+1: the next key of the same quad
 
-  // per item
-  int ntiles = 0, key0_w0 = 0, key0_w1 = 0;
+  // per item (n_sel: tiles of the listed blocks when a window pass follows
+  // them, else -1)
+  int ntiles = 0, n_sel = -1, key0_w0 = 0, key0_w1 = 0;
   int row_lo = 0, row_hi = -1, blk_lo = 0, blk_hi = -1;
   bf16x8 qf[D / 16];
   floatx16 o[D / 32];
@@ -1460,11 +1468,15 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       // count are never used)
       const int tpb = a.block / KT;
       // (every lane loaded the same count)
-      ntiles = max(0, min(__builtin_amdgcn_readfirstlane(nx_cnt), a.idx_width)) * tpb;
+      const int nsel = max(0, min(__builtin_amdgcn_readfirstlane(nx_cnt), a.idx_width)) * tpb;
+      // a window pass: the window's tiles follow the listed ones
+      const int wfirst = max(0, t0 - a.then_window + 1) / KT;
+      ntiles = a.then_window > 0 ? nsel + t1 / KT - wfirst + 1 : nsel;
+      n_sel = a.then_window > 0 ? nsel : -1;
       auto key0 = [&](int n) -> int {
         const int e = n / tpb;
         const int v0 = __shfl(nx_e0, e & 63), v1 = __shfl(nx_e1, e & 63);
-        return (e < 64 ? v0 : v1) * a.block + (n % tpb) * KT;
+        return n < nsel ? (e < 64 ? v0 : v1) * a.block + (n % tpb) * KT : (wfirst + n - nsel) * KT;
       };
       const int ln = item_lane();
       const int k0 = key0(ln), k1 = key0(ln + 64);
@@ -1482,6 +1494,45 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       issue(t0l, 1);
       bias_load(0);
     }
+  };
+
+  // Window pass after the listed blocks.  switch_a runs once the listed
+  // blocks' last softmax step is done (their row sum is final): it parks the
+  // row sum, restarts the softmax statistics and moves the visible intervals
+  // to the window; the listed blocks' last P.V product (and any rescale it
+  // still owes) runs in the next step.  switch_b runs after it: the listed
+  // blocks' output, normalised and rounded to bf16 as a separate call would
+  // store it, goes into this wave's staging region (free until the
+  // epilogue), and the accumulators restart.
+  auto switch_a = [&]() __attribute__((always_inline)) {
+    const float lt = half_sum(l);
+    if (half == 0) lstage[wave][col] = lt;
+    m = -__builtin_inff();
+    l = 0.f;
+    const int r = sub * ROWS + wave * 32 + col;
+    const int row_t = t0 + r % a.block;
+    const int t1 = min(a.S, t0 + a.block) - 1;
+    const int W = a.then_window;
+    row_lo = max(0, row_t - W + 1) - half * 4;
+    row_hi = min(row_t, a.Skv - 1) - half * 4;
+    blk_lo = max(0, t1 - W + 1);
+    blk_hi = min(t0, a.Skv - 1);
+  };
+  auto switch_b = [&]() __attribute__((always_inline)) {
+    const float lt = lstage[wave][col];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint8_t* stg = &ostage[wave][0];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[dt][rr * 4 + 0] * inv, o[dt][rr * 4 + 1] * inv);
+        pk[1] = pack_bf16x2(o[dt][rr * 4 + 2] * inv, o[dt][rr * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8) = pk;
+      }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] = floatx16{};
   };
 
   // the staged output of the previous item leaves: the wave's 32 rows are
@@ -1512,15 +1563,19 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
   // tile loop; then request the next item's query rows and first keys
   // before staging this item's output, so that those loads run under the
   // staging and the stores.
-  if (w_first < w_end) {
-    fetch_list(w_first);
-    begin(w_first);
+  // (item numbers grow with the round, so the first one past the range ends
+  // the loop)
+  int w = item_of(0);
+  if (w < w_end) {
+    fetch_list(w);
+    begin(w);
   }
-  for (int w = w_first; w < w_end; w += w_step) {
+  for (int r = 1; w < w_end; ++r) {
     // the next item, or this one again after the last (those loads are
     // never used; running begin() unconditionally keeps one version of its
     // registers)
-    const int w_next = w + w_step < w_end ? w + w_step : w;   // uniform
+    const int w_after = item_of(r);
+    const int w_next = w_after < w_end ? w_after : w;   // uniform
     m = -__builtin_inff();
     l = 0.f;
     alpha = 1.f;
@@ -1539,11 +1594,17 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     fetch_list(w_next);
 
     if (ntiles > 0) {
+      if (n_sel == 0) {   // nothing listed: the window pass from the start
+        switch_a();
+        switch_b();
+      }
       step(F{}, T{}, F{}, I0{}, 0);
       step(F{}, T{}, T{}, I1{}, 1);
       for (int n = 1; n < ntiles; ++n) {
         step(T{}, T{}, T{}, I0{}, 2 * n);
+        if (n == n_sel) switch_a();   // uniform
         step(T{}, T{}, T{}, I1{}, 2 * n + 1);
+        if (n == n_sel) switch_b();
       }
       step(T{}, F{}, T{}, I0{}, 2 * ntiles);
       step(T{}, F{}, F{}, I1{}, 2 * ntiles + 1);
@@ -1577,6 +1638,8 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
       // gated combine with the other two branches' outputs: sigmoid(z0) o1 +
       // sigmoid(z1) o2 + sigmoid(z2) (this branch, float32), rounded once.
       // The lane's pieces of both rows are all loaded before any is used.
+      // After a window pass o2 is the listed blocks' output, staged in this
+      // lane's own places of the staging region (overwritten below).
       const int r = p_sub * ROWS + wave * 32 + col;
       const int hh = r / a.block;
       const int row_t = p_t0 + r % a.block;
@@ -1592,7 +1655,10 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           w1[dt][rr] = ok ? *reinterpret_cast<const u32x2*>(p1 + dt * 32 + rr * 8 + half * 4) : u32x2{0u, 0u};
-          w2[dt][rr] = ok ? *reinterpret_cast<const u32x2*>(p2 + dt * 32 + rr * 8 + half * 4) : u32x2{0u, 0u};
+          if (a.then_window > 0)
+            w2[dt][rr] = *reinterpret_cast<const u32x2*>(stg + col * 256 + (((dt * 4 + rr) ^ (col & 15)) << 4) + half * 8);
+          else
+            w2[dt][rr] = ok ? *reinterpret_cast<const u32x2*>(p2 + dt * 32 + rr * 8 + half * 4) : u32x2{0u, 0u};
         }
       if (ok) {
         const float* z = a.gate_z + ((size_t(p_b) * a.S + row_t) * a.Hq + h) * 3;
@@ -1616,6 +1682,7 @@ void k_attn_bf16_d128_pipe(AttnArgs a, int wg_per_qb, int nqb, int per_xcd, int 
     }
     if (half == 0) lstage[wave][col] = lse_v;
     pend = true;
+    w = w_after;
   }
   if (pend) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1692,7 +1759,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs a, int nqb) {
 
 // Upper bound on the key tiles of one query block (as make_tiles counts them).
 int attn_max_tiles(const AttnArgs& a, int kt) {
-  if (a.mode == MODE_INDEX) return a.idx_width * (a.block / kt);
+  if (a.mode == MODE_INDEX)
+    return a.idx_width * (a.block / kt) + (a.then_window > 0 ? (a.then_window + a.block) / kt + 2 : 0);
   if (a.mode == MODE_WINDOW) return (a.window + a.block) / kt + 2;
   return (a.Skv + kt - 1) / kt;
 }
@@ -1726,7 +1794,8 @@ bool uses_d128_union(const AttnArgs& a) {
 // each wave's 32 rows inside one head), whole workgroups of rows
 bool uses_pipe(const AttnArgs& a) {
   return a.dtype == 1 && a.D == 128 && a.block % 64 == 0 && a.sel_heads * a.block >= 256 &&
-         (a.gate_z == nullptr || a.mode == MODE_WINDOW) && attn_max_tiles(a, 64) <= w2::kMaxTiles;
+         (a.gate_z == nullptr || a.mode == MODE_WINDOW || a.then_window > 0) &&
+         attn_max_tiles(a, 64) <= w2::kMaxTiles;
 }
 
 bool uses_d128(const AttnArgs& a) {
@@ -1740,6 +1809,8 @@ bool attention_supported(const AttnArgs& a) {
   // the additive key term exists in the float32 kernel and the D = 128 one;
   // the gated-combine epilogue in the D = 128 one
   if (a.gate_z != nullptr && !uses_d128(a)) return false;
+  // the window pass after the listed blocks exists in the pipelined kernel only
+  if (a.then_window > 0 && (a.mode != MODE_INDEX || !uses_pipe(a))) return false;
   return a.key_bias == nullptr || a.dtype == 0 || uses_d128(a);
 }
 

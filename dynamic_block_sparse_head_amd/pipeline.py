@@ -192,7 +192,7 @@ class NSAPlan:
     sliding branch; gated combine ([NSA] §03)."""
 
     def __init__(self, B, Hq, Hkv, S, D, cmp_len, cmp_stride, sel_block, sel_k, window, dtype,
-                 device, scale=None, per_token=False, fuse_combine=None):
+                 device, scale=None, per_token=False, fuse_combine=None, fuse_branches=None):
         self.B, self.Hq, self.Hkv, self.S, self.D = B, Hq, Hkv, S, D
         self.cmp_len, self.cmp_stride = cmp_len, cmp_stride
         self.sel_block, self.sel_k, self.window = sel_block, sel_k, window
@@ -208,6 +208,12 @@ class NSAPlan:
         # the sliding branch with the gated combine in its epilogue (D = 128,
         # at least 4 query heads per KV head), unless asked otherwise
         self.fuse_combine = (D == 128 and Hq // Hkv >= 4) if fuse_combine is None else fuse_combine
+        # the selected and sliding branches and the combine in one pass over
+        # each query block's rows (per-block selection, 64k-token blocks);
+        # o_sel and o_win are then not written
+        eligible = (self.fuse_combine and not per_token and sel_block % 64 == 0
+                    and (Hq // Hkv) * sel_block >= 256)
+        self.fuse_branches = eligible if fuse_branches is None else (fuse_branches and eligible)
         rows = S if per_token else self.nb
         self.scores = _empty((B, Hkv, rows, self.nb), torch.float32, device)
         self.idx = _empty((B, Hkv, rows, sel_k), torch.int32, device)
@@ -231,6 +237,10 @@ class NSAPlan:
             L.dsa_nsa_cmp_attn(q, self.ck, self.cv, self.cmp_len, self.cmp_stride,
                                self.sel_block, self.scale, self.o_cmp, self.lse_cmp, self.scores)
             L.dsa_topk_select(self.scores, self.sel_k, 0, True, self.idx, self.count)
+            if self.fuse_branches:
+                L.dsa_nsa_select_window_combine(q, k, v, self.idx, self.count, self.sel_block,
+                                                self.window, self.scale, self.o_cmp, z, self.out)
+                return self.out
             L.dsa_sparse_attn_prefill(q, k, v, self.idx, self.count, self.sel_block, 0,
                                       self.scale, self.o_sel)
         if self.fuse_combine:

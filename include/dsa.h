@@ -394,6 +394,32 @@ int dsa_nsa_window_combine(int dtype, const void* q, const void* k, const void* 
                            void* stream);
 
 /*
+ * The selected and sliding branches and the gated combine in one call
+ * ([NSA] §03: the three branches share each token's queries; [NSA] §04:
+ * work is arranged around the query rows that stay on chip).  Each 64k-token
+ * query block of each KV group holds its query rows once: its rows attend to
+ * the blocks listed in idx/count (as dsa_sparse_attn_prefill in index mode,
+ * block = sel_block), that output is rounded to bf16, then the same rows
+ * attend to the token window t-window+1 .. t (as window mode), and
+ * out = sigmoid(z0)*o_cmp + sigmoid(z1)*o_sel + sigmoid(z2)*o_win is formed in
+ * float32 from the window result and rounded once.  With sel_block = 64
+ * equal, bit for bit, to dsa_sparse_attn_prefill (index mode) into o_sel
+ * followed by dsa_nsa_window_combine; neither o_sel nor o_win goes through
+ * memory.
+ * q [B,Hq,S,D], k, v [B,Hkv,S,D], idx [B,Hkv,nb,idx_width] (ascending, -1
+ * padded, nb = ceil(S/sel_block)), count [B,Hkv,nb] int32, o_cmp and out
+ * [B,Hq,S,D], gate_logits [B,S,Hq,3] float32; all device buffers owned by the
+ * caller; no workspace.  Limits: bf16, D = 128, sel_block a multiple of 64,
+ * Hq/Hkv * sel_block >= 256, idx_width * sel_block/64 + (window +
+ * sel_block)/64 + 2 <= 128 (else DSA_E_UNSUPPORTED).
+ */
+int dsa_nsa_select_window_combine(int dtype, const void* q, const void* k, const void* v, int B,
+                                  int Hq, int Hkv, int S, int D, const int32_t* idx,
+                                  const int32_t* count, int idx_width, int sel_block, int window,
+                                  float scale, const void* o_cmp, const float* gate_logits,
+                                  void* out, void* stream);
+
+/*
  * Measurement helper, not a step of the method: reads src [bytes] (device,
  * 16-byte aligned, bytes a positive multiple of 16) once with 16-byte
  * streaming loads, each workgroup taking whole 16 KiB runs (four loads in

@@ -23,7 +23,7 @@ def _declared():
 def test_every_declared_symbol_is_exported():
     lib = ctypes.CDLL(L.LIB_PATH)
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
     assert set(names) == set(L.SIGNATURES), "binding prototypes out of sync with dsa.h"
@@ -267,6 +267,34 @@ def test_window_combine_validation():
     assert f(*a) == L.DSA_E_UNSUPPORTED                            # G = 2: fewer than 256 rows
     a = list(args); a[9] = 9000
     assert f(*a) == L.DSA_E_UNSUPPORTED                            # window too long
+
+
+def test_select_window_combine_validation():
+    lib = L.load()
+    f = lib.dsa_nsa_select_window_combine
+    # q k v B Hq Hkv S D idx count width sel_block window scale o_cmp z out stream
+    args = [1, FAKE, FAKE, FAKE, 1, 64, 4, 32768, 128, FAKE, FAKE, 16, 64, 512, 0.1, FAKE, FAKE,
+            FAKE, None]
+    a = list(args); a[8] = 64
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # D = 64
+    a = list(args); a[13] = 0
+    assert f(*a) == L.DSA_E_ARG                                    # no window
+    a = list(args); a[11] = 0
+    assert f(*a) == L.DSA_E_ARG                                    # empty lists
+    a = list(args); a[10] = None
+    assert f(*a) == L.DSA_E_ARG and "count" in _err()
+    a = list(args); a[16] = None
+    assert f(*a) == L.DSA_E_ARG and "gate_logits" in _err()
+    a = list(args); a[0] = 0
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # float32
+    a = list(args); a[12] = 32
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # 32-token blocks
+    a = list(args); a[5] = 8
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # G = 2: fewer than 256 rows
+    a = list(args); a[11] = 120
+    assert f(*a) == L.DSA_E_UNSUPPORTED                            # 120 + 10 tiles > 128
+    a = list(args); a[7] = 1 << 20; a[5] = 32; a[6] = 2
+    assert f(*a) == L.DSA_E_UNSUPPORTED and "2^31" in _err()       # group beyond 32-bit offsets
 
 
 def test_offsets_beyond_32_bits_are_rejected():

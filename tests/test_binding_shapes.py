@@ -145,6 +145,14 @@ def test_three_branch_shapes():
     _bad(L.dsa_nsa_combine, q, q, q, z(1, Gq, Sn, 3, dtype=f32), q, name="gate_logits")
     _ok(L.dsa_nsa_window_combine, q, k, k, 512, 0.1, q, q, zl, q)
     _bad(L.dsa_nsa_window_combine, q, k, k, 512, 0.1, q, z(1, Gq, Sn - 1, D), zl, q, name="o_sel")
+    idx, cnt = z(1, 1, nbs, 16, dtype=i32), z(1, 1, nbs, dtype=i32)
+    _ok(L.dsa_nsa_select_window_combine, q, k, k, idx, cnt, sb, 512, 0.1, q, zl, q)
+    _bad(L.dsa_nsa_select_window_combine, q, k, k, idx, z(1, 1, nbs - 1, dtype=i32), sb, 512, 0.1,
+         q, zl, q, name="count")
+    _bad(L.dsa_nsa_select_window_combine, q, k, k, idx, cnt, sb, 512, 0.1, z(1, Gq, Sn, D - 1), zl,
+         q, name="o_cmp")
+    _bad(L.dsa_nsa_select_window_combine, q, k, k, idx, cnt, sb, 512, 0.1, q, zl,
+         z(1, Gq + 1, Sn, D), name="out")
 
 
 def test_dma_shapes():

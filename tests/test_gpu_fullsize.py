@@ -134,7 +134,12 @@ def test_nsa_32k_full_size():
     fused = torch.empty_like(plan.out)
     L.dsa_nsa_window_combine(x["q"], x["k"], x["v"], c.window, c.scale, plan.o_cmp, plan.o_sel,
                              x["z"], fused)
+    one = torch.full_like(plan.out, float("nan"))
+    L.dsa_nsa_select_window_combine(x["q"], x["k"], x["v"], plan.idx, plan.count, c.sel_block,
+                                    c.window, c.scale, plan.o_cmp, x["z"], one)
     torch.cuda.synchronize()
+    # the one-pass selected + sliding + combine equals the two calls bit for bit
+    assert torch.equal(one.view(torch.int16), fused.view(torch.int16))
     _nsa_sampled(c, x, plan, 1, [0, 1, 16, 300, 511], fused)
 
 
@@ -180,7 +185,7 @@ def test_nsa_32k_planted_needles():
     print(f"needle strength {alpha}: oracle margins {min(gaps):.2e} .. {max(gaps):.2e}")
     assert len(x["needles"]) == 4 * c.Hkv
     plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
-                   c.window, x["q"].dtype, DEV)
+                   c.window, x["q"].dtype, DEV, fuse_branches=False)
     plan.run(x["q"], x["k"], x["v"], x["z"])
     torch.cuda.synchronize()
     gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()

@@ -326,6 +326,73 @@ def test_nsa_window_combine_fused(S, Hq, Hkv, window):
     check_bf16(to_np(fused), to_np(plan.out), "fused against two calls")
 
 
+def _bits(t):
+    return t.view(torch.int16).cpu()
+
+
+@pytest.mark.parametrize("S,B,Hq,Hkv,window", [(2048 + 64, 1, 16, 1, 512), (1000, 1, 8, 2, 512),
+                                                (777, 1, 4, 1, 100), (1100, 2, 8, 2, 512),
+                                                (64, 1, 4, 1, 512), (37, 1, 4, 1, 16)])
+def test_nsa_select_window_combine(S, B, Hq, Hkv, window):
+    """The selected and sliding branches with the gated combine in one pass
+    over each query block's rows: bit for bit the index-mode call followed by
+    the fused window + combine, and end to end against the oracle (a plan
+    that runs the fused pass, whose o_sel and o_win are never written)."""
+    c = replace(configs.NSA_32K, B=B, S=S, Hq=Hq, Hkv=Hkv, window=window)
+    x = inputs.nsa_inputs(c, seed=S + 7, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV, fuse_branches=False)
+    assert plan.fuse_combine and not plan.fuse_branches
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    one = torch.full_like(plan.out, float("nan"))
+    L.dsa_nsa_select_window_combine(x["q"], x["k"], x["v"], plan.idx, plan.count, c.sel_block,
+                                    c.window, c.scale, plan.o_cmp, x["z"], one)
+    _sync()
+    assert torch.equal(_bits(one), _bits(plan.out)), "one pass differs from the two calls"
+    fplan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                    c.window, x["q"].dtype, DEV)
+    assert fplan.fuse_branches
+    fplan.run(x["q"], x["k"], x["v"], x["z"])
+    _sync()
+    assert torch.equal(_bits(fplan.out), _bits(one))
+    q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
+    ref = On.forward(q, k, v, z, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window, c.scale,
+                     summary_dtype="bf16")
+    gi, gc = fplan.idx.cpu().numpy(), fplan.count.cpu().numpy()
+    check_indices(ref["scores"], gi, gc, c.sel_k, 0, True)
+    if np.array_equal(gi, ref["idx"]) and np.array_equal(gc, ref["count"]):
+        full = ref["out"]
+    else:   # accepted near-ties: the oracle's selected branch at the GPU's lists
+        o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale)
+        full = On.combine(ref["o_cmp"], o2, ref["o_win"], z)
+    check_bf16(to_np(fplan.out), full, "one-pass selected + sliding + combine, end to end")
+
+
+def test_nsa_select_window_combine_empty_lists():
+    """Query blocks whose list is empty (count 0) take only the window pass
+    (their selected output is zero), bit for bit as the two calls do."""
+    c = replace(configs.NSA_32K, S=1000, Hq=8, Hkv=2)
+    x = inputs.nsa_inputs(c, seed=11, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV, fuse_branches=False)
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    count = plan.count.clone()
+    count[:, :, ::3] = 0
+    count[:, 1, 5:9] = 0
+    o_sel = torch.empty_like(plan.out)
+    L.dsa_sparse_attn_prefill(x["q"], x["k"], x["v"], plan.idx, count, c.sel_block, 0, c.scale,
+                              o_sel)
+    two = torch.empty_like(plan.out)
+    L.dsa_nsa_window_combine(x["q"], x["k"], x["v"], c.window, c.scale, plan.o_cmp, o_sel, x["z"],
+                             two)
+    one = torch.full_like(plan.out, float("nan"))
+    L.dsa_nsa_select_window_combine(x["q"], x["k"], x["v"], plan.idx, count, c.sel_block,
+                                    c.window, c.scale, plan.o_cmp, x["z"], one)
+    _sync()
+    assert (o_sel[:, :, :64].float() == 0).all()
+    assert torch.equal(_bits(one), _bits(two))
+
+
 def test_nsa_combine_only():
     rng = torch.Generator().manual_seed(0)
     o = [torch.randn(1, 4, 100, 128, generator=rng).to(torch.bfloat16) for _ in range(3)]
