@@ -425,7 +425,7 @@ def bench_backward(torch, iters=10):
             "frac_of_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def bench_nsa(torch, iters=5):
+def bench_nsa(torch, iters=10, warmup=3):
     from dynamic_block_sparse_head_amd import configs, inputs
     from dynamic_block_sparse_head_amd.pipeline import NSAPlan
 
@@ -434,7 +434,8 @@ def bench_nsa(torch, iters=5):
     p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
                 x["q"].dtype, "cuda")
     args = (x["q"], x["k"], x["v"], x["z"])
-    p.run(*args)
+    for _ in range(warmup):   # untimed: the first steps of a series run slower
+        p.run(*args)
     ms = _timed(lambda: p.run(*args), iters, torch)
     # the step's calls one by one (same inputs, outputs rewritten identically)
     from dynamic_block_sparse_head_amd import binding as L
@@ -494,7 +495,8 @@ def bench_nsa_tokens(torch, iters=5):
     p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
                 x["q"].dtype, "cuda", per_token=True)
     q, k, v, z = x["q"], x["k"], x["v"], x["z"]
-    p.run(q, k, v, z)
+    for _ in range(2):   # untimed warm-up steps
+        p.run(q, k, v, z)
     ms = _timed(lambda: p.run(q, k, v, z), iters, torch)
     ms_scores = _timed(lambda: L.dsa_nsa_cmp_token_scores(q, p.ck, p.lse_cmp, c.cmp_len,
                                                           c.cmp_stride, c.sel_block, p.scale,
