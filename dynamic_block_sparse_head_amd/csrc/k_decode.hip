@@ -76,6 +76,29 @@ __device__ __forceinline__ float row_sum(float x) {
   return x;
 }
 
+// DPP within a row of 16 lanes: lane r reads lane r ^ 8, the lane mirrored
+// in its half row (bits 0-2 flipped), in its quad (bits 0-1 flipped), r ^ 1,
+// r - 4 and r - 8 (rotations), or lane n (broadcast)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppRor8 = 0x128, kDppRor4 = 0x124, kDppHalfMirror = 0x141, kDppQuadRev = 0x1B,
+              kDppQuadSwap = 0xB1, kDppBcast0 = 0x150;
+
+// One stage of a reduce-scatter over the lanes of a row: the lane keeps the
+// N values whose index bit matches `bit` (its own lane bit) and adds the
+// partner's copies of them; it sends the other N.  x[0..2N) -> y[0..N).
+template <int N, int CTRL>
+__device__ __forceinline__ void scatter_stage(const float* x, float* y, bool bit) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const float send = bit ? x[j] : x[j + N];
+    const float keep = bit ? x[j + N] : x[j];
+    y[j] = keep + dpp<CTRL>(send);
+  }
+}
+
 // grid (nsplit, B*Hkv).  PAGED: the cache is a pool [P, Hkv, PAGE, D]
 // shared by the batch, logical page p of sequence b lives in pool page
 // page_table[b][p], and only tokens below seq_len[b] exist (rows past it,
@@ -186,7 +209,87 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
       }
     }
   };
+  // D = 128 with 4 heads per group: a row of 16 lanes holds kBatch = 4
+  // tokens x 4 heads = 16 (token, head) pairs, pair j = 4 u + h.  Each lane's
+  // 16 partial dot products are reduce-scattered over the row (four DPP
+  // stages, 15 adds in all instead of 64 for a reduction to every lane), so
+  // lane r owns pair r: one score, one exponential and one row-sum term per
+  // lane; the heads' maxima and the 16 probabilities reach every lane of the
+  // row by DPP broadcasts.  lp: this lane's share of its head's row sum.
+  constexpr bool kPairs = (CPR == 16 && G == 4 && kBatch == 4);
+  const int hr = dc & 3;   // (kPairs) the head of this lane's pair
+  float lp = 0.f;
+  auto consume_pairs = [&](const Batch& bt) {
+   if constexpr (kPairs) {
+    float part[16];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, bt.k[u]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const bf16x8 qv = __builtin_bit_cast(bf16x8, q[h]);
+        float s = 0.f;
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 0, 1), __builtin_shufflevector(kv, kv, 0, 1), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 2, 3), __builtin_shufflevector(kv, kv, 2, 3), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 4, 5), __builtin_shufflevector(kv, kv, 4, 5), s, false);
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 6, 7), __builtin_shufflevector(kv, kv, 6, 7), s, false);
+        part[u * 4 + h] = s;
+      }
+    }
+    float w8[8], w4[4], w2[2], w1[1];
+    scatter_stage<8, kDppRor8>(part, w8, dc & 8);
+    scatter_stage<4, kDppHalfMirror>(w8, w4, dc & 4);
+    scatter_stage<2, kDppQuadRev>(w4, w2, dc & 2);
+    scatter_stage<1, kDppQuadSwap>(w2, w1, dc & 1);
+    bool ok = false;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ok = (dc >> 2) == u ? bt.base[u] != 0xffffffffu : ok;
+    const float sc = ok ? w1[0] * c : -__builtin_inff();
+    // the head's maximum over the 4 tokens, then every head's on every lane
+    float mx = fmaxf(sc, dpp<kDppRor8>(sc));
+    mx = fmaxf(mx, dpp<kDppRor4>(mx));
+    float mt[G];
+    mt[0] = dpp<kDppBcast0 + 0>(mx);
+    mt[1] = dpp<kDppBcast0 + 1>(mx);
+    mt[2] = dpp<kDppBcast0 + 2>(mx);
+    mt[3] = dpp<kDppBcast0 + 3>(mx);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (mt[h] > m[h]) {   // uniform across the lanes of a token group
+        const float alpha = fast_exp2(m[h] - mt[h]);
+        lp = hr == h ? lp * alpha : lp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        m[h] = mt[h];
+      }
+    }
+    float mh = m[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) mh = hr == h ? m[h] : mh;
+    const float p = fast_exp2(sc - (mh == -__builtin_inff() ? 0.f : mh));
+    lp += p;
+    float pj[16];
+#define DSA_BCAST(J) pj[J] = dpp<kDppBcast0 + J>(p);
+    DSA_BCAST(0) DSA_BCAST(1) DSA_BCAST(2) DSA_BCAST(3) DSA_BCAST(4) DSA_BCAST(5) DSA_BCAST(6)
+    DSA_BCAST(7) DSA_BCAST(8) DSA_BCAST(9) DSA_BCAST(10) DSA_BCAST(11) DSA_BCAST(12) DSA_BCAST(13)
+    DSA_BCAST(14) DSA_BCAST(15)
+#undef DSA_BCAST
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      float vf[8];
+      unpack8(PAGED && bt.base[u] == 0xffffffffu ? zero4 : bt.v[u], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pj[u * 4 + h], vf[e], acc[h][e]);
+    }
+   }
+  };
   auto consume = [&](const Batch& bt) {
+    if constexpr (kPairs) {
+      consume_pairs(bt);
+      return;
+    }
     float sc[kBatch][G];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -244,6 +347,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
     consume(B);
   }
 
+  if constexpr (kPairs) {
+    // each head's row sum: the shares of the 4 lanes holding its pairs
+    float x = lp + dpp<kDppRor8>(lp);
+    x += dpp<kDppRor4>(x);
+    l[0] = dpp<kDppBcast0 + 0>(x);
+    l[1] = dpp<kDppBcast0 + 1>(x);
+    l[2] = dpp<kDppBcast0 + 2>(x);
+    l[3] = dpp<kDppBcast0 + 3>(x);
+  }
   if (dc == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
