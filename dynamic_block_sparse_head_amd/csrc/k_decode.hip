@@ -274,14 +274,27 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
     DSA_BCAST(7) DSA_BCAST(8) DSA_BCAST(9) DSA_BCAST(10) DSA_BCAST(11) DSA_BCAST(12) DSA_BCAST(13)
     DSA_BCAST(14) DSA_BCAST(15)
 #undef DSA_BCAST
+    // P.V over token pairs (0, 1) and (2, 3): the probabilities rounded to
+    // bf16 (as the prefill kernels feed P to the matrix core), one v_dot2 per
+    // (token pair, head, dimension) on the bf16 pairs of the two tokens'
+    // values (exact products, float32 sums)
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      float vf[8];
-      unpack8(PAGED && bt.base[u] == 0xffffffffu ? zero4 : bt.v[u], vf);
+    for (int up = 0; up < 2; ++up) {
+      const u32x4 va = PAGED && bt.base[2 * up] == 0xffffffffu ? zero4 : bt.v[2 * up];
+      const u32x4 vb = PAGED && bt.base[2 * up + 1] == 0xffffffffu ? zero4 : bt.v[2 * up + 1];
+      uint32_t vv[8];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int w = 0; w < 4; ++w) {
+        vv[2 * w] = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);       // low halves
+        vv[2 * w + 1] = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // high halves
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pj[u * 4 + h], vf[e], acc[h][e]);
+      for (int h = 0; h < G; ++h) {
+        const bf16x2 pp = __builtin_bit_cast(bf16x2, pack_bf16x2(pj[8 * up + h], pj[8 * up + 4 + h]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vv[e]), acc[h][e], false);
+      }
     }
    }
   };
