@@ -83,8 +83,12 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-constexpr int kDppRor8 = 0x128, kDppRor4 = 0x124, kDppHalfMirror = 0x141, kDppQuadRev = 0x1B,
-              kDppQuadSwap = 0xB1, kDppBcast0 = 0x150;
+constexpr int kDppRor8 = 0x128, kDppRor4 = 0x124, kDppRor12 = 0x12C, kDppHalfMirror = 0x141,
+              kDppQuadRev = 0x1B, kDppQuadSwap = 0xB1, kDppBcast0 = 0x150;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, 0xF, 0xF, false));
+}
 
 // One stage of a reduce-scatter over the lanes of a row: the lane keeps the
 // N values whose index bit matches `bit` (its own lane bit) and adds the
@@ -268,16 +272,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
     for (int h = 1; h < G; ++h) mh = hr == h ? m[h] : mh;
     const float p = fast_exp2(sc - (mh == -__builtin_inff() ? 0.f : mh));
     lp += p;
-    float pj[16];
-#define DSA_BCAST(J) pj[J] = dpp<kDppBcast0 + J>(p);
-    DSA_BCAST(0) DSA_BCAST(1) DSA_BCAST(2) DSA_BCAST(3) DSA_BCAST(4) DSA_BCAST(5) DSA_BCAST(6)
-    DSA_BCAST(7) DSA_BCAST(8) DSA_BCAST(9) DSA_BCAST(10) DSA_BCAST(11) DSA_BCAST(12) DSA_BCAST(13)
-    DSA_BCAST(14) DSA_BCAST(15)
-#undef DSA_BCAST
     // P.V over token pairs (0, 1) and (2, 3): the probabilities rounded to
     // bf16 (as the prefill kernels feed P to the matrix core), one v_dot2 per
     // (token pair, head, dimension) on the bf16 pairs of the two tokens'
-    // values (exact products, float32 sums)
+    // values (exact products, float32 sums).  Lane 8 up + h packs its
+    // probability with lane 8 up + 4 + h's (token 2 up + 1, same head), and
+    // the 8 pairs reach every lane of the row.
+    const uint32_t pk = pack_bf16x2(p, dpp<kDppRor12>(p));
+    uint32_t pkj[8];
+#define DSA_BCAST(UP, H) pkj[4 * UP + H] = dpp_u<kDppBcast0 + 8 * UP + H>(pk);
+    DSA_BCAST(0, 0) DSA_BCAST(0, 1) DSA_BCAST(0, 2) DSA_BCAST(0, 3)
+    DSA_BCAST(1, 0) DSA_BCAST(1, 1) DSA_BCAST(1, 2) DSA_BCAST(1, 3)
+#undef DSA_BCAST
 #pragma unroll
     for (int up = 0; up < 2; ++up) {
       const u32x4 va = PAGED && bt.base[2 * up] == 0xffffffffu ? zero4 : bt.v[2 * up];
@@ -290,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const bf16x2 pp = __builtin_bit_cast(bf16x2, pack_bf16x2(pj[8 * up + h], pj[8 * up + 4 + h]));
+        const bf16x2 pp = __builtin_bit_cast(bf16x2, pkj[4 * up + h]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vv[e]), acc[h][e], false);
