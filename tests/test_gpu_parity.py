@@ -261,6 +261,14 @@ def test_decode_odd_counts_and_page128():
     _decode_parity(B=1, L_=128 * 40, topk=13, page=128, seed=2)
 
 
+@pytest.mark.parametrize("page,Hq", [(32, 32), (256, 32), (64, 16), (64, 64)])
+def test_decode_page_sizes_and_group_sizes(page, Hq):
+    """Four heads per KV head with 32- and 256-token pages (the per-row pair
+    reduction with two pages per slab and four slabs per page), and two and
+    eight heads per KV head (the per-lane reduction)."""
+    _decode_parity(B=2, L_=page * 48, topk=7, page=page, Hq=Hq, Hkv=8, seed=page + Hq)
+
+
 def test_decode_all_pages_is_dense():
     c = replace(configs.DECODE_128K, B=1, L=2048)
     x = inputs.decode_inputs(c, seed=4, device=DEV)
