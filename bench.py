@@ -425,7 +425,7 @@ def bench_backward(torch, iters=10):
             "frac_of_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def bench_nsa(torch, iters=10, warmup=3):
+def bench_nsa(torch, iters=10, warmup=10):
     from dynamic_block_sparse_head_amd import configs, inputs
     from dynamic_block_sparse_head_amd.pipeline import NSAPlan
 
@@ -434,9 +434,12 @@ def bench_nsa(torch, iters=10, warmup=3):
     p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
                 x["q"].dtype, "cuda")
     args = (x["q"], x["k"], x["v"], x["z"])
-    for _ in range(warmup):   # untimed: the first steps of a series run slower
+    # untimed: the first steps of a series run slower (on the box the step
+    # settles from ~5.6 to ~3.6 ms over its first ten runs)
+    for _ in range(warmup):
         p.run(*args)
     ms = _timed(lambda: p.run(*args), iters, torch)
+    step_each = _timed_each(lambda: p.run(*args), iters, torch)
     # the step's calls one by one (same inputs, outputs rewritten identically)
     from dynamic_block_sparse_head_amd import binding as L
     q, k, v, z = args
@@ -472,6 +475,7 @@ def bench_nsa(torch, iters=10, warmup=3):
     return {"workload": f"{c.name}: S=32768 Hq=64 Hkv=4 D=128; summaries 32/16, top-16 of 64-token "
                         "blocks, window 512, sigmoid gates",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(S / (ms * 1e-3), 1),
+            "step_ms_per_call_median_min_max": [round(t, 4) for t in step_each],
             "branch_flops": f1 + f2 + f3,
             "effective_tflops_whole_step": round((f1 + f2 + f3) / (ms * 1e-3) / 1e12, 2),
             "per_call_ms": per_call,
@@ -495,7 +499,7 @@ def bench_nsa_tokens(torch, iters=5):
     p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
                 x["q"].dtype, "cuda", per_token=True)
     q, k, v, z = x["q"], x["k"], x["v"], x["z"]
-    for _ in range(2):   # untimed warm-up steps
+    for _ in range(5):   # untimed warm-up steps
         p.run(q, k, v, z)
     ms = _timed(lambda: p.run(q, k, v, z), iters, torch)
     ms_scores = _timed(lambda: L.dsa_nsa_cmp_token_scores(q, p.ck, p.lse_cmp, c.cmp_len,
