@@ -376,6 +376,31 @@ def test_nsa_select_window_combine(S, B, Hq, Hkv, window):
     check_bf16(to_np(fplan.out), full, "one-pass selected + sliding + combine, end to end")
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,sel_k,window", [(1500, 8, 2, 6, 384), (1024, 4, 1, 4, 128)])
+def test_nsa_select_window_combine_128_token_blocks(S, Hq, Hkv, sel_k, window):
+    """The one pass with 128-token selection blocks (two key tiles per
+    listed block; window tiles from 128-row query blocks) end to end against
+    the oracle."""
+    c = replace(configs.NSA_32K, S=S, Hq=Hq, Hkv=Hkv, sel_block=128, sel_k=sel_k, window=window)
+    x = inputs.nsa_inputs(c, seed=S + 3, device=DEV)
+    plan = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k,
+                   c.window, x["q"].dtype, DEV)
+    assert plan.fuse_branches
+    plan.run(x["q"], x["k"], x["v"], x["z"])
+    _sync()
+    q, k, v, z = (to_np(x[n]) for n in ("q", "k", "v", "z"))
+    ref = On.forward(q, k, v, z, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window, c.scale,
+                     summary_dtype="bf16")
+    gi, gc = plan.idx.cpu().numpy(), plan.count.cpu().numpy()
+    check_indices(ref["scores"], gi, gc, c.sel_k, 0, True)
+    if np.array_equal(gi, ref["idx"]) and np.array_equal(gc, ref["count"]):
+        full = ref["out"]
+    else:
+        o2, _ = Op.sparse_attention(q, k, v, gi, gc, c.sel_block, c.scale)
+        full = On.combine(ref["o_cmp"], o2, ref["o_win"], z)
+    check_bf16(to_np(plan.out), full, "one pass, 128-token blocks, end to end")
+
+
 def test_nsa_select_window_combine_empty_lists():
     """Query blocks whose list is empty (count 0) take only the window pass
     (their selected output is zero), bit for bit as the two calls do."""
