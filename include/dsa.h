@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DSA_VERSION 100
+#define DSA_VERSION 101   /* 101: dsa_nsa_select_window_combine */
 
 enum dsa_status {
   DSA_OK = 0,

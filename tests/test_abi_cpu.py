@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = L.load()
-    assert lib.dsa_version() == 100
+    assert lib.dsa_version() == 101
     for st in (0, -1, -2, -3, -4):
         assert lib.dsa_status_string(st)
     assert lib.dsa_status_string(12345) == b"unknown dsa status"
