@@ -224,85 +224,85 @@ __global__ __launch_bounds__(kThreads) void k_decode_split(DecodeArgs a, int nsp
   const int hr = dc & 3;   // (kPairs) the head of this lane's pair
   float lp = 0.f;
   auto consume_pairs = [&](const Batch& bt) {
-   if constexpr (kPairs) {
-    float part[16];
+    if constexpr (kPairs) {
+      float part[16];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, bt.k[u]);
+      for (int u = 0; u < kBatch; ++u) {
+        const bf16x8 kv = __builtin_bit_cast(bf16x8, bt.k[u]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const bf16x8 qv = __builtin_bit_cast(bf16x8, q[h]);
+          float s = 0.f;
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 0, 1), __builtin_shufflevector(kv, kv, 0, 1), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 2, 3), __builtin_shufflevector(kv, kv, 2, 3), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 4, 5), __builtin_shufflevector(kv, kv, 4, 5), s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 6, 7), __builtin_shufflevector(kv, kv, 6, 7), s, false);
+          part[u * 4 + h] = s;
+        }
+      }
+      float w8[8], w4[4], w2[2], w1[1];
+      scatter_stage<8, kDppRor8>(part, w8, dc & 8);
+      scatter_stage<4, kDppHalfMirror>(w8, w4, dc & 4);
+      scatter_stage<2, kDppQuadRev>(w4, w2, dc & 2);
+      scatter_stage<1, kDppQuadSwap>(w2, w1, dc & 1);
+      bool ok = false;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) ok = (dc >> 2) == u ? bt.base[u] != 0xffffffffu : ok;
+      const float sc = ok ? w1[0] * c : -__builtin_inff();
+      // the head's maximum over the 4 tokens, then every head's on every lane
+      float mx = fmaxf(sc, dpp<kDppRor8>(sc));
+      mx = fmaxf(mx, dpp<kDppRor4>(mx));
+      float mt[G];
+      mt[0] = dpp<kDppBcast0 + 0>(mx);
+      mt[1] = dpp<kDppBcast0 + 1>(mx);
+      mt[2] = dpp<kDppBcast0 + 2>(mx);
+      mt[3] = dpp<kDppBcast0 + 3>(mx);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const bf16x8 qv = __builtin_bit_cast(bf16x8, q[h]);
-        float s = 0.f;
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 0, 1), __builtin_shufflevector(kv, kv, 0, 1), s, false);
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 2, 3), __builtin_shufflevector(kv, kv, 2, 3), s, false);
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 4, 5), __builtin_shufflevector(kv, kv, 4, 5), s, false);
-        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 6, 7), __builtin_shufflevector(kv, kv, 6, 7), s, false);
-        part[u * 4 + h] = s;
+        if (mt[h] > m[h]) {   // uniform across the lanes of a token group
+          const float alpha = fast_exp2(m[h] - mt[h]);
+          lp = hr == h ? lp * alpha : lp;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+          m[h] = mt[h];
+        }
       }
-    }
-    float w8[8], w4[4], w2[2], w1[1];
-    scatter_stage<8, kDppRor8>(part, w8, dc & 8);
-    scatter_stage<4, kDppHalfMirror>(w8, w4, dc & 4);
-    scatter_stage<2, kDppQuadRev>(w4, w2, dc & 2);
-    scatter_stage<1, kDppQuadSwap>(w2, w1, dc & 1);
-    bool ok = false;
+      float mh = m[0];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) ok = (dc >> 2) == u ? bt.base[u] != 0xffffffffu : ok;
-    const float sc = ok ? w1[0] * c : -__builtin_inff();
-    // the head's maximum over the 4 tokens, then every head's on every lane
-    float mx = fmaxf(sc, dpp<kDppRor8>(sc));
-    mx = fmaxf(mx, dpp<kDppRor4>(mx));
-    float mt[G];
-    mt[0] = dpp<kDppBcast0 + 0>(mx);
-    mt[1] = dpp<kDppBcast0 + 1>(mx);
-    mt[2] = dpp<kDppBcast0 + 2>(mx);
-    mt[3] = dpp<kDppBcast0 + 3>(mx);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (mt[h] > m[h]) {   // uniform across the lanes of a token group
-        const float alpha = fast_exp2(m[h] - mt[h]);
-        lp = hr == h ? lp * alpha : lp;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
-        m[h] = mt[h];
-      }
-    }
-    float mh = m[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) mh = hr == h ? m[h] : mh;
-    const float p = fast_exp2(sc - (mh == -__builtin_inff() ? 0.f : mh));
-    lp += p;
-    // P.V over token pairs (0, 1) and (2, 3): the probabilities rounded to
-    // bf16 (as the prefill kernels feed P to the matrix core), one v_dot2 per
-    // (token pair, head, dimension) on the bf16 pairs of the two tokens'
-    // values (exact products, float32 sums).  Lane 8 up + h packs its
-    // probability with lane 8 up + 4 + h's (token 2 up + 1, same head), and
-    // the 8 pairs reach every lane of the row.
-    const uint32_t pk = pack_bf16x2(p, dpp<kDppRor12>(p));
-    uint32_t pkj[8];
+      for (int h = 1; h < G; ++h) mh = hr == h ? m[h] : mh;
+      const float p = fast_exp2(sc - (mh == -__builtin_inff() ? 0.f : mh));
+      lp += p;
+      // P.V over token pairs (0, 1) and (2, 3): the probabilities rounded to
+      // bf16 (as the prefill kernels feed P to the matrix core), one v_dot2 per
+      // (token pair, head, dimension) on the bf16 pairs of the two tokens'
+      // values (exact products, float32 sums).  Lane 8 up + h packs its
+      // probability with lane 8 up + 4 + h's (token 2 up + 1, same head), and
+      // the 8 pairs reach every lane of the row.
+      const uint32_t pk = pack_bf16x2(p, dpp<kDppRor12>(p));
+      uint32_t pkj[8];
 #define DSA_BCAST(UP, H) pkj[4 * UP + H] = dpp_u<kDppBcast0 + 8 * UP + H>(pk);
-    DSA_BCAST(0, 0) DSA_BCAST(0, 1) DSA_BCAST(0, 2) DSA_BCAST(0, 3)
-    DSA_BCAST(1, 0) DSA_BCAST(1, 1) DSA_BCAST(1, 2) DSA_BCAST(1, 3)
+      DSA_BCAST(0, 0) DSA_BCAST(0, 1) DSA_BCAST(0, 2) DSA_BCAST(0, 3)
+      DSA_BCAST(1, 0) DSA_BCAST(1, 1) DSA_BCAST(1, 2) DSA_BCAST(1, 3)
 #undef DSA_BCAST
 #pragma unroll
-    for (int up = 0; up < 2; ++up) {
-      const u32x4 va = PAGED && bt.base[2 * up] == 0xffffffffu ? zero4 : bt.v[2 * up];
-      const u32x4 vb = PAGED && bt.base[2 * up + 1] == 0xffffffffu ? zero4 : bt.v[2 * up + 1];
-      uint32_t vv[8];
+      for (int up = 0; up < 2; ++up) {
+        const u32x4 va = PAGED && bt.base[2 * up] == 0xffffffffu ? zero4 : bt.v[2 * up];
+        const u32x4 vb = PAGED && bt.base[2 * up + 1] == 0xffffffffu ? zero4 : bt.v[2 * up + 1];
+        uint32_t vv[8];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        vv[2 * w] = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);       // low halves
-        vv[2 * w + 1] = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // high halves
-      }
+        for (int w = 0; w < 4; ++w) {
+          vv[2 * w] = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);       // low halves
+          vv[2 * w + 1] = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);   // high halves
+        }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const bf16x2 pp = __builtin_bit_cast(bf16x2, pkj[4 * up + h]);
+        for (int h = 0; h < G; ++h) {
+          const bf16x2 pp = __builtin_bit_cast(bf16x2, pkj[4 * up + h]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vv[e]), acc[h][e], false);
+          for (int e = 0; e < 8; ++e)
+            acc[h][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vv[e]), acc[h][e], false);
+        }
       }
     }
-   }
   };
   auto consume = [&](const Batch& bt) {
     if constexpr (kPairs) {
