@@ -340,7 +340,8 @@ def _bits(t):
 
 @pytest.mark.parametrize("S,B,Hq,Hkv,window", [(2048 + 64, 1, 16, 1, 512), (1000, 1, 8, 2, 512),
                                                 (777, 1, 4, 1, 100), (1100, 2, 8, 2, 512),
-                                                (64, 1, 4, 1, 512), (37, 1, 4, 1, 16)])
+                                                (64, 1, 4, 1, 512), (37, 1, 4, 1, 16),
+                                                (1000, 1, 16, 2, 256)])
 def test_nsa_select_window_combine(S, B, Hq, Hkv, window):
     """The selected and sliding branches with the gated combine in one pass
     over each query block's rows: bit for bit the index-mode call followed by
