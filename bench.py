@@ -434,7 +434,7 @@ def bench_nsa(torch, iters=10, warmup=10):
     p = NSAPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.cmp_len, c.cmp_stride, c.sel_block, c.sel_k, c.window,
                 x["q"].dtype, "cuda")
     args = (x["q"], x["k"], x["v"], x["z"])
-    # untimed: the first steps of a series run slower (on the box the step
+    # untimed: the first steps of a series run slower (on an MI355X the step
     # settles from ~5.6 to ~3.6 ms over its first ten runs)
     for _ in range(warmup):
         p.run(*args)
