@@ -129,6 +129,8 @@ def bench_prefill(cfg, steps, warmup, torch):
     reps = max(steps, 10)
     ms_scores = _timed(lambda: plan.score(q, k), reps, torch)
     ms_topk = _timed(plan.select, reps, torch)
+    for _ in range(2):   # untimed: the first call after the other kernels finds colder caches
+        plan.attend(q, k, v)
     ms_attn = _timed(lambda: plan.attend(q, k, v), reps, torch)
     attn_each = _timed_each(lambda: plan.attend(q, k, v), max(reps, 20), torch)
     sel = int(plan.count.to(torch.int64).sum().item())  # (group, query block, key block) triples
