@@ -24,6 +24,7 @@ sample of the headline workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -619,6 +620,12 @@ def main():
     torch.cuda.set_device(0)
     from dynamic_block_sparse_head_amd import binding
     binding.load()
+    # no garbage-collection pauses inside timed regions: a pause between two
+    # event records leaves the GPU idle and counts against a short kernel
+    # (one such 39 ms pause once showed up as a 2 ms decode average); each
+    # leg collects before it starts
+    gc.collect()
+    gc.disable()
 
     if args.copy_calibration:
         copy_calibration(torch)
@@ -646,6 +653,7 @@ def main():
         line = {"metric": METRIC, "n_gpus": 1}
     if args.only in (None, "prefill16k"):
         from dynamic_block_sparse_head_amd import configs
+        gc.collect()
         r16 = bench_prefill(configs.PREFILL_16K, args.steps, args.warmup, torch)
         extra["prefill_16k"] = {**_prefill_detail(r16), "roofline": _roofline(r16, ATTN16K_TRAFFIC)}
     legs = [("decode", "decode", bench_decode), ("nsa", "nsa", bench_nsa),
@@ -656,9 +664,11 @@ def main():
     _progress("prefill legs done")
     for only, key, fn in legs:
         if args.only in (None, only):
+            gc.collect()
             extra[key] = fn(torch)
             _progress(f"{key} done")
     line.update(extra)
+    gc.enable()
     if not args.no_cpu_baseline and args.only in (None, "prefill"):
         line["cpu_baseline"] = cpu_baseline()
         _progress("cpu baseline done")
