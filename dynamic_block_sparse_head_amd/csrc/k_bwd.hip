@@ -868,9 +868,10 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
   auto rt_of = [&](int buf) __attribute__((always_inline)) {
     return reinterpret_cast<float*>(&qd[buf][2 * 64 * ROWB]);
   };
-  // a pair's P: group q4 of lane l's 16 floats at [q4][l] (consecutive lanes
-  // in consecutive 16-byte slots: no bank conflicts)
-  __shared__ __attribute__((aligned(16))) floatx4 xp[NW / 2][4][64];
+  // a pair's P in bf16 (the operand A multiplies with), by step parity:
+  // group h of lane l's 16 values at [h][l] (consecutive lanes in
+  // consecutive 16-byte slots: no bank conflicts)
+  __shared__ __attribute__((aligned(16))) bf16x8 xp[2][NW / 2][2][64];
   __shared__ int lst[kDkdvList];          // the inverted list (the launcher checks it fits)
 
   const int w = xcd_work_id(per_xcd);
@@ -934,11 +935,39 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
   tr_bases(rh * 32, lane, lt0, lt8);                       // Q^T / dO^T (transposed A operand)
   bf16x8 kvf[D / 16];   // A: this wave's K rows; B: its V rows
 
-  // One step: A requests its Q operands, B its dO operands, then the first
-  // product (S or dP) and, under it, the second product's transposed
-  // operands; A forms P and parks it; after the pair barrier A adds dO^T P
-  // into dv, B forms dS and adds Q^T dS into dk.
-  auto step = [&](int t0, const uint8_t* cur, const float* rtc) __attribute__((always_inline)) {
+  // The second products trail the first by one step: the P that A parks in
+  // step n is published by the barrier that ends the step, and B forms dS
+  // from it in step n + 1, from its dP - D of step n; each wave holds its
+  // transposed operands (and A its P) of step n in registers until then.
+  // One barrier per step.
+  bf16x8 trp[2][D / 32];     // the previous step's transposed operands
+  bf16x8 opp[2];             // A: the previous step's P in bf16
+  floatx16 xprev;            // B: the previous step's dP - D
+  auto second_prev = [&](int ppar) __attribute__((always_inline)) {
+    bf16x8 op[2];
+    if (role_b) {
+      const bf16x8 pb[2] = {xp[ppar][pr][0][lane], xp[ppar][pr][1][lane]};
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)   // a hidden pair has P = 0, so its dS is 0 as well
+        op[rr >> 3][rr & 7] = static_cast<__bf16>(static_cast<float>(pb[rr >> 3][rr & 7]) * xprev[rr]);
+    } else {
+      op[0] = opp[0];
+      op[1] = opp[1];
+    }
+    // dO^T P (A) or Q^T dS (B)
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trp[ks2][dt], op[ks2], acc[dt], 0, 0, 0);
+  };
+
+  // One step: A requests its Q operands, B its dO operands; the previous
+  // step's second product; the first product (S or dP) and, under it, this
+  // step's transposed operands (dO^T for A, Q^T for B); A forms P and parks
+  // it, B keeps dP - D.
+  auto step = [&](int t0, const uint8_t* cur, const float* rtc, int par, bool prev)
+      __attribute__((always_inline)) {
     const uint8_t* rows = cur + (role_b ? 64 * ROWB : 0);
     const uint8_t* trs = cur + (role_b ? 0 : 64 * ROWB);
     // the per-lane operand addresses are formed here, each step, rather than
@@ -949,18 +978,15 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) ra[ks] = rd_row(rows, la_, ks);
     __builtin_amdgcn_sched_barrier(0);   // keep the requests ahead of the products
+    if (prev) second_prev(par ^ 1);
     floatx16 x = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[ks], kvf[ks], x, 0, 0, 0);
-    // the second product's transposed operands (dO^T for A, Q^T for B),
-    // requested under the first
-    bf16x8 tr[2][D / 32];
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) tr[ks2][dt] = rd_tr(trs, lt0_, lt8_, ks2, dt);
+      for (int dt = 0; dt < D / 32; ++dt) trp[ks2][dt] = rd_tr(trs, lt0_, lt8_, ks2, dt);
     __builtin_amdgcn_sched_barrier(0);   // ... and ahead of the softmax arithmetic
-    bf16x8 op[2];   // the second product's B operand: P (A) or dS (B), bf16
     if (!role_b) {
       // every row of this half at or after every key of its tile, all inside
       // the sequence: no masking
@@ -970,7 +996,6 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const int qr0 = rh * 32 + q4 * 8 + half * 4;
         const floatx4 l4 = *reinterpret_cast<const floatx4*>(rtc + qr0);
-        floatx4 p4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int rr = q4 * 4 + e;
@@ -982,33 +1007,20 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
             const bool vis = key <= tt && key < a.S && tt < a.S;
             p = vis ? fast_exp2(fmaf(x[rr], c, -l4[e])) : 0.f;
           }
-          op[rr >> 3][rr & 7] = static_cast<__bf16>(p);
-          p4[e] = p;
+          opp[rr >> 3][rr & 7] = static_cast<__bf16>(p);
         }
-        xp[pr][q4][lane] = p4;
       }
-    }
-    lds_barrier();   // the pair's P is parked
-    if (role_b) {
+      xp[par][pr][0][lane] = opp[0];
+      xp[par][pr][1][lane] = opp[1];
+    } else {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int qr0 = rh * 32 + q4 * 8 + half * 4;
         const floatx4 d4 = *reinterpret_cast<const floatx4*>(rtc + 64 + qr0);
-        const floatx4 p4 = xp[pr][q4][lane];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = q4 * 4 + e;
-          // a hidden pair has P = 0, so its dS is 0 as well
-          op[rr >> 3][rr & 7] = static_cast<__bf16>(p4[e] * (x[rr] - d4[e]));
-        }
+        for (int e = 0; e < 4; ++e) xprev[q4 * 4 + e] = x[q4 * 4 + e] - d4[e];
       }
     }
-    // the second product: dO^T P (A) or Q^T dS (B)
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr[ks2][dt], op[ks2], acc[dt], 0, 0, 0);
   };
 
   if (nsteps > 0) {
@@ -1048,7 +1060,7 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
         stage_rt(tp, rt_of(pbuf));
         stage(tp, qd[pbuf]);
       }
-      step(entry(n) * BLK, qd[cb], rt_of(cb));
+      step(entry(n) * BLK, qd[cb], rt_of(cb), n & 1, n > 0);
       // tile n + 1 has landed (each wave waits for its own loads); the row
       // loads of tile n + 2, issued last, may still be in flight
       if (pf) wait_vm<kOps>();
@@ -1056,6 +1068,9 @@ void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
       lds_barrier();
       cb = cb == NB - 1 ? 0 : cb + 1;
     }
+    // the last step's second products (B's P was published by the last
+    // barrier)
+    second_prev((nsteps - 1) & 1);
   }
 
   // the second row half's waves hand their sums to the first half's (the
