@@ -402,7 +402,7 @@ def bench_dma(torch, iters=10):
             "attn_frac_of_mfma_peak": round(flops / (ms_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
-def bench_backward(torch, iters=10):
+def bench_backward(torch, iters=10, warmup=10):
     """Gradients of the 16K prefill's attention (dq, dk, dv) for an N(0,1)
     upstream gradient, the forward's selection held fixed.  Effective FLOPs
     count the five products of each selected (query block, key block, head)
@@ -416,7 +416,10 @@ def bench_backward(torch, iters=10):
     q, k, v = x["q"], x["k"], x["v"]
     plan = PrefillPlan(c.B, c.Hq, c.Hkv, c.S, c.D, c.block, c.topk, c.n_local, q.dtype, "cuda")
     plan.run(q, k, v)
-    plan.backward(q, k, v, dout)
+    # untimed: like the three-branch step, the first calls of a series run
+    # slower (~2.1 ms settling to ~1.8 ms over its first ten or so)
+    for _ in range(warmup):
+        plan.backward(q, k, v, dout)
     ms = _timed(lambda: plan.backward(q, k, v, dout), iters, torch)
     sel = int(plan.count.to(torch.int64).sum().item())
     flops = 10.0 * c.D * c.block * c.block * c.G * sel
