@@ -851,12 +851,12 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv_d128(BwdK a, int per_xcd, int 
 // dk, dv, D = 128, blocks of 64: eight waves in pairs.  For key tile kt and
 // row half rh, wave A (waves 0..3) computes S = Q K^T, P and dv^T += dO^T P;
 // wave B (waves 4..7) computes dP = dO V^T, dS = P (dP - D) with A's P
-// (float32, through LDS) and dk^T += Q^T dS.  Each wave holds one
-// accumulator set and one fixed operand (K or V rows), so two waves fit a
-// SIMD and one's softmax and operand reads run beside the other's products
-// (a single wave holding both sets keeps the matrix core about a quarter
-// busy).  Tiles, arithmetic and summation order are those of
-// k_bwd_dkdv_d128, so the results are identical.
+// (the bf16 values A's own product takes, through LDS) and dk^T += Q^T dS.
+// Each wave holds one accumulator set and one fixed operand (K or V rows),
+// so two waves fit a SIMD and one's softmax and operand reads run beside the
+// other's products (a single wave holding both sets keeps the matrix core
+// about a quarter busy).  Tiles and summation order are those of
+// k_bwd_dkdv_d128; dS differs from it only by the bf16 rounding of P.
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_bwd_dkdv_pair(BwdK a, int per_xcd, int total) {
   using namespace f128;
